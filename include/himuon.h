@@ -1,0 +1,170 @@
+/*
+ * himuon.h -- C ABI of libhimuon, the HiMuon (Hierarchical Muon) optimizer step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one described in "Hierarchical Muon: Tiled Newton-Schulz
+ * Updates for Efficient Muon Optimization" (Abstract): every momentum-gradient
+ * matrix is cut into T x T tiles, the same finite Newton-Schulz (NS) map runs on
+ * each tile independently, and the tile results are put back in place and applied
+ * to the weights.  The page names tile-size-dependent GPU kernels, cross-layer
+ * batching, memory-bounded chunking and runtime tile-size schedules as what this
+ * structure allows; this library provides each of them.
+ *
+ * One step, for every layer (W fp32 H x W weights, M momentum, G gradient):
+ *   M <- beta * M + G                       (formed as one fp32 fused multiply-add,
+ *                                            stored in the momentum dtype, RNE)
+ *   for every tile Y of M (row-major grid anchored at (0,0), ragged edge tiles
+ *   kept at their own h x w size; T = HIMUON_TILE_FULL or T >= max(H, W) is one
+ *   tile per matrix):
+ *     X = Y / (||Y||_F + eps), transposed when h > w so that X is r x s, r <= s
+ *     K times:  A = X X^T;  X <- a X + (b A + c A^2) X
+ *     O_tile = X (transposed back when h > w)
+ *   W <- W - lr * O
+ * The coefficients (a, b, c) are a parameter: cubic (1.5, -0.5, 0) and quintic
+ * (3.4445, -4.7750, 2.0315) are the two shipped settings.
+ *
+ * Conventions for every entry point:
+ *  - returns himuon_status; never throws; never blocks on the GPU except where
+ *    stated; a failure leaves a message in himuon_last_error() (per thread).
+ *  - matrices are row-major; ld_* are leading dimensions in elements (>= cols).
+ *  - all device pointers are owned by the caller and must stay valid while a
+ *    step that uses them is in flight.  Layers must not alias one another.
+ */
+#ifndef HIMUON_H
+#define HIMUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define HIMUON_API __attribute__((visibility("default")))
+#else
+#define HIMUON_API
+#endif
+
+typedef enum {
+  HIMUON_OK = 0,
+  HIMUON_EINVAL = -1,       /* bad argument, shape, leading dimension or config   */
+  HIMUON_EBUDGET = -2,      /* workspace budget below what one tile needs          */
+  HIMUON_ENOMEM = -3,       /* host or device allocation failed                    */
+  HIMUON_EDEVICE = -4,      /* HIP runtime error (launch, copy, no device)         */
+  HIMUON_EUNSUPPORTED = -5  /* valid request this build does not implement         */
+} himuon_status;
+
+/* storage dtype of momentum and gradient */
+typedef enum { HIMUON_F32 = 0, HIMUON_BF16 = 1 } himuon_dtype;
+
+/* arithmetic of the NS matrix products (all accumulate in fp32) */
+typedef enum {
+  HIMUON_PREC_F32 = 0,    /* fp32 operands (fp32 MFMA)                                  */
+  HIMUON_PREC_BF16 = 1,   /* operands rounded once to bf16, one bf16 MFMA per product   */
+  HIMUON_PREC_BF16X3 = 2  /* operands split x = hi + lo (both bf16), three bf16 products
+                             hi*hi + hi*lo + lo*hi per product: fp32-class accuracy at
+                             3x the bf16 MFMA work                                       */
+} himuon_precision;
+
+#define HIMUON_TILE_FULL 0            /* one tile per matrix: full-matrix Muon        */
+#define HIMUON_FLAG_WRITE_UPDATE 1u   /* also store O (fp32) to layer.update          */
+
+typedef struct { double a, b, c; } himuon_coeffs;
+
+typedef struct {
+  int64_t rows, cols;            /* H, W                                               */
+  int64_t ld_w, ld_m, ld_g, ld_u;/* leading dimensions in elements, >= cols            */
+  float *weight;                 /* device, fp32 master weights, updated in place      */
+  void *momentum;                /* device, state dtype, updated in place              */
+  const void *grad;              /* device, state dtype, read only                     */
+  float *update;                 /* device fp32 H x W or NULL; written when the plan has
+                                    HIMUON_FLAG_WRITE_UPDATE                           */
+} himuon_layer;
+
+typedef struct {
+  int32_t tile;                  /* T >= 1, or HIMUON_TILE_FULL                        */
+  int32_t steps;                 /* K >= 0                                             */
+  himuon_coeffs coeffs;          /* (a, b, c)                                          */
+  float beta;                    /* momentum factor, e.g. 0.95                         */
+  float eps;                     /* normaliser guard, e.g. 1e-7                        */
+  size_t workspace_budget;       /* bytes of caller workspace the plan may use         */
+  himuon_dtype state_dtype;      /* dtype of momentum and grad, same for all layers    */
+  himuon_precision precision;    /* arithmetic of the NS products                      */
+  uint32_t flags;                /* HIMUON_FLAG_*                                      */
+} himuon_config;
+
+typedef struct {
+  int32_t tile;                  /* current T (0 = FULL)                               */
+  int32_t kernel_tile;           /* LDS tile edge of the fused kernel (32/64/128), or 0
+                                    when the large-tile GEMM path runs                 */
+  int64_t layers, tiles;         /* tiles of the current partition                     */
+  int64_t fused_tiles;           /* tiles run by the fused kernel                      */
+  int64_t gemm_tiles;            /* tiles run by the large-tile GEMM path              */
+  int64_t chunks;                /* launches groups of the GEMM path (>= 1 if any)     */
+  size_t workspace_bytes;        /* workspace one step needs (<= budget)               */
+  size_t table_bytes;            /* device bytes of the descriptor tables              */
+  double ns_flops;               /* algorithmic NS flops per step:
+                                    sum over tiles K (4 r^2 s + 2 r^3 [c != 0])        */
+  double issued_flops;           /* MFMA flops issued per step (padding, symmetric
+                                    blocks and the BF16X3 split included)              */
+  double step_bytes;             /* algorithmic HBM bytes per step: G, M read, M
+                                    written (state dtype), W read and written (fp32)   */
+} himuon_stats;
+
+typedef struct {
+  int32_t layer;                 /* index into the plan's layer list                   */
+  int32_t transposed;            /* 1 when h > w (iterated on the transpose)           */
+  int64_t row0, col0, rows, cols;/* tile origin and size inside its matrix             */
+} himuon_tile;
+
+typedef struct himuon_plan_s himuon_plan_t;
+
+/* Validate the layers and config and build the tile-descriptor table over all layers
+ * (row-major tiles, layers in order), the chunk list of the large-tile path and the
+ * workspace layout.  Host work only: no device memory is touched until the first
+ * himuon_step.  The layer array is copied.  EINVAL: bad shape/ld/pointer/config;
+ * EBUDGET: the budget cannot hold the workspace of the largest single tile.  */
+HIMUON_API himuon_status himuon_plan(const himuon_layer *layers, int32_t n_layers,
+                          const himuon_config *cfg, himuon_plan_t **out);
+
+/* Workspace bytes one step of this plan needs (<= cfg.workspace_budget; 0 when every
+ * tile runs in the fused kernel). */
+HIMUON_API himuon_status himuon_workspace_size(const himuon_plan_t *p, size_t *bytes);
+
+/* Enqueue one full step (momentum, tiled NS, weight update) for every layer on
+ * hip_stream (a hipStream_t; NULL = the default stream).  workspace is a device
+ * buffer of at least himuon_workspace_size bytes (may be NULL when that is 0).
+ * Does not synchronise.  The first step after himuon_plan or a tile-size change
+ * uploads the descriptor table (allocating its device buffer when it grew);
+ * later steps allocate nothing.  A plan must not be stepped on two streams
+ * concurrently.  EDEVICE on a HIP error. */
+HIMUON_API himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes,
+                          float lr, void *hip_stream);
+
+/* Change T between steps (runtime tile-size schedule).  Rebuilds the tables on the
+ * host; the next himuon_step uploads them, stream-ordered after earlier steps on
+ * that stream.  A new T whose workspace exceeds the budget gives more chunks, not
+ * an error, unless a single tile does not fit (EBUDGET). */
+HIMUON_API himuon_status himuon_set_tile_schedule(himuon_plan_t *p, int32_t tile);
+
+/* Counters of the current partition. */
+HIMUON_API himuon_status himuon_plan_stats(const himuon_plan_t *p, himuon_stats *out);
+
+/* Copy up to cap tile descriptors (in table order) into out; *n receives the total
+ * number of tiles.  out may be NULL with cap 0 to query the count. */
+HIMUON_API himuon_status himuon_plan_tiles(const himuon_plan_t *p, himuon_tile *out, int64_t cap,
+                                int64_t *n);
+
+/* Release the plan and its device tables.  The caller synchronises the stream of
+ * the last step first. */
+HIMUON_API void himuon_plan_destroy(himuon_plan_t *p);
+
+/* Message of the last failure on this thread ("" if none). */
+HIMUON_API const char *himuon_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HIMUON_H */

@@ -1,0 +1,164 @@
+"""C-ABI library on the CPU: it loads, exports every entry point of include/himuon.h,
+and its planner (host code only, no device calls) builds the same tile table as the
+oracle, bit for bit, with the oracle's flop and byte counts."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+import synth
+import tiled_newton_schulz_tile_amd as hm
+
+HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "himuon.h")
+FAKE = 1 << 32  # device addresses are not touched by the planner
+
+
+def declared_entry_points():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"HIMUON_API\s+[\w\s\*]*?\b(himuon_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    names = declared_entry_points()
+    assert names == sorted(hm.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", hm.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for n in names:
+        assert n in exported, n
+    # the library's own C++ internals stay hidden
+    assert all(not e.startswith("_ZN6himuon") for e in exported)
+
+
+def fake_layers(shapes, write_update=False):
+    out = []
+    for i, (H, W) in enumerate(shapes):
+        base = FAKE * (i + 1)
+        out.append(hm.himuon_layer(H, W, W, W, W, W if write_update else 0,
+                                   base, base + (1 << 30), base + (2 << 30),
+                                   base + (3 << 30) if write_update else None))
+    return out
+
+
+def plan_for(shapes, T, **kw):
+    cfg = hm.make_config(T, **kw)
+    return hm.himuon_plan(fake_layers(shapes, kw.get("flags", 0) & 1), cfg)
+
+
+@pytest.mark.parametrize("shapes,T", [
+    ([(256, 512)], 64), ([(256, 512)], 128), ([(256, 512)], 512), ([(256, 512)], 0),
+    ([(250, 500), (37, 53), (130, 70)], 64), ([(97, 131)], 32), ([(300, 170)], 100),
+    ([(5, 3), (1, 1), (0, 7)], 2), ([(768, 2304), (3072, 768)], 128),
+])
+def test_tile_table_equals_oracle(shapes, T):
+    p = plan_for(shapes, T)
+    try:
+        got = hm.himuon_plan_tiles(p)
+        want = [(li, int(h > w), r0, c0, h, w) for li, (H, W) in enumerate(shapes)
+                for r0, c0, h, w in oracle.tiles(H, W, T)]
+        assert got == want
+    finally:
+        hm.himuon_plan_destroy(p)
+
+
+@pytest.mark.parametrize("name,T", [("single-256x512", 64), ("gpt2-small-12L", 128),
+                                    ("decoder-1b-16L", 32), ("llama3-8b-32L", 128)])
+@pytest.mark.parametrize("coeffs", [hm.QUINTIC, hm.CUBIC])
+def test_stats_match_oracle_counts(name, T, coeffs):
+    shapes = synth.STACKS[name]
+    p = plan_for(shapes, T, coeffs=coeffs, steps=5)
+    try:
+        st = hm.himuon_plan_stats(p)
+        assert st["tiles"] == sum(len(oracle.tiles(H, W, T)) for H, W in shapes)
+        assert st["ns_flops"] == oracle.ns_flops(shapes, T, 5, coeffs)
+        assert st["step_bytes"] == oracle.step_bytes(shapes, 2)
+        assert st["fused_tiles"] == st["tiles"] and st["gemm_tiles"] == 0
+        assert st["workspace_bytes"] == 0 and hm.himuon_workspace_size(p) == 0
+        assert st["kernel_tile"] == (32 if T <= 32 else 64 if T <= 64 else 128)
+    finally:
+        hm.himuon_plan_destroy(p)
+
+
+def test_llama_stack_tile_count_and_work():
+    p = plan_for(synth.STACKS["llama3-8b-32L"], 128)
+    st = hm.himuon_plan_stats(p)
+    hm.himuon_plan_destroy(p)
+    assert st["tiles"] == 425984
+    assert st["ns_flops"] == 6 * 6979321856 * 128 * 5
+    # BF16X3 issues three bf16 products per product: 3x the algorithmic work for T=128
+    assert st["issued_flops"] == 3 * st["ns_flops"]
+
+
+def test_full_and_large_tiles_use_gemm_path_and_chunks():
+    shapes = [(4096, 14336), (14336, 4096), (4096, 1024)]
+    p = plan_for(shapes, 0, workspace_budget=10 ** 9)
+    try:
+        st = hm.himuon_plan_stats(p)
+        assert st["gemm_tiles"] == 3 and st["fused_tiles"] == 0
+        assert st["chunks"] >= 2 and 0 < st["workspace_bytes"] <= 10 ** 9
+        assert st["ns_flops"] == oracle.ns_flops(shapes, 0, 5, hm.QUINTIC)
+    finally:
+        hm.himuon_plan_destroy(p)
+
+
+def test_budget_too_small_for_one_tile_is_ebudget():
+    with pytest.raises(hm.HiMuonError) as e:
+        plan_for([(4096, 4096)], 0, workspace_budget=1000)
+    assert e.value.status == -2 and "budget" in str(e.value)
+
+
+def test_set_tile_schedule_rebuilds_table():
+    shapes = [(300, 170), (100, 260)]
+    p = plan_for(shapes, 64, workspace_budget=10 ** 9)
+    try:
+        for T in (128, 32, 256, 0, 64):
+            hm.himuon_set_tile_schedule(p, T)
+            want = [(li, int(h > w), r0, c0, h, w) for li, (H, W) in enumerate(shapes)
+                    for r0, c0, h, w in oracle.tiles(H, W, T)]
+            assert hm.himuon_plan_tiles(p) == want
+            assert hm.himuon_plan_stats(p)["tile"] == T
+        with pytest.raises(hm.HiMuonError):
+            hm.himuon_set_tile_schedule(p, -3)
+        assert hm.himuon_plan_stats(p)["tile"] == 64  # unchanged after a failed change
+    finally:
+        hm.himuon_plan_destroy(p)
+
+
+@pytest.mark.parametrize("mutate,msg", [
+    (lambda L, c: setattr(L[0], "ld_m", 100), "leading dimension"),
+    (lambda L, c: setattr(L[0], "weight", None), "NULL"),
+    (lambda L, c: setattr(L[0], "grad", FAKE + 1), "aligned"),
+    (lambda L, c: setattr(L[0], "rows", -1), "rows/cols"),
+    (lambda L, c: setattr(c, "tile", -1), "tile"),
+    (lambda L, c: setattr(c, "steps", -1), "steps"),
+    (lambda L, c: setattr(c, "precision", 7), "precision"),
+    (lambda L, c: setattr(c, "state_dtype", 5), "state_dtype"),
+    (lambda L, c: setattr(c, "flags", 8), "flag"),
+    (lambda L, c: setattr(c, "eps", float("nan")), "finite"),
+    (lambda L, c: setattr(L[0], "update", None) or setattr(c, "flags", 1), "NULL"),
+])
+def test_invalid_arguments_are_einval(mutate, msg):
+    L = fake_layers([(200, 300)], write_update=True)
+    cfg = hm.make_config(64)
+    mutate(L, cfg)
+    with pytest.raises(hm.HiMuonError) as e:
+        hm.himuon_plan(L, cfg)
+    assert e.value.status == -1 and msg in str(e.value)
+
+
+def test_empty_plan_and_empty_matrices():
+    p = hm.himuon_plan([], hm.make_config(64))
+    assert hm.himuon_plan_stats(p)["tiles"] == 0
+    hm.himuon_plan_destroy(p)
+    p = plan_for([(0, 10), (10, 0)], 64)
+    assert hm.himuon_plan_tiles(p) == []
+    hm.himuon_plan_destroy(p)
+
+
+def test_null_arguments_rejected():
+    assert hm._lib.himuon_plan(None, 0, None, None) == -1
+    assert hm._lib.himuon_step(None, None, 0, 0.02, None) == -1
+    assert hm._lib.himuon_plan_stats(None, None) == -1
+    hm._lib.himuon_plan_destroy(None)  # no-op

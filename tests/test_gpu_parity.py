@@ -1,0 +1,268 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded inputs (MI355X only).
+
+Bars: fp32 path max-abs <= 1e-4; bf16 path max-abs <= 2e-2 and relative
+Frobenius <= 1e-2 (per matrix); tile indexing and reassembly bit-exact.  The
+oracle's NS input is the momentum the GPU stored (its rounding is checked
+separately, bit for bit, against the oracle's model of the stored code).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+hm = pytest.importorskip("tiled_newton_schulz_tile_amd")
+Q, C = oracle.COEFFS_QUINTIC, oracle.COEFFS_CUBIC
+DEV = "cuda"
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def gpu_step(mats, T, K=5, coeffs=Q, prec=None, state=torch.bfloat16, beta=0.95, lr=0.02,
+             eps=1e-7, M0=None, W0=None, steps=1, grads=None):
+    """Run `steps` HiMuon steps on the GPU.  mats: list of CPU G matrices (any float dtype).
+    Returns per step a list of (W, M, U) CPU tensors and the pre-step M of each step."""
+    _need_gpu()
+    n = len(mats)
+    Gs = [g.to(state).to(DEV) for g in mats]
+    Ms = [torch.zeros_like(g) if M0 is None else M0[i].to(state).to(DEV) for i, g in enumerate(Gs)]
+    Ws = [(torch.zeros(g.shape, dtype=torch.float32) if W0 is None else W0[i].float()).to(DEV)
+          for i, g in enumerate(Gs)]
+    Us = [torch.full(g.shape, float("nan"), dtype=torch.float32, device=DEV) for g in Gs]
+    opt = hm.HiMuon([(Ws[i], Ms[i], Gs[i], Us[i]) for i in range(n)], T, K, coeffs, beta, eps,
+                    precision=prec)
+    out, pre = [], []
+    for s in range(steps):
+        if s > 0 and grads is not None:
+            for i in range(n):
+                Gs[i].copy_(grads[s - 1][i].to(state))
+        pre.append([m.cpu().clone() for m in Ms])
+        opt.step(lr)
+        torch.cuda.synchronize()
+        out.append([(Ws[i].cpu().clone(), Ms[i].cpu().clone(), Us[i].cpu().clone()) for i in range(n)])
+    opt.close()
+    return out, pre
+
+
+def errs(U, O):
+    U = U.double().numpy()
+    d = U - O
+    return float(np.abs(d).max()), float(np.linalg.norm(d) / max(np.linalg.norm(O), 1e-300))
+
+
+def assert_bar(U, O, prec, tight=None):
+    mx, rf = errs(U, O)
+    assert np.isfinite(U.numpy()).all()
+    if prec == hm.PREC_F32:
+        assert mx <= 1e-4, (mx, rf)
+    else:
+        assert mx <= 2e-2 and rf <= 1e-2, (mx, rf)
+    if tight is not None:
+        assert mx <= tight, (mx, rf)
+    return mx, rf
+
+
+def power_law(H, W, seed, dtype=torch.float32):
+    return synth.power_law_matrix(H, W, seed, dtype=dtype)
+
+
+# ------------------------------------------------------------------ single 256x512 fp32
+@pytest.mark.parametrize("T", [64, 128])
+def test_single_matrix_fp32(T):
+    G = power_law(256, 512, 0)
+    (res,), _ = gpu_step([G], T, state=torch.float32, prec=hm.PREC_F32)
+    W, M, U = res[0]
+    assert torch.equal(M, G)                        # M0 = 0: first momentum is G exactly
+    O = oracle.tiled_ns(M.double().numpy(), T, 5, Q)
+    assert_bar(U, O, hm.PREC_F32)
+    np.testing.assert_allclose(W.double().numpy(), -0.02 * O, atol=0.02 * 1e-4 + 1e-7, rtol=0)
+
+
+# ------------------------------------------------------------------ bf16 stacks
+GPT2_LAYER = [(768, 2304), (768, 768), (768, 3072), (3072, 768)]
+
+
+@pytest.mark.parametrize("T", [32, 64, 128])
+def test_gpt2_layer_bf16x3_quintic(T):
+    mats = [power_law(h, w, 100 + i) for i, (h, w) in enumerate(GPT2_LAYER)]
+    (res,), _ = gpu_step(mats, T, prec=hm.PREC_BF16X3)
+    for (W, M, U), G in zip(res, mats):
+        assert torch.equal(M, G.to(torch.bfloat16))
+        O = oracle.tiled_ns(M.double().numpy(), T, 5, Q)
+        assert_bar(U, O, hm.PREC_BF16X3, tight=2e-3)
+
+
+@pytest.mark.parametrize("T", [64, 128])
+def test_gpt2_layer_bf16_plain_cubic(T):
+    mats = [power_law(h, w, 200 + i) for i, (h, w) in enumerate(GPT2_LAYER[:2])]
+    (res,), _ = gpu_step(mats, T, coeffs=C, prec=hm.PREC_BF16)
+    for (W, M, U), G in zip(res, mats):
+        O = oracle.tiled_ns(M.double().numpy(), T, 5, C)
+        assert_bar(U, O, hm.PREC_BF16)
+
+
+# ------------------------------------------------------------------ ragged, rectangular, degenerate
+RAGGED = [(300, 170), (100, 260), (37, 53), (129, 1), (1, 200), (65, 65), (33, 97)]
+
+
+@pytest.mark.parametrize("T", [1, 7, 32, 64, 100, 128])
+@pytest.mark.parametrize("prec,state", [(0, torch.float32), (2, torch.bfloat16)])
+@pytest.mark.parametrize("coeffs,K", [(Q, 5), (Q, 8), (C, 5)])
+def test_ragged_shapes(T, prec, state, coeffs, K):
+    mats = [power_law(h, w, 300 + i) for i, (h, w) in enumerate(RAGGED)]
+    (res,), _ = gpu_step(mats, T, K=K, coeffs=coeffs, prec=prec, state=state)
+    for (W, M, U), G in zip(res, mats):
+        O = oracle.tiled_ns(M.double().numpy(), T, K, coeffs)
+        assert_bar(U, O, prec, tight=None if prec == 0 else 5e-3)
+
+
+def test_k_zero_is_normalised_momentum():
+    mats = [power_law(h, w, 400 + i) for i, (h, w) in enumerate(RAGGED)]
+    (res,), _ = gpu_step(mats, 64, K=0, prec=hm.PREC_F32, state=torch.float32)
+    for (W, M, U), G in zip(res, mats):
+        assert_bar(U, oracle.tiled_ns(M.double().numpy(), 64, 0, Q), hm.PREC_F32, tight=1e-6)
+
+
+# ------------------------------------------------------------------ exact indexing / reassembly
+@pytest.mark.parametrize("shape", [(100, 113), (113, 100)])
+def test_reassembly_bit_exact(shape):
+    # +-1 entries; every tile has a square number of elements (64^2, 64x49, 36x64, 36x49),
+    # so with eps = 0 and K = 0 the output is +-1/sqrt(h w), computed exactly rounded on
+    # both sides: any misplaced element shows up as a bit difference
+    rng = np.random.default_rng(7)
+    G = torch.from_numpy(np.where(rng.random(shape) < 0.5, -1.0, 1.0).astype(np.float32))
+    (res,), _ = gpu_step([G], 64, K=0, eps=0.0, prec=hm.PREC_F32, state=torch.float32)
+    U = res[0][2]
+    O = oracle.tiled_ns(G.double().numpy(), 64, 0, Q, eps=0.0).astype(np.float32)
+    assert np.array_equal(U.numpy(), O)
+
+
+@pytest.mark.parametrize("state,prec", [(torch.float32, 0), (torch.bfloat16, 2)])
+def test_transpose_equivariance(state, prec):
+    G = power_law(250, 500, 11)
+    (a,), _ = gpu_step([G], 64, prec=prec, state=state)
+    (b,), _ = gpu_step([G.T.contiguous()], 64, prec=prec, state=state)
+    Ua, Ub = a[0][2], b[0][2]
+    for r0, c0, h, w in oracle.tiles(250, 500, 64):
+        blk_a = Ua[r0:r0 + h, c0:c0 + w]
+        blk_b = Ub[c0:c0 + w, r0:r0 + h].T
+        if h != w:   # iterated on the same short-side matrix: bit-identical
+            assert torch.equal(blk_a, blk_b), (r0, c0, h, w)
+        else:
+            assert (blk_a - blk_b).abs().max() < (1e-5 if prec == 0 else 1e-3)
+
+
+def test_tile_locality():
+    G = power_law(256, 384, 12)
+    G2 = G.clone()
+    G2[128:192, 64:128] = power_law(64, 64, 99)
+    (a,), _ = gpu_step([G], 64, prec=2)
+    (b,), _ = gpu_step([G2], 64, prec=2)
+    mask = torch.ones(256, 384, dtype=torch.bool)
+    mask[128:192, 64:128] = False
+    assert torch.equal(a[0][2][mask], b[0][2][mask])
+    assert not torch.equal(a[0][2][~mask], b[0][2][~mask])
+
+
+def test_deterministic():
+    mats = [power_law(h, w, 500 + i) for i, (h, w) in enumerate(RAGGED[:3])]
+    (a,), _ = gpu_step(mats, 64, prec=2)
+    (b,), _ = gpu_step(mats, 64, prec=2)
+    for x, y in zip(a, b):
+        for s, t in zip(x, y):
+            assert torch.equal(s, t)
+
+
+# ------------------------------------------------------------------ special values
+@pytest.mark.parametrize("T", [32, 64, 128])
+@pytest.mark.parametrize("coeffs", [Q, C])
+def test_orthogonal_tiles(T, coeffs):
+    Qm, _ = torch.linalg.qr(torch.randn(T, T, dtype=torch.float64, generator=torch.Generator().manual_seed(T)))
+    (res,), _ = gpu_step([Qm.float().contiguous()], T, prec=0, state=torch.float32, coeffs=coeffs)
+    val = oracle.phi_iterate(1.0 / (math.sqrt(T) + 1e-7), 5, coeffs)
+    assert (res[0][2].double() - val * Qm).abs().max() < 1e-4
+
+
+def test_zero_tile_and_sign_momentum():
+    G = power_law(96, 160, 13)
+    G[:64, 64:128] = 0
+    W0 = torch.randn(96, 160)
+    (res,), _ = gpu_step([G], 64, prec=0, state=torch.float32, W0=[W0])
+    W, M, U = res[0]
+    assert (U[:64, 64:128] == 0).all()
+    assert torch.equal(W[:64, 64:128], W0[:64, 64:128])
+    # T = 1: every tile is one element, NS gives phi^K(y / (|y| + eps)): sign momentum (cubic)
+    (res,), _ = gpu_step([G], 1, prec=0, state=torch.float32, coeffs=C)
+    want = oracle.phi_iterate(G.double().numpy() / (np.abs(G.double().numpy()) + 1e-7), 5, C)
+    assert np.abs(res[0][2].double().numpy() - want).max() < 1e-5
+
+
+# ------------------------------------------------------------------ momentum and update
+def test_momentum_code_and_two_steps_bf16():
+    shapes = [(200, 330), (128, 128)]
+    G1 = [power_law(h, w, 600 + i) for i, (h, w) in enumerate(shapes)]
+    G2 = [power_law(h, w, 700 + i) for i, (h, w) in enumerate(shapes)]
+    M0 = [power_law(h, w, 800 + i).to(torch.bfloat16) for i, (h, w) in enumerate(shapes)]
+    W0 = [synth.weights(h, w, 900 + i) for i, (h, w) in enumerate(shapes)]
+    out, pre = gpu_step(G1, 64, M0=M0, W0=W0, steps=2, grads=[G2], beta=0.9, lr=0.05)
+    for s, Gs in enumerate((G1, G2)):
+        for i in range(len(shapes)):
+            W, M, U = out[s][i]
+            Mprev = pre[s][i].float().numpy()
+            Gb = Gs[i].to(torch.bfloat16).float().numpy()
+            want = oracle.momentum_stored(Mprev, Gb, 0.9, "bf16")
+            assert np.array_equal(M.float().numpy(), want)
+            O = oracle.tiled_ns(M.double().numpy(), 64, 5, Q)
+            assert_bar(U, O, hm.PREC_BF16X3, tight=2e-3)
+            Wprev = (W0[i] if s == 0 else out[0][i][0]).double().numpy()
+            np.testing.assert_allclose(W.double().numpy(), oracle.apply_update(Wprev, O, 0.05),
+                                       atol=0.05 * 2e-3 + 1e-6, rtol=0)
+
+
+def test_fp32_momentum_code():
+    G = power_law(130, 70, 14)
+    M0 = power_law(130, 70, 15)
+    (res,), _ = gpu_step([G], 64, M0=[M0], state=torch.float32, prec=0, beta=0.95)
+    want = oracle.momentum_stored(M0.numpy(), G.numpy(), 0.95, "f32")
+    assert np.array_equal(res[0][1].numpy(), want)
+
+
+# ------------------------------------------------------------------ strided and unaligned rows
+@pytest.mark.parametrize("ld_extra", [0, 3, 8])
+def test_leading_dimension(ld_extra):
+    _need_gpu()
+    H, W = 150, 200
+    G = power_law(H, W, 16)
+    ld = W + ld_extra
+    Gb = torch.zeros(H, ld, dtype=torch.bfloat16, device=DEV)
+    Mb = torch.zeros(H, ld, dtype=torch.bfloat16, device=DEV)
+    Wb = torch.zeros(H, ld, dtype=torch.float32, device=DEV)
+    Ub = torch.zeros(H, ld, dtype=torch.float32, device=DEV)
+    Gb[:, :W] = G.to(torch.bfloat16).to(DEV)
+    views = [t[:, :W] for t in (Wb, Mb, Gb, Ub)]
+    opt = hm.HiMuon([tuple(views)], 64, 5, Q)
+    opt.step(0.02)
+    torch.cuda.synchronize()
+    opt.close()
+    O = oracle.tiled_ns(views[1].cpu().double().numpy(), 64, 5, Q)
+    assert_bar(views[3].cpu(), O, hm.PREC_BF16X3, tight=2e-3)
+    # padding columns untouched
+    assert (Ub[:, W:] == 0).all() and (Wb[:, W:] == 0).all() and (Mb[:, W:] == 0).all()
+
+
+def test_plan_stats_and_empty_layer_on_gpu():
+    _need_gpu()
+    Wt = torch.zeros(0, 5, device=DEV)
+    opt = hm.HiMuon([(Wt, Wt.to(torch.bfloat16), Wt.to(torch.bfloat16))], 64)
+    opt.step(0.02)
+    torch.cuda.synchronize()
+    assert opt.stats()["tiles"] == 0
+    opt.close()

@@ -1,0 +1,650 @@
+// Fused HiMuon tile kernel for tiles up to 128 x 128 on gfx950.
+//
+// One workgroup owns one or more tiles and takes each of them through the whole
+// step without leaving the CU:
+//   momentum  M <- beta M + G  (HBM read of G and M, write of M),
+//   per-tile Frobenius norm (fixed-order reduction, wavefront shuffles),
+//   K Newton-Schulz steps with X, A = X X^T and B = b A + c A^2 resident in LDS
+//   and registers (MFMA 32x32 tiles, fp32 accumulation),
+//   W <- W - lr O  (HBM read and write of W).
+// HBM therefore sees exactly one read and one write of every element; no
+// workspace.  The same finite NS map runs on every tile independently, which is
+// what "Hierarchical Muon: Tiled Newton-Schulz Updates for Efficient Muon
+// Optimization" (Abstract) defines; cross-layer batching comes from the tile
+// table, which spans all layers of the plan.
+//
+// Data layout in LDS, per tile (edge TS in {32, 64, 128}, zero padded):
+//   X  : the oriented tile (short side r = rows), row-major, TS x TS
+//   AB : A = X X^T, then B = b A + c A^2 (both symmetric), row-major, TS x TS
+// Element formats: PREC_F32 one fp32 array; PREC_BF16 one bf16 array;
+// PREC_BF16X3 two bf16 arrays (hi = bf16(x), lo = bf16(x - hi)).
+// Each wave owns a WB x WB block (WB = 64, or 32 when TS = 32) of every product.
+//
+// Products (all as D[m][n] = sum_k P[m][k] Q[n][k] with contiguous k):
+//   Gram    A[p][q]   = sum_k X[p][k] X[q][k]
+//   square  S[p][q]   = sum_k A[p][k] A[q][k]            (A symmetric)
+//   update  D[j][i]   = sum_k X[k][j] B[i][k] = (B X)^T  (B symmetric)
+// The update accumulates on top of a * X^T held in registers in MFMA output
+// layout, so X stays in fp32 between steps; only the MFMA operands are rounded.
+#include "himuon_internal.h"
+
+namespace himuon {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// A wave's accumulators: NB x NB MFMA 32x32 output blocks.
+template <int NB>
+struct Acc {
+  f32x16 b[NB][NB];
+};
+
+// ------------------------------------------------------------------ geometry
+template <int TS, int PREC>
+struct Geo {
+  static constexpr int WB = TS >= 64 ? 64 : 32;       // wave block edge
+  static constexpr int NB = WB / 32;                  // 32x32 MFMA blocks per wave edge
+  static constexpr int WPT = (TS / WB) * (TS / WB);   // waves per tile
+  static constexpr int TPB = TS == 128 ? 1 : (TS == 64 ? 2 : 4);  // tiles per workgroup
+  static constexpr int NT = 64 * WPT;                 // threads per tile
+  static constexpr int THREADS = NT * TPB;
+  static constexpr int PB = TS + 8;                   // bf16 row pitch (elements)
+  static constexpr int PF = TS + 4;                   // fp32 row pitch (elements)
+  static constexpr int REGION = PREC == PREC_F32 ? TS * PF * 4
+                              : PREC == PREC_BF16 ? TS * PB * 2 : TS * PB * 4;
+  static constexpr int TILE_LDS = 2 * REGION;
+  static_assert(TILE_LDS >= TS * PF * 4, "staging must fit in the tile area");
+};
+
+// A matrix in LDS in the precision's element format.
+template <int PREC>
+struct Mat;
+template <>
+struct Mat<PREC_F32> {
+  float *f;
+};
+template <>
+struct Mat<PREC_BF16> {
+  __bf16 *hi;
+};
+template <>
+struct Mat<PREC_BF16X3> {
+  __bf16 *hi, *lo;
+};
+
+template <int TS, int PREC>
+__device__ inline Mat<PREC> make_mat(char *base) {
+  Mat<PREC> m;
+  if constexpr (PREC == PREC_F32) {
+    m.f = reinterpret_cast<float *>(base);
+  } else if constexpr (PREC == PREC_BF16) {
+    m.hi = reinterpret_cast<__bf16 *>(base);
+  } else {
+    m.hi = reinterpret_cast<__bf16 *>(base);
+    m.lo = reinterpret_cast<__bf16 *>(base + TS * Geo<TS, PREC>::PB * 2);
+  }
+  return m;
+}
+
+// Synchronise the threads that share one tile.
+template <int WPT>
+__device__ inline void tile_sync() {
+  if constexpr (WPT > 1) {
+    __syncthreads();
+  } else {
+    // one wave per tile: LDS traffic of a wave is processed in order; only the
+    // compiler has to be kept from moving LDS accesses across this point
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+__device__ inline f32x16 mma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x16 mma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// 8 bf16 of column j, rows k..k+7 (row pitch PB)
+template <int PB>
+__device__ inline bf16x8 gather_col_bf16(const __bf16 *buf, int k, int j) {
+  const unsigned short *p = reinterpret_cast<const unsigned short *>(buf) + k * PB + j;
+  u16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = p[e * PB];
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ------------------------------------------------------------------ wave GEMM
+// acc.b[bi][bj] += sum_k L(m, k) R(n, k) for m in the wave's L block, n in its R block.
+// L(m, k) = Lmat[m][k] (TRANS_L false) or Lmat[k][m] (TRANS_L true); R(n, k) = Rmat[n][k].
+// MFMA lane layout (32x32): operand lane l holds row (l % 32) of its 32-block and a
+// run of contiguous k selected by l / 32; both operands use the same k runs.
+template <int TS, int PREC, bool TRANS_L>
+__device__ inline void wave_gemm(Acc<Geo<TS, PREC>::NB> &acc, const Mat<PREC> &Lm, int l0, const Mat<PREC> &Rm, int r0,
+                                 int lane) {
+  using G = Geo<TS, PREC>;
+  constexpr int NB = G::NB;
+  const int li = lane & 31, half = lane >> 5;
+  if constexpr (PREC == PREC_F32) {
+    constexpr int PF = G::PF;
+#pragma unroll 2
+    for (int kb = 0; kb < TS; kb += 8) {
+      const int k = kb + 4 * half;
+      f32x4 lf[NB], rf[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int m = l0 + b * 32 + li;
+        if constexpr (TRANS_L) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lf[b][e] = Lm.f[(k + e) * PF + m];
+        } else {
+          lf[b] = *reinterpret_cast<const f32x4 *>(Lm.f + m * PF + k);
+        }
+        rf[b] = *reinterpret_cast<const f32x4 *>(Rm.f + (r0 + b * 32 + li) * PF + k);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = mma_f32(lf[bi][e], rf[bj][e], acc.b[bi][bj]);
+    }
+  } else {
+    constexpr int PB = G::PB;
+#pragma unroll 2
+    for (int kb = 0; kb < TS; kb += 16) {
+      const int k = kb + 8 * half;
+      bf16x8 lh[NB], rh[NB];
+      bf16x8 ll[NB], rl[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int m = l0 + b * 32 + li;
+        const int n = r0 + b * 32 + li;
+        if constexpr (TRANS_L) {
+          lh[b] = gather_col_bf16<PB>(Lm.hi, k, m);
+        } else {
+          lh[b] = *reinterpret_cast<const bf16x8 *>(Lm.hi + m * PB + k);
+        }
+        rh[b] = *reinterpret_cast<const bf16x8 *>(Rm.hi + n * PB + k);
+        if constexpr (PREC == PREC_BF16X3) {
+          if constexpr (TRANS_L) {
+            ll[b] = gather_col_bf16<PB>(Lm.lo, k, m);
+          } else {
+            ll[b] = *reinterpret_cast<const bf16x8 *>(Lm.lo + m * PB + k);
+          }
+          rl[b] = *reinterpret_cast<const bf16x8 *>(Rm.lo + n * PB + k);
+        }
+      }
+      if constexpr (PREC == PREC_BF16X3) {
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = mma_bf16(ll[bi], rh[bj], acc.b[bi][bj]);
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = mma_bf16(lh[bi], rl[bj], acc.b[bi][bj]);
+      }
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = mma_bf16(lh[bi], rh[bj], acc.b[bi][bj]);
+    }
+  }
+}
+
+// Element (bi, bj, r) of a wave's accumulators sits at
+//   row = p0 + bi*32 + 8*(r/4) + 4*(lane/32) + r%4,  col = q0 + bj*32 + lane%32.
+// These helpers move 4 consecutive rows (r%4 = 0..3) of one column at a time to or
+// from position [col][row..row+3] of a row-major LDS matrix, i.e. they store the
+// transpose of the accumulator block.
+
+// Store the transpose of the accumulators into a matrix in the precision's format.
+template <int TS, int PREC>
+__device__ inline void store_acc_t(const Acc<Geo<TS, PREC>::NB> &acc, const Mat<PREC> &m, int p0, int q0, int lane) {
+  using G = Geo<TS, PREC>;
+  constexpr int NB = G::NB;
+  const int li = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = p0 + bi * 32 + 8 * g + 4 * half;
+        const int col = q0 + bj * 32 + li;
+        f32x4 v = {acc.b[bi][bj][4 * g + 0], acc.b[bi][bj][4 * g + 1], acc.b[bi][bj][4 * g + 2],
+                   acc.b[bi][bj][4 * g + 3]};
+        if constexpr (PREC == PREC_F32) {
+          *reinterpret_cast<f32x4 *>(m.f + col * G::PF + row) = v;
+        } else {
+          bf16x4 hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hi[e] = (__bf16)v[e];
+          *reinterpret_cast<bf16x4 *>(m.hi + col * G::PB + row) = hi;
+          if constexpr (PREC == PREC_BF16X3) {
+            bf16x4 lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lo[e] = (__bf16)(v[e] - (float)hi[e]);
+            *reinterpret_cast<bf16x4 *>(m.lo + col * G::PB + row) = lo;
+          }
+        }
+      }
+}
+
+// fp32 staging (pitch PF) <-> accumulators, transposed as above; load scales by s.
+template <int TS, int PREC>
+__device__ inline void load_acc_t(Acc<Geo<TS, PREC>::NB> &acc, const float *st, int p0, int q0, int lane, float s) {
+  using G = Geo<TS, PREC>;
+  const int li = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int bi = 0; bi < G::NB; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < G::NB; ++bj)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = p0 + bi * 32 + 8 * g + 4 * half;
+        const int col = q0 + bj * 32 + li;
+        f32x4 v = *reinterpret_cast<const f32x4 *>(st + col * G::PF + row);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc.b[bi][bj][4 * g + e] = v[e] * s;
+      }
+}
+
+template <int TS, int PREC>
+__device__ inline void store_acc_t_f32(const Acc<Geo<TS, PREC>::NB> &acc, float *st, int p0, int q0, int lane) {
+  using G = Geo<TS, PREC>;
+  const int li = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int bi = 0; bi < G::NB; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < G::NB; ++bj)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = p0 + bi * 32 + 8 * g + 4 * half;
+        const int col = q0 + bj * 32 + li;
+        f32x4 v = {acc.b[bi][bj][4 * g + 0], acc.b[bi][bj][4 * g + 1], acc.b[bi][bj][4 * g + 2],
+                   acc.b[bi][bj][4 * g + 3]};
+        *reinterpret_cast<f32x4 *>(st + col * G::PF + row) = v;
+      }
+}
+
+// ------------------------------------------------------------------ global access
+// 8 consecutive state elements of one row.
+template <typename S>
+struct Chunk8;
+template <>
+struct Chunk8<__bf16> {
+  u32x4 v;
+  __device__ float get(int e) const {
+    const unsigned int w = v[e >> 1];
+    return __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <>
+struct Chunk8<float> {
+  f32x4 a, b;
+  __device__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
+
+template <typename S>
+__device__ inline Chunk8<S> load_chunk(const S *p, int n, bool vec) {
+  Chunk8<S> c;
+  if constexpr (sizeof(S) == 2) {
+    if (vec && n == 8) {
+      c.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    } else {
+      unsigned short t[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = e < n ? reinterpret_cast<const unsigned short *>(p)[e] : 0;
+      c.v = u32x4{t[0] | (unsigned)t[1] << 16, t[2] | (unsigned)t[3] << 16,
+                  t[4] | (unsigned)t[5] << 16, t[6] | (unsigned)t[7] << 16};
+    }
+  } else {
+    if (vec && n == 8) {
+      c.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+      c.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p) + 1);
+    } else {
+      float t[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = e < n ? p[e] : 0.f;
+      c.a = f32x4{t[0], t[1], t[2], t[3]};
+      c.b = f32x4{t[4], t[5], t[6], t[7]};
+    }
+  }
+  return c;
+}
+
+// Round an fp32 value to the state dtype; returns the stored code and its value.
+__device__ inline unsigned short to_bf16_bits(float x) {
+  return __builtin_bit_cast(unsigned short, (__bf16)x);
+}
+
+// ------------------------------------------------------------------ the kernel
+template <int TS, int PREC, typename S>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, Geo<TS, PREC>::THREADS)))
+__attribute__((amdgpu_waves_per_eu(1, 2)))
+void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__restrict__ tiles,
+                       int64_t ntiles, NSParams prm) {
+  using G = Geo<TS, PREC>;
+  constexpr int NT = G::NT, NB = G::NB, WB = G::WB, PF = G::PF;
+  __shared__ __attribute__((aligned(16))) char lds[G::TPB * G::TILE_LDS];
+  __shared__ float red[G::TPB][G::WPT];
+
+  const int grp = threadIdx.x / NT;          // tile slot in the workgroup
+  const int gt = threadIdx.x % NT;           // thread within the tile group
+  const int lane = threadIdx.x & 63;
+  const int wv = gt >> 6;                    // wave within the tile group
+  const int64_t tix = (int64_t)blockIdx.x * G::TPB + grp;
+  if (tix >= ntiles) return;                 // uniform per tile group
+
+  const FusedTile t = tiles[tix];
+  const LayerDesc L = layers[t.layer];
+  const int h = t.h, w = t.w;
+  const bool tall = h > w;
+  char *area = lds + grp * G::TILE_LDS;
+  float *st = reinterpret_cast<float *>(area);          // fp32 staging, TS x PF
+  const Mat<PREC> X = make_mat<TS, PREC>(area);
+  const Mat<PREC> AB = make_mat<TS, PREC>(area + G::REGION);
+  const int p0 = (wv / (TS / WB)) * WB;                  // wave block origin
+  const int q0 = (wv % (TS / WB)) * WB;
+
+  // ---- momentum and staging of the oriented, zero-padded tile ---------------
+  {
+    constexpr int CPR = TS / 8;
+    constexpr int ITER = TS * CPR / NT;                  // chunks per thread
+    constexpr int BATCH = ITER < 4 ? ITER : 4;
+    S *mbase = reinterpret_cast<S *>(L.m);
+    const S *gbase = reinterpret_cast<const S *>(L.g);
+    const bool vec = L.vec_ok && (t.col0 % 8 == 0);
+#pragma unroll
+    for (int b0 = 0; b0 < ITER; b0 += BATCH) {
+      Chunk8<S> cg[BATCH], cm[BATCH];
+      int nn[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const int q = gt + (b0 + i) * NT;
+        const int r = q / CPR, c = (q % CPR) * 8;
+        int n = r < h ? w - c : 0;
+        n = n < 0 ? 0 : (n > 8 ? 8 : n);
+        nn[i] = n;
+        const int64_t gr = (int64_t)(t.row0 + r);
+        cg[i] = load_chunk<S>(gbase + gr * L.ld_g + t.col0 + c, n, vec);
+        cm[i] = load_chunk<S>(mbase + gr * L.ld_m + t.col0 + c, n, vec);
+      }
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const int q = gt + (b0 + i) * NT;
+        const int r = q / CPR, c = (q % CPR) * 8;
+        const int n = nn[i];
+        float v[8];
+        Chunk8<S> out;
+        if constexpr (sizeof(S) == 2) {
+          unsigned short code[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            code[e] = to_bf16_bits(__builtin_fmaf(prm.beta, cm[i].get(e), cg[i].get(e)));
+            v[e] = __builtin_bit_cast(float, (unsigned)code[e] << 16);
+          }
+          out.v = u32x4{code[0] | (unsigned)code[1] << 16, code[2] | (unsigned)code[3] << 16,
+                        code[4] | (unsigned)code[5] << 16, code[6] | (unsigned)code[7] << 16};
+          S *dst = mbase + (int64_t)(t.row0 + r) * L.ld_m + t.col0 + c;
+          if (vec && n == 8) {
+            *reinterpret_cast<u32x4 *>(dst) = out.v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e < n) reinterpret_cast<unsigned short *>(dst)[e] = code[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(prm.beta, cm[i].get(e), cg[i].get(e));
+          S *dst = mbase + (int64_t)(t.row0 + r) * L.ld_m + t.col0 + c;
+          if (vec && n == 8) {
+            reinterpret_cast<f32x4 *>(dst)[0] = f32x4{v[0], v[1], v[2], v[3]};
+            reinterpret_cast<f32x4 *>(dst)[1] = f32x4{v[4], v[5], v[6], v[7]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e < n) dst[e] = v[e];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e >= n) v[e] = 0.f;                        // zero padding
+        if (!tall) {
+          *reinterpret_cast<f32x4 *>(st + r * PF + c) = f32x4{v[0], v[1], v[2], v[3]};
+          *reinterpret_cast<f32x4 *>(st + r * PF + c + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) st[(c + e) * PF + r] = v[e];
+        }
+      }
+    }
+  }
+  tile_sync<G::WPT>();
+
+  // ---- Frobenius norm of the oriented tile, fixed summation order -----------
+  float inv;
+  {
+    float ss = 0.f;
+    constexpr int C4 = TS * TS / 4;
+#pragma unroll 4
+    for (int q = gt; q < C4; q += NT) {
+      const int r = q / (TS / 4), c = (q % (TS / 4)) * 4;
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(st + r * PF + c);
+      ss = __builtin_fmaf(v[0], v[0], ss);
+      ss = __builtin_fmaf(v[1], v[1], ss);
+      ss = __builtin_fmaf(v[2], v[2], ss);
+      ss = __builtin_fmaf(v[3], v[3], ss);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if constexpr (G::WPT > 1) {
+      if (lane == 0) red[grp][wv] = ss;
+      tile_sync<G::WPT>();
+      ss = red[grp][0];
+#pragma unroll
+      for (int i = 1; i < G::WPT; ++i) ss += red[grp][i];
+    }
+    inv = 1.0f / (__builtin_sqrtf(ss) + prm.eps);
+  }
+
+  // X in registers (fp32, MFMA output layout of the update product: block holds X^T)
+  Acc<NB> xr;
+  load_acc_t<TS, PREC>(xr, st, p0, q0, lane, inv);
+  tile_sync<G::WPT>();
+  store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
+  tile_sync<G::WPT>();
+
+  // ---- K Newton-Schulz steps --------------------------------------------------
+  const float ca = prm.a, cb = prm.b, cc = prm.c;
+  for (int it = 0; it < prm.steps; ++it) {
+    Acc<NB> acc;
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = f32x16{};
+    wave_gemm<TS, PREC, false>(acc, X, p0, X, q0, lane);           // A = X X^T
+    if (cc != 0.f) {
+      store_acc_t<TS, PREC>(acc, AB, p0, q0, lane);                  // A is symmetric
+      tile_sync<G::WPT>();
+      Acc<NB> sq;
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj) sq.b[bi][bj] = f32x16{};
+      wave_gemm<TS, PREC, false>(sq, AB, p0, AB, q0, lane);         // A^2 = A A^T
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            acc.b[bi][bj][e] = __builtin_fmaf(cc, sq.b[bi][bj][e], cb * acc.b[bi][bj][e]);
+      tile_sync<G::WPT>();                                           // A fully read
+    } else {
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc.b[bi][bj][e] *= cb;
+    }
+    store_acc_t<TS, PREC>(acc, AB, p0, q0, lane);                    // B (symmetric)
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xr.b[bi][bj][e] *= ca;
+    tile_sync<G::WPT>();
+    wave_gemm<TS, PREC, true>(xr, X, p0, AB, q0, lane);             // X^T <- a X^T + X^T B
+    tile_sync<G::WPT>();
+    if (it + 1 < prm.steps) {
+      store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
+      tile_sync<G::WPT>();
+    }
+  }
+
+  // ---- reassembly and weight update ------------------------------------------
+  tile_sync<G::WPT>();
+  store_acc_t_f32<TS, PREC>(xr, st, p0, q0, lane);
+  tile_sync<G::WPT>();
+  {
+    constexpr int CPR = TS / 4;
+    constexpr int ITER = TS * CPR / NT;
+    constexpr int BATCH = ITER < 8 ? ITER : 8;
+    const bool vec = L.vec_w && (t.col0 % 4 == 0);
+    const float nlr = -prm.lr;
+#pragma unroll
+    for (int b0 = 0; b0 < ITER; b0 += BATCH) {
+      f32x4 wv4[BATCH];
+      int nn[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const int q = gt + (b0 + i) * NT;
+        const int r = q / CPR, c = (q % CPR) * 4;
+        int n = r < h ? w - c : 0;
+        n = n < 0 ? 0 : (n > 4 ? 4 : n);
+        nn[i] = n;
+        const float *src = L.w + (int64_t)(t.row0 + r) * L.ld_w + t.col0 + c;
+        if (vec && n == 4) {
+          wv4[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src));
+        } else {
+          float tmp[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) tmp[e] = e < n ? src[e] : 0.f;
+          wv4[i] = f32x4{tmp[0], tmp[1], tmp[2], tmp[3]};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const int q = gt + (b0 + i) * NT;
+        const int r = q / CPR, c = (q % CPR) * 4;
+        const int n = nn[i];
+        if (n == 0) continue;
+        float o[4];
+        if (!tall) {
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(st + r * PF + c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = v[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = st[(c + e) * PF + r];
+        }
+        float *dst = L.w + (int64_t)(t.row0 + r) * L.ld_w + t.col0 + c;
+        float nw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nw[e] = __builtin_fmaf(nlr, o[e], wv4[i][e]);
+        if (vec && n == 4) {
+          *reinterpret_cast<f32x4 *>(dst) = f32x4{nw[0], nw[1], nw[2], nw[3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e < n) dst[e] = nw[e];
+        }
+        if (prm.write_update) {
+          float *ud = L.u + (int64_t)(t.row0 + r) * L.ld_u + t.col0 + c;
+          if (vec && n == 4) {
+            *reinterpret_cast<f32x4 *>(ud) = f32x4{o[0], o[1], o[2], o[3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (e < n) ud[e] = o[e];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int TS, int PREC, typename S>
+hipError_t launch_one(const LayerDesc *layers, const FusedTile *tiles, int64_t n,
+                      const NSParams &p, hipStream_t stream) {
+  using G = Geo<TS, PREC>;
+  const int64_t blocks = (n + G::TPB - 1) / G::TPB;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fused_step_kernel<TS, PREC, S>), dim3((unsigned)blocks), dim3(G::THREADS), 0,
+                     stream, layers, tiles, n, p);
+  return hipGetLastError();
+}
+
+template <int TS, int PREC>
+hipError_t launch_state(int state_bf16, const LayerDesc *layers, const FusedTile *tiles, int64_t n,
+                        const NSParams &p, hipStream_t stream) {
+  return state_bf16 ? launch_one<TS, PREC, __bf16>(layers, tiles, n, p, stream)
+                    : launch_one<TS, PREC, float>(layers, tiles, n, p, stream);
+}
+
+template <int TS>
+hipError_t launch_prec(int prec, int state_bf16, const LayerDesc *layers, const FusedTile *tiles,
+                       int64_t n, const NSParams &p, hipStream_t stream) {
+  switch (prec) {
+    case PREC_F32: return launch_state<TS, PREC_F32>(state_bf16, layers, tiles, n, p, stream);
+    case PREC_BF16: return launch_state<TS, PREC_BF16>(state_bf16, layers, tiles, n, p, stream);
+    case PREC_BF16X3: return launch_state<TS, PREC_BF16X3>(state_bf16, layers, tiles, n, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fused(int ts, int prec, int state_bf16, const LayerDesc *layers,
+                        const FusedTile *tiles, int64_t n, const NSParams &p, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  switch (ts) {
+    case 32: return launch_prec<32>(prec, state_bf16, layers, tiles, n, p, stream);
+    case 64: return launch_prec<64>(prec, state_bf16, layers, tiles, n, p, stream);
+    case 128: return launch_prec<128>(prec, state_bf16, layers, tiles, n, p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+size_t fused_lds_bytes(int ts, int prec) {
+  auto f = [&](auto tsc) -> size_t {
+    constexpr int TS = decltype(tsc)::value;
+    switch (prec) {
+      case PREC_F32: return Geo<TS, PREC_F32>::TPB * Geo<TS, PREC_F32>::TILE_LDS;
+      case PREC_BF16: return Geo<TS, PREC_BF16>::TPB * Geo<TS, PREC_BF16>::TILE_LDS;
+      default: return Geo<TS, PREC_BF16X3>::TPB * Geo<TS, PREC_BF16X3>::TILE_LDS;
+    }
+  };
+  switch (ts) {
+    case 32: return f(std::integral_constant<int, 32>{});
+    case 64: return f(std::integral_constant<int, 64>{});
+    case 128: return f(std::integral_constant<int, 128>{});
+    default: return 0;
+  }
+}
+
+}  // namespace himuon

@@ -1,0 +1,249 @@
+// Host planner of the HiMuon step (see plan.h).
+//
+// The partition follows "Hierarchical Muon: Tiled Newton-Schulz Updates for
+// Efficient Muon Optimization" (Abstract): each matrix is cut into T x T tiles;
+// here the grid is anchored at (0, 0), tiles are listed row-major, layer after
+// layer, and the last tile row / column keeps its ragged size.  T = 0 (FULL) or
+// T >= max(H, W) gives one tile per matrix.  Tiles whose longer side is at most
+// 128 run in the fused kernel (edge 32, 64 or 128, zero padded); larger tiles
+// take the GEMM path, whose workspace is cut into chunks under the budget
+// (memory-bounded chunking, same page).
+#include "plan.h"
+
+#include <cmath>
+#include <cstdint>
+#include <sstream>
+
+namespace himuon {
+
+namespace {
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool finite(double v) { return std::isfinite(v); }
+}  // namespace
+
+int fused_edge_for(int64_t e) {
+  if (e <= 0) return 0;
+  if (e <= 32) return 32;
+  if (e <= 64) return 64;
+  if (e <= 128) return 128;
+  return 0;
+}
+
+size_t gemm_tile_workspace(int64_t r, int64_t s, int prec) {
+  (void)prec;
+  // X (double buffered, fp32), A and B (fp32, r x r), scale slot
+  return 2 * align256((size_t)r * s * 4) + 2 * align256((size_t)r * r * 4) + 256;
+}
+
+himuon_status plan_init(Plan &p, const himuon_layer *layers, int32_t n, const himuon_config *cfg,
+                        std::string &err) {
+  std::ostringstream m;
+  if (!cfg) {
+    err = "config is NULL";
+    return HIMUON_EINVAL;
+  }
+  if (n < 0 || (n > 0 && !layers)) {
+    err = "layer list is NULL or n_layers < 0";
+    return HIMUON_EINVAL;
+  }
+  const himuon_config &c = *cfg;
+  if (c.tile < 0) {
+    err = "tile must be >= 1 or HIMUON_TILE_FULL (0)";
+    return HIMUON_EINVAL;
+  }
+  if (c.steps < 0 || c.steps > 10000) {
+    err = "steps must be in [0, 10000]";
+    return HIMUON_EINVAL;
+  }
+  if (!finite(c.coeffs.a) || !finite(c.coeffs.b) || !finite(c.coeffs.c) || !std::isfinite(c.beta) ||
+      !std::isfinite(c.eps) || c.eps < 0) {
+    err = "coefficients, beta and eps must be finite (eps >= 0)";
+    return HIMUON_EINVAL;
+  }
+  if (c.state_dtype != HIMUON_F32 && c.state_dtype != HIMUON_BF16) {
+    err = "state_dtype must be HIMUON_F32 or HIMUON_BF16";
+    return HIMUON_EINVAL;
+  }
+  if (c.precision != HIMUON_PREC_F32 && c.precision != HIMUON_PREC_BF16 &&
+      c.precision != HIMUON_PREC_BF16X3) {
+    err = "precision must be HIMUON_PREC_F32, HIMUON_PREC_BF16 or HIMUON_PREC_BF16X3";
+    return HIMUON_EINVAL;
+  }
+  if (c.flags & ~HIMUON_FLAG_WRITE_UPDATE) {
+    err = "unknown flag bits";
+    return HIMUON_EINVAL;
+  }
+  const bool want_u = c.flags & HIMUON_FLAG_WRITE_UPDATE;
+  const size_t esz = c.state_dtype == HIMUON_BF16 ? 2 : 4;
+  p.layers.assign(layers, layers + n);
+  p.ldesc.clear();
+  for (int32_t i = 0; i < n; ++i) {
+    const himuon_layer &L = layers[i];
+    if (L.rows < 0 || L.cols < 0 || L.rows >= kMaxDim || L.cols >= kMaxDim) {
+      m << "layer " << i << ": rows/cols out of range";
+      err = m.str();
+      return HIMUON_EINVAL;
+    }
+    const bool empty = L.rows == 0 || L.cols == 0;
+    if (!empty) {
+      if (L.ld_w < L.cols || L.ld_m < L.cols || L.ld_g < L.cols || (want_u && L.ld_u < L.cols)) {
+        m << "layer " << i << ": leading dimension smaller than cols";
+        err = m.str();
+        return HIMUON_EINVAL;
+      }
+      if (!L.weight || !L.momentum || !L.grad || (want_u && !L.update)) {
+        m << "layer " << i << ": NULL device pointer";
+        err = m.str();
+        return HIMUON_EINVAL;
+      }
+      if (((uintptr_t)L.weight & 3) || ((uintptr_t)L.momentum & (esz - 1)) ||
+          ((uintptr_t)L.grad & (esz - 1)) || (want_u && ((uintptr_t)L.update & 3))) {
+        m << "layer " << i << ": pointer not aligned to its element size";
+        err = m.str();
+        return HIMUON_EINVAL;
+      }
+    }
+    LayerDesc d{};
+    d.w = L.weight;
+    d.m = L.momentum;
+    d.g = L.grad;
+    d.u = want_u ? L.update : nullptr;
+    d.ld_w = L.ld_w;
+    d.ld_m = L.ld_m;
+    d.ld_g = L.ld_g;
+    d.ld_u = want_u ? L.ld_u : 0;
+    d.rows = (int32_t)L.rows;
+    d.cols = (int32_t)L.cols;
+    d.vec_ok = (L.ld_m % 8 == 0) && (L.ld_g % 8 == 0) && ((uintptr_t)L.momentum % 16 == 0) &&
+               ((uintptr_t)L.grad % 16 == 0);
+    d.vec_w = (L.ld_w % 4 == 0) && ((uintptr_t)L.weight % 16 == 0) &&
+              (!want_u || ((L.ld_u % 4 == 0) && ((uintptr_t)L.update % 16 == 0)));
+    p.ldesc.push_back(d);
+  }
+  p.cfg = c;
+  return HIMUON_OK;
+}
+
+himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
+  if (tile < 0) {
+    err = "tile must be >= 1 or HIMUON_TILE_FULL (0)";
+    return HIMUON_EINVAL;
+  }
+  const himuon_config &c = p.cfg;
+  const int prec = (int)c.precision;
+  const int64_t K = c.steps;
+  const bool quintic = c.coeffs.c != 0.0;
+  const double split = prec == HIMUON_PREC_BF16X3 ? 3.0 : 1.0;
+  const size_t esz = c.state_dtype == HIMUON_BF16 ? 2 : 4;
+
+  std::vector<FusedTile> by_edge[3];
+  std::vector<GemmTile> gt;
+  std::vector<himuon_tile> order;
+  double ns_flops = 0, issued = 0, bytes = 0;
+  size_t max_ws = 0;
+  for (size_t li = 0; li < p.layers.size(); ++li) {
+    const int64_t H = p.layers[li].rows, W = p.layers[li].cols;
+    if (H == 0 || W == 0) continue;
+    bytes += (double)H * W * (3.0 * esz + 8.0);
+    const int64_t T = tile == 0 ? std::max(H, W) : tile;
+    for (int64_t r0 = 0; r0 < H; r0 += T) {
+      for (int64_t c0 = 0; c0 < W; c0 += T) {
+        const int64_t h = std::min(T, H - r0), w = std::min(T, W - c0);
+        const int64_t r = std::min(h, w), s = std::max(h, w);
+        ns_flops += (double)K * (4.0 * r * r * s + (quintic ? 2.0 * r * r * r : 0.0));
+        order.push_back(himuon_tile{(int32_t)li, h > w ? 1 : 0, r0, c0, h, w});
+        const int e = fused_edge_for(s);
+        if (e) {
+          by_edge[e == 32 ? 0 : (e == 64 ? 1 : 2)].push_back(
+              FusedTile{(int32_t)li, (int32_t)r0, (int32_t)c0, (int16_t)h, (int16_t)w});
+          issued += (double)K * split * 2.0 * e * e * e * (quintic ? 3.0 : 2.0);
+        } else {
+          GemmTile g{};
+          g.layer = (int32_t)li;
+          g.row0 = (int32_t)r0;
+          g.col0 = (int32_t)c0;
+          g.h = (int32_t)h;
+          g.w = (int32_t)w;
+          g.r = (int32_t)r;
+          g.s = (int32_t)s;
+          g.tall = h > w;
+          gt.push_back(g);
+          max_ws = std::max(max_ws, gemm_tile_workspace(r, s, prec));
+          issued += (double)K * split * (4.0 * r * r * s + (quintic ? 2.0 * r * r * r : 0.0));
+        }
+      }
+    }
+  }
+  if (!gt.empty() && max_ws > c.workspace_budget) {
+    std::ostringstream m;
+    m << "workspace budget " << c.workspace_budget << " B is below the " << max_ws
+      << " B one tile of the large-tile path needs";
+    err = m.str();
+    return HIMUON_EBUDGET;
+  }
+  // chunks: consecutive GEMM tiles whose workspaces fit the budget together
+  std::vector<GemmChunk> chunks;
+  size_t ws_max = 0;
+  {
+    size_t cur = 0;
+    int64_t first = 0;
+    for (size_t i = 0; i < gt.size(); ++i) {
+      const size_t need = gemm_tile_workspace(gt[i].r, gt[i].s, prec);
+      if (cur + need > c.workspace_budget && i > (size_t)first) {
+        chunks.push_back(GemmChunk{first, (int64_t)i - first, cur});
+        ws_max = std::max(ws_max, cur);
+        first = (int64_t)i;
+        cur = 0;
+      }
+      const size_t base = cur;
+      const size_t xb = align256((size_t)gt[i].r * gt[i].s * 4);
+      const size_t ab = align256((size_t)gt[i].r * gt[i].r * 4);
+      gt[i].ws_x0 = (int64_t)base;
+      gt[i].ws_x1 = (int64_t)(base + xb);
+      gt[i].ws_a = (int64_t)(base + 2 * xb);
+      gt[i].ws_b = (int64_t)(base + 2 * xb + ab);
+      gt[i].ws_scale = (int64_t)(base + 2 * xb + 2 * ab);
+      cur += need;
+    }
+    if (!gt.empty()) {
+      chunks.push_back(GemmChunk{first, (int64_t)gt.size() - first, cur});
+      ws_max = std::max(ws_max, cur);
+    }
+  }
+
+  p.tile = tile;
+  p.ftiles.clear();
+  p.fgroups.clear();
+  const int edges[3] = {32, 64, 128};
+  for (int k = 0; k < 3; ++k) {
+    if (by_edge[k].empty()) continue;
+    p.fgroups.push_back(FusedGroup{edges[k], (int64_t)p.ftiles.size(), (int64_t)by_edge[k].size()});
+    p.ftiles.insert(p.ftiles.end(), by_edge[k].begin(), by_edge[k].end());
+  }
+  p.gtiles = std::move(gt);
+  p.chunks = std::move(chunks);
+  p.order = std::move(order);
+  p.workspace_bytes = ws_max;
+
+  himuon_stats &st = p.stats;
+  st = himuon_stats{};
+  st.tile = tile;
+  st.kernel_tile = p.fgroups.size() == 1 && p.gtiles.empty() ? p.fgroups[0].ts : 0;
+  st.layers = (int64_t)p.layers.size();
+  st.tiles = (int64_t)p.order.size();
+  st.fused_tiles = (int64_t)p.ftiles.size();
+  st.gemm_tiles = (int64_t)p.gtiles.size();
+  st.chunks = (int64_t)p.chunks.size();
+  st.workspace_bytes = ws_max;
+  st.table_bytes = p.ldesc.size() * sizeof(LayerDesc) + p.ftiles.size() * sizeof(FusedTile) +
+                   p.gtiles.size() * sizeof(GemmTile);
+  st.ns_flops = ns_flops;
+  st.issued_flops = issued;
+  st.step_bytes = bytes;
+  return HIMUON_OK;
+}
+
+}  // namespace himuon
