@@ -1,0 +1,194 @@
+"""Benchmark of one HiMuon optimizer step on one MI355X.
+
+Workload: the Llama-3-8B-shaped stack (32 layers of q/o 4096x4096, k/v 4096x1024,
+gate/up 4096x14336, down 14336x4096: 224 matrices, 6,979,321,856 parameters),
+bf16 momentum and gradient, fp32 master weights, T = 128, K = 5, quintic
+coefficients, workspace budget 4e9 bytes.  A step is momentum update, tiled
+Newton-Schulz and weight update over every matrix, inputs resident in HBM.
+
+Prints one JSON line.  `value` is the whole-step throughput in algorithmic NS
+TFLOP/s (sum over tiles of K (4 r^2 s + 2 r^3) per step / step time);
+`ms_per_step` is the step time.  A sweep over T (including FULL when the
+large-tile path is available) is reported in `sweep`.
+
+    python bench.py [--steps K] [--warmup W] [--tile T] [--sweep 32,64,128] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
+METRIC = "HiMuon step ms & NS TFLOP/s (% MFMA peak) vs T, 8B-shaped stack"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_inputs(shapes, device, seed0=3000):
+    import synth
+    import torch
+    t0 = time.time()
+    layers = synth.stack_inputs(shapes, seed0, device=device, state_dtype=torch.bfloat16,
+                                share_factors=True)
+    torch.cuda.synchronize()
+    log(f"[bench] generated {len(layers)} matrices in {time.time() - t0:.1f}s")
+    return layers
+
+
+def time_steps(opt, steps, warmup, lr=0.02):
+    """Times `steps` steps after `warmup` untimed ones with HIP events on the stream
+    the kernels are launched on; returns per-step milliseconds."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        opt.step(lr, stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        opt.step(lr, stream)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def cpu_baseline(K, coeffs, tile):
+    """The fp64 oracle on the host, on a bounded sample of the workload: one
+    4096 x 14336 matrix of the stack (3,584 tiles at T = 128), momentum + tiled NS +
+    update.  Throughput in algorithmic NS TFLOP/s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads") or 0) for i in threadpool_info()) or os.cpu_count()
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    rng = np.random.default_rng(0)
+    H, W = 4096, 14336
+    G = rng.standard_normal((H, W), dtype=np.float32) * 0.01
+    M = np.zeros((H, W), dtype=np.float32)
+    Wt = np.zeros((H, W), dtype=np.float32)
+    t0 = time.time()
+    oracle.step([(Wt, M, G)], tile, K, coeffs)
+    dt = time.time() - t0
+    fl = oracle.ns_flops([(H, W)], tile, K, coeffs)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one 4096x14336 matrix of the stack (T={tile}, K={K}, quintic, fp64 numpy), "
+                      f"{dt:.1f} s for {fl:.3e} NS flops; whole-step time at this rate "
+                      f"scales by the flop ratio",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tile", type=int, default=128)
+    ap.add_argument("--sweep", type=str, default="32,64")
+    ap.add_argument("--sweep-steps", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--workload", type=str, default="llama3-8b-32L")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the HiMuon step is tile-local and this build runs on "
+              "one MI355X; multi-GPU sharding is a design note only. Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import tiled_newton_schulz_tile_amd as hm
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    shapes = synth.STACKS[args.workload]
+    K, coeffs = 5, hm.QUINTIC
+    layers = build_inputs(shapes, dev)
+    opt = hm.HiMuon(layers, args.tile, K, coeffs, beta=0.95, eps=1e-7,
+                    workspace_budget=4 * 10 ** 9, precision=hm.PREC_BF16X3)
+    st = opt.stats()
+    log(f"[bench] plan: {st['tiles']} tiles, kernel tile {st['kernel_tile']}, "
+        f"{st['ns_flops']:.4e} NS flops/step, workspace {st['workspace_bytes']} B")
+    ms = time_steps(opt, args.steps, args.warmup)
+    ms_mean = sum(ms) / len(ms)
+    log(f"[bench] T={args.tile}: {ms_mean:.3f} ms/step (min {min(ms):.3f}, max {max(ms):.3f})")
+    tflops = st["ns_flops"] / (ms_mean * 1e-3) / 1e12
+    issued = st["issued_flops"] / (ms_mean * 1e-3) / 1e12
+    gbps = st["step_bytes"] / (ms_mean * 1e-3) / 1e9
+
+    sweep = [{"tile": args.tile, "ms": ms_mean, "ns_tflops": tflops,
+              "pct_mfma_peak": 100 * tflops / MFMA_BF16_PEAK_TFLOPS}]
+    for tok in [t for t in args.sweep.split(",") if t.strip()]:
+        T = 0 if tok.strip().lower() == "full" else int(tok)
+        if T == args.tile:
+            continue
+        try:
+            opt.set_tile_schedule(T)
+            s2 = opt.stats()
+            m2 = time_steps(opt, args.sweep_steps, 1)
+            m2 = sum(m2) / len(m2)
+            tf2 = s2["ns_flops"] / (m2 * 1e-3) / 1e12
+            sweep.append({"tile": "full" if T == 0 else T, "ms": m2, "ns_tflops": tf2,
+                          "pct_mfma_peak": 100 * tf2 / MFMA_BF16_PEAK_TFLOPS})
+            log(f"[bench] sweep T={tok}: {m2:.3f} ms/step, {tf2:.1f} NS TFLOP/s")
+        except hm.HiMuonError as e:
+            sweep.append({"tile": tok, "error": str(e)})
+            log(f"[bench] sweep T={tok}: {e}")
+    opt.close()
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] timing the oracle on the host (bounded sample)")
+        cpu = cpu_baseline(K, coeffs, args.tile)
+        log(f"[bench] oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads "
+            f"({cpu['seconds']:.1f}s)")
+        cpu.pop("seconds", None)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_mean, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "precision": "bf16x3: operands split hi+lo bf16, 3 MFMA products, fp32 accumulate",
+        "data": "synthetic: G = U diag(1/i) V^T + 0.01 N(0,1) per matrix (Haar U, V shared per "
+                "shape), M0 = 0, W0 = 0.02 N(0,1); seeded",
+        "config": {"workload": f"{args.workload} HiMuon step (Llama-3-8B-shaped stack, 224 "
+                               f"matrices, 6.98e9 params), T={args.tile}, K={K}, quintic",
+                   "tile": args.tile, "ns_steps": K, "coeffs": "quintic", "state_dtype": "bf16",
+                   "weight_dtype": "f32", "workspace_budget": 4 * 10 ** 9,
+                   "tiles": st["tiles"], "params": sum(h * w for h, w in shapes)},
+        "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        "issued_mfma_tflops": round(issued, 2),
+        "hbm_gbps": round(gbps, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "fused_step_kernel<128, bf16x3, bf16 state>",
+                     "launches_per_step": 1, "algorithmic_flops_per_launch": st["ns_flops"],
+                     "issued_flops_per_launch": st["issued_flops"],
+                     "algorithmic_bytes_per_launch": st["step_bytes"]},
+        "sweep": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
