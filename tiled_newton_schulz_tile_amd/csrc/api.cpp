@@ -154,8 +154,8 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
   const auto *dl = reinterpret_cast<const himuon::LayerDesc *>(p->d_buf);
   const auto *dft = reinterpret_cast<const himuon::FusedTile *>(p->d_buf + p->off_ftiles);
   for (const himuon::FusedGroup &g : pl.fgroups) {
-    hipError_t e = himuon::launch_fused(g.ts, (int)c.precision, c.state_dtype == HIMUON_BF16, dl,
-                                        dft + g.first, g.n, prm, stream);
+    hipError_t e = himuon::launch_fused(g.ts, (int)c.precision, c.state_dtype == HIMUON_BF16,
+                                        g.dense, dl, dft + g.first, g.n, prm, stream);
     if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
   }
   return HIMUON_OK;

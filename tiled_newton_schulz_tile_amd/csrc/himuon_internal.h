@@ -52,8 +52,9 @@ struct NSParams {
 
 // ---- launchers (ns_fused.hip) --------------------------------------------------
 // Runs momentum, K NS steps and the weight update for every tile of `tiles`
-// (device array of n FusedTile) with kernel tile edge ts in {32, 64, 128}.
-hipError_t launch_fused(int ts, int prec, int state_bf16, const LayerDesc *layers,
+// (device array of n FusedTile) with kernel tile edge ts in {32, 64, 128}.  dense:
+// every tile is exactly ts x ts with 16-byte aligned rows (no edge handling).
+hipError_t launch_fused(int ts, int prec, int state_bf16, bool dense, const LayerDesc *layers,
                         const FusedTile *tiles, int64_t n, const NSParams &p,
                         hipStream_t stream);
 

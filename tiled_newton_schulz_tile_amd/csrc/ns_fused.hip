@@ -24,8 +24,9 @@
 //   Gram    A[p][q]   = sum_k X[p][k] X[q][k]
 //   square  S[p][q]   = sum_k A[p][k] A[q][k]            (A symmetric)
 //   update  D[j][i]   = sum_k X[k][j] B[i][k] = (B X)^T  (B symmetric)
-// The update accumulates on top of a * X^T held in registers in MFMA output
-// layout, so X stays in fp32 between steps; only the MFMA operands are rounded.
+// With fp32 or split (hi + lo) operands, a is added to B's diagonal and the update is
+// one product X^T (a I + B); with plain bf16 operands the update accumulates on top of
+// a X^T held in fp32 registers, so only the product's operands are rounded.
 #include "himuon_internal.h"
 
 namespace himuon {
@@ -38,6 +39,21 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+#define GLOBAL_AS __attribute__((address_space(1)))
+#define LDS_AS __attribute__((address_space(3)))
+
+// Global-memory views of the caller's pointers (global_load/store instead of flat).
+template <class T>
+__device__ __forceinline__ GLOBAL_AS T *gmem(T *p) {
+  return (GLOBAL_AS T *)p;
+}
+template <class T>
+__device__ __forceinline__ const GLOBAL_AS T *gmem(const T *p) {
+  return (const GLOBAL_AS T *)p;
+}
 
 // A wave's accumulators: NB x NB MFMA 32x32 output blocks.
 template <int NB>
@@ -79,7 +95,7 @@ struct Mat<PREC_BF16X3> {
 };
 
 template <int TS, int PREC>
-__device__ inline Mat<PREC> make_mat(char *base) {
+__device__ __forceinline__ Mat<PREC> make_mat(char *base) {
   Mat<PREC> m;
   if constexpr (PREC == PREC_F32) {
     m.f = reinterpret_cast<float *>(base);
@@ -94,9 +110,11 @@ __device__ inline Mat<PREC> make_mat(char *base) {
 
 // Synchronise the threads that share one tile.
 template <int WPT>
-__device__ inline void tile_sync() {
+__device__ __forceinline__ void tile_sync() {
   if constexpr (WPT > 1) {
-    __syncthreads();
+    // this wave's LDS traffic is complete, then meet the other waves of the tile;
+    // global loads in flight (the next tile's prefetch) are deliberately not waited for
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   } else {
     // one wave per tile: LDS traffic of a wave is processed in order; only the
     // compiler has to be kept from moving LDS accesses across this point
@@ -106,100 +124,119 @@ __device__ inline void tile_sync() {
   }
 }
 
-__device__ inline f32x16 mma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+__device__ __forceinline__ f32x16 mma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ inline f32x16 mma_f32(float a, float b, f32x16 c) {
+__device__ __forceinline__ f32x16 mma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// 8 bf16 of column j, rows k..k+7 (row pitch PB)
+// MFMA operand of a transposed row-major bf16 matrix: lane l receives
+// buf[k .. k+7][m + l % 32] (k already includes the lane half's k offset).
+// ds_read_tr16_b64 works on groups of 16 lanes: lane i of a group receives element
+// i % 4 of the 8-byte chunks read by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.  So lane
+// L reads 4 consecutive columns of row k + L/4 and receives column L of rows k..k+3.
 template <int PB>
-__device__ inline bf16x8 gather_col_bf16(const __bf16 *buf, int k, int j) {
-  const unsigned short *p = reinterpret_cast<const unsigned short *>(buf) + k * PB + j;
-  u16x8 v;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = p[e * PB];
+__device__ __forceinline__ bf16x8 tr_frag(const __bf16 *buf, int k, int m, int lane) {
+  const int L = lane & 15, g = (lane >> 4) & 1;
+  const __bf16 *p = buf + (k + (L >> 2)) * PB + m + 16 * g + 4 * (L & 3);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(p));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(p + 4 * PB));
+  const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
 
 // ------------------------------------------------------------------ wave GEMM
-// acc.b[bi][bj] += sum_k L(m, k) R(n, k) for m in the wave's L block, n in its R block.
+// acc.b[bi][bj] (+)= sum_k L(m, k) R(n, k) for m in the wave's L block, n in its R block.
 // L(m, k) = Lmat[m][k] (TRANS_L false) or Lmat[k][m] (TRANS_L true); R(n, k) = Rmat[n][k].
 // MFMA lane layout (32x32): operand lane l holds row (l % 32) of its 32-block and a
 // run of contiguous k selected by l / 32; both operands use the same k runs.
-template <int TS, int PREC, bool TRANS_L>
-__device__ inline void wave_gemm(Acc<Geo<TS, PREC>::NB> &acc, const Mat<PREC> &Lm, int l0, const Mat<PREC> &Rm, int r0,
-                                 int lane) {
+// ZERO: this chunk starts the sum (the accumulators are not read).
+template <int TS, int PREC, bool TRANS_L, bool ZERO>
+__device__ __forceinline__ void gemm_chunk(Acc<Geo<TS, PREC>::NB> &acc, const Mat<PREC> &Lm, int l0,
+                                           const Mat<PREC> &Rm, int r0, int lane, int kb) {
   using G = Geo<TS, PREC>;
   constexpr int NB = G::NB;
   const int li = lane & 31, half = lane >> 5;
   if constexpr (PREC == PREC_F32) {
     constexpr int PF = G::PF;
-#pragma unroll 2
-    for (int kb = 0; kb < TS; kb += 8) {
-      const int k = kb + 4 * half;
-      f32x4 lf[NB], rf[NB];
+    const int k = kb + 4 * half;
+    f32x4 lf[NB], rf[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int m = l0 + b * 32 + li;
-        if constexpr (TRANS_L) {
+    for (int b = 0; b < NB; ++b) {
+      const int m = l0 + b * 32 + li;
+      if constexpr (TRANS_L) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) lf[b][e] = Lm.f[(k + e) * PF + m];
-        } else {
-          lf[b] = *reinterpret_cast<const f32x4 *>(Lm.f + m * PF + k);
-        }
-        rf[b] = *reinterpret_cast<const f32x4 *>(Rm.f + (r0 + b * 32 + li) * PF + k);
+        for (int e = 0; e < 4; ++e) lf[b][e] = Lm.f[(k + e) * PF + m];
+      } else {
+        lf[b] = *reinterpret_cast<const f32x4 *>(Lm.f + m * PF + k);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-          for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = mma_f32(lf[bi][e], rf[bj][e], acc.b[bi][bj]);
+      rf[b] = *reinterpret_cast<const f32x4 *>(Rm.f + (r0 + b * 32 + li) * PF + k);
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj)
+          acc.b[bi][bj] = mma_f32(lf[bi][e], rf[bj][e], (ZERO && e == 0) ? f32x16{} : acc.b[bi][bj]);
   } else {
     constexpr int PB = G::PB;
-#pragma unroll 2
-    for (int kb = 0; kb < TS; kb += 16) {
-      const int k = kb + 8 * half;
-      bf16x8 lh[NB], rh[NB];
-      bf16x8 ll[NB], rl[NB];
+    const int k = kb + 8 * half;
+    bf16x8 lh[NB], rh[NB];
+    bf16x8 ll[NB], rl[NB];
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int m = l0 + b * 32 + li;
-        const int n = r0 + b * 32 + li;
-        if constexpr (TRANS_L) {
-          lh[b] = gather_col_bf16<PB>(Lm.hi, k, m);
-        } else {
-          lh[b] = *reinterpret_cast<const bf16x8 *>(Lm.hi + m * PB + k);
-        }
-        rh[b] = *reinterpret_cast<const bf16x8 *>(Rm.hi + n * PB + k);
-        if constexpr (PREC == PREC_BF16X3) {
-          if constexpr (TRANS_L) {
-            ll[b] = gather_col_bf16<PB>(Lm.lo, k, m);
-          } else {
-            ll[b] = *reinterpret_cast<const bf16x8 *>(Lm.lo + m * PB + k);
-          }
-          rl[b] = *reinterpret_cast<const bf16x8 *>(Rm.lo + n * PB + k);
-        }
+    for (int b = 0; b < NB; ++b) {
+      const int m = l0 + b * 32 + li;
+      const int n = r0 + b * 32 + li;
+      if constexpr (TRANS_L) {
+        lh[b] = tr_frag<PB>(Lm.hi, k, l0 + b * 32, lane);
+      } else {
+        lh[b] = *reinterpret_cast<const bf16x8 *>(Lm.hi + m * PB + k);
       }
+      rh[b] = *reinterpret_cast<const bf16x8 *>(Rm.hi + n * PB + k);
       if constexpr (PREC == PREC_BF16X3) {
-#pragma unroll
-        for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-          for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = mma_bf16(ll[bi], rh[bj], acc.b[bi][bj]);
-#pragma unroll
-        for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-          for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = mma_bf16(lh[bi], rl[bj], acc.b[bi][bj]);
+        if constexpr (TRANS_L) {
+          ll[b] = tr_frag<PB>(Lm.lo, k, l0 + b * 32, lane);
+        } else {
+          ll[b] = *reinterpret_cast<const bf16x8 *>(Lm.lo + m * PB + k);
+        }
+        rl[b] = *reinterpret_cast<const bf16x8 *>(Rm.lo + n * PB + k);
       }
+    }
+    if constexpr (PREC == PREC_BF16X3) {
+      // small cross terms first: lo * hi + hi * lo + hi * hi
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj)
+          acc.b[bi][bj] = mma_bf16(ll[bi], rh[bj], ZERO ? f32x16{} : acc.b[bi][bj]);
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = mma_bf16(lh[bi], rl[bj], acc.b[bi][bj]);
 #pragma unroll
       for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
         for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = mma_bf16(lh[bi], rh[bj], acc.b[bi][bj]);
+    } else {
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj)
+          acc.b[bi][bj] = mma_bf16(lh[bi], rh[bj], ZERO ? f32x16{} : acc.b[bi][bj]);
     }
   }
+}
+
+// Full K = TS contraction; ZERO: start from zero, else accumulate onto acc.
+template <int TS, int PREC, bool TRANS_L, bool ZERO>
+__device__ __forceinline__ void wave_gemm(Acc<Geo<TS, PREC>::NB> &acc, const Mat<PREC> &Lm, int l0,
+                                          const Mat<PREC> &Rm, int r0, int lane) {
+  constexpr int KC = PREC == PREC_F32 ? 8 : 16;
+  gemm_chunk<TS, PREC, TRANS_L, ZERO>(acc, Lm, l0, Rm, r0, lane, 0);
+#pragma unroll 2
+  for (int kb = KC; kb < TS; kb += KC) gemm_chunk<TS, PREC, TRANS_L, false>(acc, Lm, l0, Rm, r0, lane, kb);
 }
 
 // Element (bi, bj, r) of a wave's accumulators sits at
@@ -209,8 +246,11 @@ __device__ inline void wave_gemm(Acc<Geo<TS, PREC>::NB> &acc, const Mat<PREC> &L
 // transpose of the accumulator block.
 
 // Store the transpose of the accumulators into a matrix in the precision's format.
-template <int TS, int PREC>
-__device__ inline void store_acc_t(const Acc<Geo<TS, PREC>::NB> &acc, const Mat<PREC> &m, int p0, int q0, int lane) {
+// SCALE: the stored value is s_store * acc; BACK: afterwards acc <- s_back * acc (one pass
+// over the accumulators serves both).
+template <int TS, int PREC, bool SCALE = false, bool BACK = false>
+__device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NB> &acc, const Mat<PREC> &m, int p0, int q0,
+                                            int lane, float s_store = 1.f, float s_back = 1.f) {
   using G = Geo<TS, PREC>;
   constexpr int NB = G::NB;
   const int li = lane & 31, half = lane >> 5;
@@ -222,8 +262,13 @@ __device__ inline void store_acc_t(const Acc<Geo<TS, PREC>::NB> &acc, const Mat<
       for (int g = 0; g < 4; ++g) {
         const int row = p0 + bi * 32 + 8 * g + 4 * half;
         const int col = q0 + bj * 32 + li;
-        f32x4 v = {acc.b[bi][bj][4 * g + 0], acc.b[bi][bj][4 * g + 1], acc.b[bi][bj][4 * g + 2],
-                   acc.b[bi][bj][4 * g + 3]};
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = acc.b[bi][bj][4 * g + e];
+          v[e] = SCALE ? x * s_store : x;
+          if constexpr (BACK) acc.b[bi][bj][4 * g + e] = x * s_back;
+        }
         if constexpr (PREC == PREC_F32) {
           *reinterpret_cast<f32x4 *>(m.f + col * G::PF + row) = v;
         } else {
@@ -241,9 +286,26 @@ __device__ inline void store_acc_t(const Acc<Geo<TS, PREC>::NB> &acc, const Mat<
       }
 }
 
+// m[i][i] += d on the diagonal of the wave's block (diagonal blocks only).  Each diagonal
+// element was written by this same wave, and LDS accesses of one wave complete in order.
+template <int TS, int PREC>
+__device__ __forceinline__ void add_diag(const Mat<PREC> &m, int p0, int q0, int lane, float d) {
+  using G = Geo<TS, PREC>;
+  if (p0 != q0 || lane >= G::WB) return;
+  const int i = p0 + lane;
+  if constexpr (PREC == PREC_F32) {
+    m.f[i * G::PF + i] += d;
+  } else {
+    const float v = (float)m.hi[i * G::PB + i] + (float)m.lo[i * G::PB + i] + d;
+    const __bf16 hi = (__bf16)v;
+    m.hi[i * G::PB + i] = hi;
+    m.lo[i * G::PB + i] = (__bf16)(v - (float)hi);
+  }
+}
+
 // fp32 staging (pitch PF) <-> accumulators, transposed as above; load scales by s.
 template <int TS, int PREC>
-__device__ inline void load_acc_t(Acc<Geo<TS, PREC>::NB> &acc, const float *st, int p0, int q0, int lane, float s) {
+__device__ __forceinline__ void load_acc_t(Acc<Geo<TS, PREC>::NB> &acc, const float *st, int p0, int q0, int lane, float s) {
   using G = Geo<TS, PREC>;
   const int li = lane & 31, half = lane >> 5;
 #pragma unroll
@@ -261,7 +323,7 @@ __device__ inline void load_acc_t(Acc<Geo<TS, PREC>::NB> &acc, const float *st, 
 }
 
 template <int TS, int PREC>
-__device__ inline void store_acc_t_f32(const Acc<Geo<TS, PREC>::NB> &acc, float *st, int p0, int q0, int lane) {
+__device__ __forceinline__ void store_acc_t_f32(const Acc<Geo<TS, PREC>::NB> &acc, float *st, int p0, int q0, int lane) {
   using G = Geo<TS, PREC>;
   const int li = lane & 31, half = lane >> 5;
 #pragma unroll
@@ -285,7 +347,7 @@ struct Chunk8;
 template <>
 struct Chunk8<__bf16> {
   u32x4 v;
-  __device__ float get(int e) const {
+  __device__ __forceinline__ float get(int e) const {
     const unsigned int w = v[e >> 1];
     return __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
   }
@@ -293,30 +355,33 @@ struct Chunk8<__bf16> {
 template <>
 struct Chunk8<float> {
   f32x4 a, b;
-  __device__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
+  __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
 };
 
+// n (0..8) valid elements at p; the rest read as zero
 template <typename S>
-__device__ inline Chunk8<S> load_chunk(const S *p, int n, bool vec) {
+__device__ __forceinline__ Chunk8<S> load_chunk(const S *p, int n, bool vec) {
   Chunk8<S> c;
   if constexpr (sizeof(S) == 2) {
     if (vec && n == 8) {
-      c.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+      c.v = __builtin_nontemporal_load(gmem(reinterpret_cast<const u32x4 *>(p)));
     } else {
+      const GLOBAL_AS unsigned short *q = gmem(reinterpret_cast<const unsigned short *>(p));
       unsigned short t[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t[e] = e < n ? reinterpret_cast<const unsigned short *>(p)[e] : 0;
+      for (int e = 0; e < 8; ++e) t[e] = e < n ? q[e] : 0;
       c.v = u32x4{t[0] | (unsigned)t[1] << 16, t[2] | (unsigned)t[3] << 16,
                   t[4] | (unsigned)t[5] << 16, t[6] | (unsigned)t[7] << 16};
     }
   } else {
     if (vec && n == 8) {
-      c.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-      c.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p) + 1);
+      c.a = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4 *>(p)));
+      c.b = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4 *>(p) + 1));
     } else {
+      const GLOBAL_AS float *q = gmem(p);
       float t[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) t[e] = e < n ? p[e] : 0.f;
+      for (int e = 0; e < 8; ++e) t[e] = e < n ? q[e] : 0.f;
       c.a = f32x4{t[0], t[1], t[2], t[3]};
       c.b = f32x4{t[4], t[5], t[6], t[7]};
     }
@@ -324,308 +389,399 @@ __device__ inline Chunk8<S> load_chunk(const S *p, int n, bool vec) {
   return c;
 }
 
-// Round an fp32 value to the state dtype; returns the stored code and its value.
-__device__ inline unsigned short to_bf16_bits(float x) {
+template <typename S>
+__device__ __forceinline__ Chunk8<S> load_chunk_vec(const S *p) {
+  Chunk8<S> c;
+  if constexpr (sizeof(S) == 2) {
+    c.v = __builtin_nontemporal_load(gmem(reinterpret_cast<const u32x4 *>(p)));
+  } else {
+    c.a = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4 *>(p)));
+    c.b = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4 *>(p) + 1));
+  }
+  return c;
+}
+
+__device__ __forceinline__ unsigned short to_bf16_bits(float x) {
   return __builtin_bit_cast(unsigned short, (__bf16)x);
 }
 
+__device__ __forceinline__ int clamp_n(int n, int hi) { return n < 0 ? 0 : (n > hi ? hi : n); }
+
+// Per-thread share of one tile's HBM traffic: GM_IT chunks of 8 state elements of G and
+// of M (momentum prologue), W_IT chunks of 4 weights (update epilogue).  Chunk q of a
+// thread covers tile row q / (TS/8), columns 8 (q % (TS/8)) .. +7 (resp. 4-wide for W).
+template <int TS, int NT, typename S>
+struct TileRegs {
+  static constexpr int CPR = TS / 8, GM_IT = TS * CPR / NT;
+  static constexpr int WPR = TS / 4, W_IT = TS * WPR / NT;
+  Chunk8<S> g[GM_IT], m[GM_IT];
+  f32x4 w[W_IT];
+
+  // DENSE: the tile fills TS x TS and its rows are 16-byte aligned, so every chunk is a
+  // full vector access and the code has no data-dependent branches (a branch merge
+  // would make the compiler wait for the loads in flight).
+  template <bool DENSE>
+  __device__ __forceinline__ void load_gm(const FusedTile &t, const LayerDesc &L, int gt) {
+    const S *mb = reinterpret_cast<const S *>(L.m);
+    const S *gb = reinterpret_cast<const S *>(L.g);
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int i = 0; i < GM_IT; ++i) {
+        const int q = gt + i * NT;
+        const int r = q / CPR, c = (q % CPR) * 8;
+        const int64_t gr = (int64_t)(t.row0 + r);
+        g[i] = load_chunk_vec<S>(gb + gr * L.ld_g + t.col0 + c);
+        m[i] = load_chunk_vec<S>(mb + gr * L.ld_m + t.col0 + c);
+      }
+      return;
+    }
+    const bool vec = L.vec_ok && (t.col0 % 8 == 0);
+#pragma unroll
+    for (int i = 0; i < GM_IT; ++i) {
+      const int q = gt + i * NT;
+      const int r = q / CPR, c = (q % CPR) * 8;
+      const int n = r < t.h ? clamp_n(t.w - c, 8) : 0;
+      const int64_t gr = (int64_t)(t.row0 + r);
+      g[i] = load_chunk<S>(gb + gr * L.ld_g + t.col0 + c, n, vec);
+      m[i] = load_chunk<S>(mb + gr * L.ld_m + t.col0 + c, n, vec);
+    }
+  }
+
+  template <bool DENSE>
+  __device__ __forceinline__ void load_w(const FusedTile &t, const LayerDesc &L, int gt) {
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int i = 0; i < W_IT; ++i) {
+        const int q = gt + i * NT;
+        const int r = q / WPR, c = (q % WPR) * 4;
+        const float *src = L.w + (int64_t)(t.row0 + r) * L.ld_w + t.col0 + c;
+        w[i] = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4 *>(src)));
+      }
+      return;
+    }
+    const bool vec = L.vec_w && (t.col0 % 4 == 0);
+#pragma unroll
+    for (int i = 0; i < W_IT; ++i) {
+      const int q = gt + i * NT;
+      const int r = q / WPR, c = (q % WPR) * 4;
+      const int n = r < t.h ? clamp_n(t.w - c, 4) : 0;
+      const float *src = L.w + (int64_t)(t.row0 + r) * L.ld_w + t.col0 + c;
+      if (vec && n == 4) {
+        w[i] = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4 *>(src)));
+      } else {
+        const GLOBAL_AS float *q4 = gmem(src);
+        float tmp[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tmp[e] = e < n ? q4[e] : 0.f;
+        w[i] = f32x4{tmp[0], tmp[1], tmp[2], tmp[3]};
+      }
+    }
+  }
+
+  // M <- beta M + G: store the new momentum and stage its values, oriented on the
+  // short side and zero padded, as fp32 TS x TS (pitch PF) in LDS.
+  template <int PF, bool DENSE>
+  __device__ __forceinline__ void momentum(const FusedTile &t, const LayerDesc &L, int gt, float beta, float *st) const {
+    S *mb = reinterpret_cast<S *>(L.m);
+    const bool vec = DENSE || (L.vec_ok && (t.col0 % 8 == 0));
+    const bool tall = !DENSE && t.h > t.w;
+#pragma unroll
+    for (int i = 0; i < GM_IT; ++i) {
+      const int q = gt + i * NT;
+      const int r = q / CPR, c = (q % CPR) * 8;
+      const int n = DENSE ? 8 : (r < t.h ? clamp_n(t.w - c, 8) : 0);
+      S *dst = mb + (int64_t)(t.row0 + r) * L.ld_m + t.col0 + c;
+      float v[8];
+      if constexpr (sizeof(S) == 2) {
+        unsigned short code[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          code[e] = to_bf16_bits(__builtin_fmaf(beta, m[i].get(e), g[i].get(e)));
+          v[e] = __builtin_bit_cast(float, (unsigned)code[e] << 16);
+        }
+        if (vec && n == 8) {
+          *gmem(reinterpret_cast<u32x4 *>(dst)) =
+              u32x4{code[0] | (unsigned)code[1] << 16, code[2] | (unsigned)code[3] << 16,
+                    code[4] | (unsigned)code[5] << 16, code[6] | (unsigned)code[7] << 16};
+        } else {
+          GLOBAL_AS unsigned short *d16 = gmem(reinterpret_cast<unsigned short *>(dst));
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < n) d16[e] = code[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(beta, m[i].get(e), g[i].get(e));
+        if (vec && n == 8) {
+          gmem(reinterpret_cast<f32x4 *>(dst))[0] = f32x4{v[0], v[1], v[2], v[3]};
+          gmem(reinterpret_cast<f32x4 *>(dst))[1] = f32x4{v[4], v[5], v[6], v[7]};
+        } else {
+          GLOBAL_AS float *d32 = gmem(dst);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e < n) d32[e] = v[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e >= n) v[e] = 0.f;  // zero padding
+      if (!tall) {
+        *reinterpret_cast<f32x4 *>(st + r * PF + c) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4 *>(st + r * PF + c + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st[(c + e) * PF + r] = v[e];
+      }
+    }
+  }
+
+  // W <- W - lr O (and U <- O) from the staged fp32 output tile.
+  template <int PF, bool DENSE>
+  __device__ __forceinline__ void update(const FusedTile &t, const LayerDesc &L, int gt, float lr, bool write_u,
+                         const float *st) const {
+    const bool vec = DENSE || (L.vec_w && (t.col0 % 4 == 0));
+    const bool tall = !DENSE && t.h > t.w;
+    const float nlr = -lr;
+#pragma unroll
+    for (int i = 0; i < W_IT; ++i) {
+      const int q = gt + i * NT;
+      const int r = q / WPR, c = (q % WPR) * 4;
+      const int n = DENSE ? 4 : (r < t.h ? clamp_n(t.w - c, 4) : 0);
+      if (n == 0) continue;
+      float o[4];
+      if (!tall) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(st + r * PF + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = v[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = st[(c + e) * PF + r];
+      }
+      float nw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) nw[e] = __builtin_fmaf(nlr, o[e], w[i][e]);
+      GLOBAL_AS float *dst = gmem(L.w + (int64_t)(t.row0 + r) * L.ld_w + t.col0 + c);
+      if (vec && n == 4) {
+        *reinterpret_cast<GLOBAL_AS f32x4 *>(dst) = f32x4{nw[0], nw[1], nw[2], nw[3]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e < n) dst[e] = nw[e];
+      }
+      if (write_u) {
+        GLOBAL_AS float *ud = gmem(L.u + (int64_t)(t.row0 + r) * L.ld_u + t.col0 + c);
+        if (vec && n == 4) {
+          *reinterpret_cast<GLOBAL_AS f32x4 *>(ud) = f32x4{o[0], o[1], o[2], o[3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e < n) ud[e] = o[e];
+        }
+      }
+    }
+  }
+};
+
 // ------------------------------------------------------------------ the kernel
-template <int TS, int PREC, typename S>
+// Persistent: each tile group of a workgroup walks tiles tix, tix + stride, ...  While
+// tile i iterates, the loads of tile i+1's G and M are in flight (bf16 state), so their
+// HBM latency hides behind the MFMA work.
+template <int TS, int PREC, typename S, bool DENSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, Geo<TS, PREC>::THREADS)))
 __attribute__((amdgpu_waves_per_eu(1, 2)))
 void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__restrict__ tiles,
                        int64_t ntiles, NSParams prm) {
   using G = Geo<TS, PREC>;
   constexpr int NT = G::NT, NB = G::NB, WB = G::WB, PF = G::PF;
+  constexpr bool PREFETCH = sizeof(S) == 2;
   __shared__ __attribute__((aligned(16))) char lds[G::TPB * G::TILE_LDS];
   __shared__ float red[G::TPB][G::WPT];
 
-  const int grp = threadIdx.x / NT;          // tile slot in the workgroup
-  const int gt = threadIdx.x % NT;           // thread within the tile group
+  const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / NT);  // tile slot in the workgroup
+  const int gt = threadIdx.x % NT;                                     // thread within the tile group
   const int lane = threadIdx.x & 63;
-  const int wv = gt >> 6;                    // wave within the tile group
-  const int64_t tix = (int64_t)blockIdx.x * G::TPB + grp;
-  if (tix >= ntiles) return;                 // uniform per tile group
+  const int wv = __builtin_amdgcn_readfirstlane(gt >> 6);             // wave within the tile group
+  const int64_t stride = (int64_t)gridDim.x * G::TPB;
+  int64_t tix = (int64_t)blockIdx.x * G::TPB + grp;
+  if (tix >= ntiles) return;                                           // uniform per tile group
 
-  const FusedTile t = tiles[tix];
-  const LayerDesc L = layers[t.layer];
-  const int h = t.h, w = t.w;
-  const bool tall = h > w;
   char *area = lds + grp * G::TILE_LDS;
   float *st = reinterpret_cast<float *>(area);          // fp32 staging, TS x PF
   const Mat<PREC> X = make_mat<TS, PREC>(area);
   const Mat<PREC> AB = make_mat<TS, PREC>(area + G::REGION);
   const int p0 = (wv / (TS / WB)) * WB;                  // wave block origin
   const int q0 = (wv % (TS / WB)) * WB;
-
-  // ---- momentum and staging of the oriented, zero-padded tile ---------------
-  {
-    constexpr int CPR = TS / 8;
-    constexpr int ITER = TS * CPR / NT;                  // chunks per thread
-    constexpr int BATCH = ITER < 4 ? ITER : 4;
-    S *mbase = reinterpret_cast<S *>(L.m);
-    const S *gbase = reinterpret_cast<const S *>(L.g);
-    const bool vec = L.vec_ok && (t.col0 % 8 == 0);
-#pragma unroll
-    for (int b0 = 0; b0 < ITER; b0 += BATCH) {
-      Chunk8<S> cg[BATCH], cm[BATCH];
-      int nn[BATCH];
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        const int q = gt + (b0 + i) * NT;
-        const int r = q / CPR, c = (q % CPR) * 8;
-        int n = r < h ? w - c : 0;
-        n = n < 0 ? 0 : (n > 8 ? 8 : n);
-        nn[i] = n;
-        const int64_t gr = (int64_t)(t.row0 + r);
-        cg[i] = load_chunk<S>(gbase + gr * L.ld_g + t.col0 + c, n, vec);
-        cm[i] = load_chunk<S>(mbase + gr * L.ld_m + t.col0 + c, n, vec);
-      }
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        const int q = gt + (b0 + i) * NT;
-        const int r = q / CPR, c = (q % CPR) * 8;
-        const int n = nn[i];
-        float v[8];
-        Chunk8<S> out;
-        if constexpr (sizeof(S) == 2) {
-          unsigned short code[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            code[e] = to_bf16_bits(__builtin_fmaf(prm.beta, cm[i].get(e), cg[i].get(e)));
-            v[e] = __builtin_bit_cast(float, (unsigned)code[e] << 16);
-          }
-          out.v = u32x4{code[0] | (unsigned)code[1] << 16, code[2] | (unsigned)code[3] << 16,
-                        code[4] | (unsigned)code[5] << 16, code[6] | (unsigned)code[7] << 16};
-          S *dst = mbase + (int64_t)(t.row0 + r) * L.ld_m + t.col0 + c;
-          if (vec && n == 8) {
-            *reinterpret_cast<u32x4 *>(dst) = out.v;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (e < n) reinterpret_cast<unsigned short *>(dst)[e] = code[e];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(prm.beta, cm[i].get(e), cg[i].get(e));
-          S *dst = mbase + (int64_t)(t.row0 + r) * L.ld_m + t.col0 + c;
-          if (vec && n == 8) {
-            reinterpret_cast<f32x4 *>(dst)[0] = f32x4{v[0], v[1], v[2], v[3]};
-            reinterpret_cast<f32x4 *>(dst)[1] = f32x4{v[4], v[5], v[6], v[7]};
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (e < n) dst[e] = v[e];
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e >= n) v[e] = 0.f;                        // zero padding
-        if (!tall) {
-          *reinterpret_cast<f32x4 *>(st + r * PF + c) = f32x4{v[0], v[1], v[2], v[3]};
-          *reinterpret_cast<f32x4 *>(st + r * PF + c + 4) = f32x4{v[4], v[5], v[6], v[7]};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) st[(c + e) * PF + r] = v[e];
-        }
-      }
-    }
-  }
-  tile_sync<G::WPT>();
-
-  // ---- Frobenius norm of the oriented tile, fixed summation order -----------
-  float inv;
-  {
-    float ss = 0.f;
-    constexpr int C4 = TS * TS / 4;
-#pragma unroll 4
-    for (int q = gt; q < C4; q += NT) {
-      const int r = q / (TS / 4), c = (q % (TS / 4)) * 4;
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(st + r * PF + c);
-      ss = __builtin_fmaf(v[0], v[0], ss);
-      ss = __builtin_fmaf(v[1], v[1], ss);
-      ss = __builtin_fmaf(v[2], v[2], ss);
-      ss = __builtin_fmaf(v[3], v[3], ss);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-    if constexpr (G::WPT > 1) {
-      if (lane == 0) red[grp][wv] = ss;
-      tile_sync<G::WPT>();
-      ss = red[grp][0];
-#pragma unroll
-      for (int i = 1; i < G::WPT; ++i) ss += red[grp][i];
-    }
-    inv = 1.0f / (__builtin_sqrtf(ss) + prm.eps);
-  }
-
-  // X in registers (fp32, MFMA output layout of the update product: block holds X^T)
-  Acc<NB> xr;
-  load_acc_t<TS, PREC>(xr, st, p0, q0, lane, inv);
-  tile_sync<G::WPT>();
-  store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
-  tile_sync<G::WPT>();
-
-  // ---- K Newton-Schulz steps --------------------------------------------------
   const float ca = prm.a, cb = prm.b, cc = prm.c;
-  for (int it = 0; it < prm.steps; ++it) {
-    Acc<NB> acc;
-#pragma unroll
-    for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-      for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = f32x16{};
-    wave_gemm<TS, PREC, false>(acc, X, p0, X, q0, lane);           // A = X X^T
-    if (cc != 0.f) {
-      store_acc_t<TS, PREC>(acc, AB, p0, q0, lane);                  // A is symmetric
-      tile_sync<G::WPT>();
-      Acc<NB> sq;
-#pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < NB; ++bj) sq.b[bi][bj] = f32x16{};
-      wave_gemm<TS, PREC, false>(sq, AB, p0, AB, q0, lane);         // A^2 = A A^T
-#pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < NB; ++bj)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            acc.b[bi][bj][e] = __builtin_fmaf(cc, sq.b[bi][bj][e], cb * acc.b[bi][bj][e]);
-      tile_sync<G::WPT>();                                           // A fully read
-    } else {
-#pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < NB; ++bj)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc.b[bi][bj][e] *= cb;
-    }
-    store_acc_t<TS, PREC>(acc, AB, p0, q0, lane);                    // B (symmetric)
-#pragma unroll
-    for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-      for (int bj = 0; bj < NB; ++bj)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) xr.b[bi][bj][e] *= ca;
-    tile_sync<G::WPT>();
-    wave_gemm<TS, PREC, true>(xr, X, p0, AB, q0, lane);             // X^T <- a X^T + X^T B
-    tile_sync<G::WPT>();
-    if (it + 1 < prm.steps) {
-      store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
-      tile_sync<G::WPT>();
-    }
-  }
 
-  // ---- reassembly and weight update ------------------------------------------
-  tile_sync<G::WPT>();
-  store_acc_t_f32<TS, PREC>(xr, st, p0, q0, lane);
-  tile_sync<G::WPT>();
-  {
-    constexpr int CPR = TS / 4;
-    constexpr int ITER = TS * CPR / NT;
-    constexpr int BATCH = ITER < 8 ? ITER : 8;
-    const bool vec = L.vec_w && (t.col0 % 4 == 0);
-    const float nlr = -prm.lr;
-#pragma unroll
-    for (int b0 = 0; b0 < ITER; b0 += BATCH) {
-      f32x4 wv4[BATCH];
-      int nn[BATCH];
-#pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        const int q = gt + (b0 + i) * NT;
-        const int r = q / CPR, c = (q % CPR) * 4;
-        int n = r < h ? w - c : 0;
-        n = n < 0 ? 0 : (n > 4 ? 4 : n);
-        nn[i] = n;
-        const float *src = L.w + (int64_t)(t.row0 + r) * L.ld_w + t.col0 + c;
-        if (vec && n == 4) {
-          wv4[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(src));
-        } else {
-          float tmp[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) tmp[e] = e < n ? src[e] : 0.f;
-          wv4[i] = f32x4{tmp[0], tmp[1], tmp[2], tmp[3]};
-        }
+  TileRegs<TS, NT, S> io;
+  FusedTile t = tiles[tix];
+  LayerDesc L = layers[t.layer];
+  io.template load_gm<DENSE>(t, L, gt);
+
+  while (true) {
+    // ---- momentum and staging of the oriented, zero-padded tile -------------
+    io.template momentum<PF, DENSE>(t, L, gt, prm.beta, st);
+    const int64_t nxt = tix + stride;
+    FusedTile tn = t;
+    LayerDesc Ln = L;
+    if constexpr (PREFETCH) {
+      if (nxt < ntiles) {
+        tn = tiles[nxt];
+        Ln = layers[tn.layer];
+        io.template load_gm<DENSE>(tn, Ln, gt);
+      }
+    }
+    tile_sync<G::WPT>();
+
+    // ---- Frobenius norm of the oriented tile, fixed summation order ---------
+    float inv;
+    {
+      float ss = 0.f;
+      constexpr int C4 = TS * TS / 4;
+#pragma unroll 4
+      for (int q = gt; q < C4; q += NT) {
+        const int r = q / (TS / 4), c = (q % (TS / 4)) * 4;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(st + r * PF + c);
+        ss = __builtin_fmaf(v[0], v[0], ss);
+        ss = __builtin_fmaf(v[1], v[1], ss);
+        ss = __builtin_fmaf(v[2], v[2], ss);
+        ss = __builtin_fmaf(v[3], v[3], ss);
       }
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        const int q = gt + (b0 + i) * NT;
-        const int r = q / CPR, c = (q % CPR) * 4;
-        const int n = nn[i];
-        if (n == 0) continue;
-        float o[4];
-        if (!tall) {
-          const f32x4 v = *reinterpret_cast<const f32x4 *>(st + r * PF + c);
+      for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+      if constexpr (G::WPT > 1) {
+        if (lane == 0) red[grp][wv] = ss;
+        tile_sync<G::WPT>();
+        ss = red[grp][0];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = v[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = st[(c + e) * PF + r];
-        }
-        float *dst = L.w + (int64_t)(t.row0 + r) * L.ld_w + t.col0 + c;
-        float nw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) nw[e] = __builtin_fmaf(nlr, o[e], wv4[i][e]);
-        if (vec && n == 4) {
-          *reinterpret_cast<f32x4 *>(dst) = f32x4{nw[0], nw[1], nw[2], nw[3]};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (e < n) dst[e] = nw[e];
-        }
-        if (prm.write_update) {
-          float *ud = L.u + (int64_t)(t.row0 + r) * L.ld_u + t.col0 + c;
-          if (vec && n == 4) {
-            *reinterpret_cast<f32x4 *>(ud) = f32x4{o[0], o[1], o[2], o[3]};
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (e < n) ud[e] = o[e];
-          }
-        }
+        for (int i = 1; i < G::WPT; ++i) ss += red[grp][i];
       }
+      inv = 1.0f / (__builtin_sqrtf(ss) + prm.eps);
+    }
+
+    // X in registers (fp32, MFMA output layout of the update product: block holds X^T)
+    Acc<NB> xr;
+    load_acc_t<TS, PREC>(xr, st, p0, q0, lane, inv);
+    tile_sync<G::WPT>();
+    store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
+    tile_sync<G::WPT>();
+
+    // ---- K Newton-Schulz steps ------------------------------------------------
+    // FOLD_A (fp32 and bf16x3): X <- (a I + B) X with a folded into B's diagonal; the
+    // LDS copy of X (fp32, or hi + lo bf16) carries X between steps.  Plain bf16 keeps
+    // X in fp32 registers and forms a X there, since its LDS copy is bf16-rounded.
+    constexpr bool FOLD_A = PREC != PREC_BF16;
+    for (int it = 0; it < prm.steps; ++it) {
+      Acc<NB> acc;
+      wave_gemm<TS, PREC, false, true>(acc, X, p0, X, q0, lane);     // A = X X^T
+      if (cc != 0.f) {
+        // B = b A + c A^2 = c ((b/c) A + A A^T): accumulate A A^T onto (b/c) A
+        store_acc_t<TS, PREC, false, true>(acc, AB, p0, q0, lane, 1.f, cb / cc);  // A (symmetric)
+        tile_sync<G::WPT>();
+        wave_gemm<TS, PREC, false, false>(acc, AB, p0, AB, q0, lane);
+        tile_sync<G::WPT>();                                             // A fully read
+        store_acc_t<TS, PREC, true>(acc, AB, p0, q0, lane, cc);        // B (symmetric)
+      } else {
+        store_acc_t<TS, PREC, true>(acc, AB, p0, q0, lane, cb);        // B = b A
+      }
+      if constexpr (FOLD_A) {
+        add_diag<TS, PREC>(AB, p0, q0, lane, ca);                      // B + a I
+      } else {
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) xr.b[bi][bj][e] *= ca;
+      }
+      tile_sync<G::WPT>();
+      wave_gemm<TS, PREC, true, FOLD_A>(xr, X, p0, AB, q0, lane);     // X^T <- X^T (aI + B)
+      tile_sync<G::WPT>();
+      if (it + 1 < prm.steps) {
+        store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
+        tile_sync<G::WPT>();
+      }
+    }
+
+    // ---- reassembly and weight update ------------------------------------------
+    io.template load_w<DENSE>(t, L, gt);
+    tile_sync<G::WPT>();
+    store_acc_t_f32<TS, PREC>(xr, st, p0, q0, lane);
+    tile_sync<G::WPT>();
+    io.template update<PF, DENSE>(t, L, gt, prm.lr, prm.write_update != 0, st);
+    if (nxt >= ntiles) break;
+    tile_sync<G::WPT>();                 // staging fully read before the next tile lands
+    tix = nxt;
+    if constexpr (PREFETCH) {
+      t = tn;
+      L = Ln;
+    } else {
+      t = tiles[tix];
+      L = layers[t.layer];
+      io.template load_gm<DENSE>(t, L, gt);
     }
   }
 }
 
-template <int TS, int PREC, typename S>
+// Workgroups per CU the fused kernel can keep resident, and CUs of the current device.
+template <class F>
+int resident_groups(F kernel, int threads) {
+  static thread_local int cached_dev = -1;
+  static thread_local int cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev != cached_dev) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached_dev = dev;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  return cus * (per_cu > 0 ? per_cu : 1);
+}
+
+template <int TS, int PREC, typename S, bool DENSE>
 hipError_t launch_one(const LayerDesc *layers, const FusedTile *tiles, int64_t n,
                       const NSParams &p, hipStream_t stream) {
   using G = Geo<TS, PREC>;
-  const int64_t blocks = (n + G::TPB - 1) / G::TPB;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fused_step_kernel<TS, PREC, S>), dim3((unsigned)blocks), dim3(G::THREADS), 0,
-                     stream, layers, tiles, n, p);
+  auto kern = fused_step_kernel<TS, PREC, S, DENSE>;
+  int64_t blocks = (n + G::TPB - 1) / G::TPB;
+  const int resident = resident_groups(kern, G::THREADS);
+  if (resident <= 0) return hipErrorInvalidDevice;
+  if (blocks > resident) blocks = resident;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(G::THREADS), 0, stream, layers, tiles, n, p);
   return hipGetLastError();
 }
 
 template <int TS, int PREC>
-hipError_t launch_state(int state_bf16, const LayerDesc *layers, const FusedTile *tiles, int64_t n,
-                        const NSParams &p, hipStream_t stream) {
-  return state_bf16 ? launch_one<TS, PREC, __bf16>(layers, tiles, n, p, stream)
-                    : launch_one<TS, PREC, float>(layers, tiles, n, p, stream);
+hipError_t launch_state(int state_bf16, bool dense, const LayerDesc *layers, const FusedTile *tiles,
+                        int64_t n, const NSParams &p, hipStream_t stream) {
+  if (state_bf16)
+    return dense ? launch_one<TS, PREC, __bf16, true>(layers, tiles, n, p, stream)
+                 : launch_one<TS, PREC, __bf16, false>(layers, tiles, n, p, stream);
+  return dense ? launch_one<TS, PREC, float, true>(layers, tiles, n, p, stream)
+               : launch_one<TS, PREC, float, false>(layers, tiles, n, p, stream);
 }
 
 template <int TS>
-hipError_t launch_prec(int prec, int state_bf16, const LayerDesc *layers, const FusedTile *tiles,
-                       int64_t n, const NSParams &p, hipStream_t stream) {
+hipError_t launch_prec(int prec, int state_bf16, bool dense, const LayerDesc *layers,
+                       const FusedTile *tiles, int64_t n, const NSParams &p, hipStream_t stream) {
   switch (prec) {
-    case PREC_F32: return launch_state<TS, PREC_F32>(state_bf16, layers, tiles, n, p, stream);
-    case PREC_BF16: return launch_state<TS, PREC_BF16>(state_bf16, layers, tiles, n, p, stream);
-    case PREC_BF16X3: return launch_state<TS, PREC_BF16X3>(state_bf16, layers, tiles, n, p, stream);
+    case PREC_F32: return launch_state<TS, PREC_F32>(state_bf16, dense, layers, tiles, n, p, stream);
+    case PREC_BF16: return launch_state<TS, PREC_BF16>(state_bf16, dense, layers, tiles, n, p, stream);
+    case PREC_BF16X3: return launch_state<TS, PREC_BF16X3>(state_bf16, dense, layers, tiles, n, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_fused(int ts, int prec, int state_bf16, const LayerDesc *layers,
+hipError_t launch_fused(int ts, int prec, int state_bf16, bool dense, const LayerDesc *layers,
                         const FusedTile *tiles, int64_t n, const NSParams &p, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   switch (ts) {
-    case 32: return launch_prec<32>(prec, state_bf16, layers, tiles, n, p, stream);
-    case 64: return launch_prec<64>(prec, state_bf16, layers, tiles, n, p, stream);
-    case 128: return launch_prec<128>(prec, state_bf16, layers, tiles, n, p, stream);
+    case 32: return launch_prec<32>(prec, state_bf16, dense, layers, tiles, n, p, stream);
+    case 64: return launch_prec<64>(prec, state_bf16, dense, layers, tiles, n, p, stream);
+    case 128: return launch_prec<128>(prec, state_bf16, dense, layers, tiles, n, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

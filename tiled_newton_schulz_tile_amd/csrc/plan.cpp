@@ -139,7 +139,7 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
   const double split = prec == HIMUON_PREC_BF16X3 ? 3.0 : 1.0;
   const size_t esz = c.state_dtype == HIMUON_BF16 ? 2 : 4;
 
-  std::vector<FusedTile> by_edge[3];
+  std::vector<FusedTile> by_edge[3][2];   // [edge][dense]
   std::vector<GemmTile> gt;
   std::vector<himuon_tile> order;
   double ns_flops = 0, issued = 0, bytes = 0;
@@ -157,7 +157,9 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
         order.push_back(himuon_tile{(int32_t)li, h > w ? 1 : 0, r0, c0, h, w});
         const int e = fused_edge_for(s);
         if (e) {
-          by_edge[e == 32 ? 0 : (e == 64 ? 1 : 2)].push_back(
+          const LayerDesc &d = p.ldesc[li];
+          const bool dense = h == e && w == e && d.vec_ok && d.vec_w && c0 % 8 == 0;
+          by_edge[e == 32 ? 0 : (e == 64 ? 1 : 2)][dense ? 1 : 0].push_back(
               FusedTile{(int32_t)li, (int32_t)r0, (int32_t)c0, (int16_t)h, (int16_t)w});
           issued += (double)K * split * 2.0 * e * e * e * (quintic ? 3.0 : 2.0);
         } else {
@@ -219,9 +221,12 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
   p.fgroups.clear();
   const int edges[3] = {32, 64, 128};
   for (int k = 0; k < 3; ++k) {
-    if (by_edge[k].empty()) continue;
-    p.fgroups.push_back(FusedGroup{edges[k], (int64_t)p.ftiles.size(), (int64_t)by_edge[k].size()});
-    p.ftiles.insert(p.ftiles.end(), by_edge[k].begin(), by_edge[k].end());
+    for (int dn = 1; dn >= 0; --dn) {
+      const auto &v = by_edge[k][dn];
+      if (v.empty()) continue;
+      p.fgroups.push_back(FusedGroup{edges[k], dn == 1, (int64_t)p.ftiles.size(), (int64_t)v.size()});
+      p.ftiles.insert(p.ftiles.end(), v.begin(), v.end());
+    }
   }
   p.gtiles = std::move(gt);
   p.chunks = std::move(chunks);
@@ -231,7 +236,12 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
   himuon_stats &st = p.stats;
   st = himuon_stats{};
   st.tile = tile;
-  st.kernel_tile = p.fgroups.size() == 1 && p.gtiles.empty() ? p.fgroups[0].ts : 0;
+  st.kernel_tile = 0;
+  if (p.gtiles.empty() && !p.fgroups.empty()) {
+    st.kernel_tile = p.fgroups[0].ts;
+    for (const FusedGroup &g : p.fgroups)
+      if (g.ts != st.kernel_tile) st.kernel_tile = 0;
+  }
   st.layers = (int64_t)p.layers.size();
   st.tiles = (int64_t)p.order.size();
   st.fused_tiles = (int64_t)p.ftiles.size();

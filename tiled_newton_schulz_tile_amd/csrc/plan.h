@@ -18,6 +18,7 @@ int fused_edge_for(int64_t e);
 
 struct FusedGroup {
   int ts;             // kernel tile edge
+  bool dense;         // tiles fill ts x ts exactly, rows 16-byte aligned
   int64_t first, n;   // range in Plan::ftiles
 };
 
