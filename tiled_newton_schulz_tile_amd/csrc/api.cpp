@@ -6,7 +6,7 @@
 #include <new>
 #include <string>
 
-#include "../../include/himuon.h"
+#include "himuon.h"
 #include "himuon_internal.h"
 #include "plan.h"
 

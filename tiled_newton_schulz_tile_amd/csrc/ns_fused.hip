@@ -18,7 +18,9 @@
 //   AB : A = X X^T, then B = b A + c A^2 (both symmetric), row-major, TS x TS
 // Element formats: PREC_F32 one fp32 array; PREC_BF16 one bf16 array;
 // PREC_BF16X3 two bf16 arrays (hi = bf16(x), lo = bf16(x - hi)).
-// Each wave owns a WB x WB block (WB = 64, or 32 when TS = 32) of every product.
+// Each wave owns a 64 x 32 block (32 x 32 when TS = 32) of every product, so a 128 tile
+// has 8 waves and two waves share each SIMD: one wave's LDS and VALU work overlaps the
+// other's MFMAs.
 //
 // Products (all as D[m][n] = sum_k P[m][k] Q[n][k] with contiguous k):
 //   Gram    A[p][q]   = sum_k X[p][k] X[q][k]
@@ -55,27 +57,33 @@ __device__ __forceinline__ const GLOBAL_AS T *gmem(const T *p) {
   return (const GLOBAL_AS T *)p;
 }
 
-// A wave's accumulators: NB x NB MFMA 32x32 output blocks.
-template <int NB>
+// A wave's accumulators: NI x NJ MFMA 32x32 output blocks.
+template <int NI, int NJ>
 struct Acc {
-  f32x16 b[NB][NB];
+  f32x16 b[NI][NJ];
 };
 
 // ------------------------------------------------------------------ geometry
 template <int TS, int PREC>
 struct Geo {
-  static constexpr int WB = TS >= 64 ? 64 : 32;       // wave block edge
-  static constexpr int NB = WB / 32;                  // 32x32 MFMA blocks per wave edge
-  static constexpr int WPT = (TS / WB) * (TS / WB);   // waves per tile
-  static constexpr int TPB = TS == 128 ? 1 : (TS == 64 ? 2 : 4);  // tiles per workgroup
+  // each wave owns a WBM x WBN block of every product; two waves share a SIMD
+  static constexpr int WBM = TS >= 64 ? 64 : 32;      // wave block rows
+  static constexpr int WBN = 32;                      // wave block columns
+  static constexpr int NI = WBM / 32, NJ = WBN / 32;  // 32x32 MFMA blocks per wave
+  static constexpr int WPT = (TS / WBM) * (TS / WBN); // waves per tile: 8, 2, 1
+  static constexpr int TPB = WPT == 1 ? 4 : 1;        // tiles per workgroup
   static constexpr int NT = 64 * WPT;                 // threads per tile
   static constexpr int THREADS = NT * TPB;
   static constexpr int PB = TS + 8;                   // bf16 row pitch (elements)
   static constexpr int PF = TS + 4;                   // fp32 row pitch (elements)
   static constexpr int REGION = PREC == PREC_F32 ? TS * PF * 4
                               : PREC == PREC_BF16 ? TS * PB * 2 : TS * PB * 4;
-  static constexpr int TILE_LDS = 2 * REGION;
-  static_assert(TILE_LDS >= TS * PF * 4, "staging must fit in the tile area");
+  static constexpr int TILE_LDS = 2 * REGION > TS * PF * 4 ? 2 * REGION : TS * PF * 4;
+  // element offset of (r, c) in a bf16 matrix
+  static __device__ __forceinline__ int bidx(int r, int c) { return r * PB + c; }
+  // workgroup barriers synchronise one tile: several tiles per workgroup only with
+  // one wave per tile
+  static_assert(WPT == 1 || TPB == 1, "tile groups must not share s_barrier");
 };
 
 // A matrix in LDS in the precision's element format.
@@ -131,17 +139,19 @@ __device__ __forceinline__ f32x16 mma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// MFMA operand of a transposed row-major bf16 matrix: lane l receives
+// MFMA operand of a transposed row-major bf16 matrix (layout G::bidx): lane l receives
 // buf[k .. k+7][m + l % 32] (k already includes the lane half's k offset).
 // ds_read_tr16_b64 works on groups of 16 lanes: lane i of a group receives element
 // i % 4 of the 8-byte chunks read by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.  So lane
 // L reads 4 consecutive columns of row k + L/4 and receives column L of rows k..k+3.
-template <int PB>
+template <class G>
 __device__ __forceinline__ bf16x8 tr_frag(const __bf16 *buf, int k, int m, int lane) {
   const int L = lane & 15, g = (lane >> 4) & 1;
-  const __bf16 *p = buf + (k + (L >> 2)) * PB + m + 16 * g + 4 * (L & 3);
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(p));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(p + 4 * PB));
+  const int col = m + 16 * g + 4 * (L & 3);
+  const __bf16 *p0 = buf + G::bidx(k + (L >> 2), col);
+  const __bf16 *p1 = buf + G::bidx(k + 4 + (L >> 2), col);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(p0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(p1));
   const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -153,17 +163,17 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16 *buf, int k, int m, int l
 // run of contiguous k selected by l / 32; both operands use the same k runs.
 // ZERO: this chunk starts the sum (the accumulators are not read).
 template <int TS, int PREC, bool TRANS_L, bool ZERO>
-__device__ __forceinline__ void gemm_chunk(Acc<Geo<TS, PREC>::NB> &acc, const Mat<PREC> &Lm, int l0,
+__device__ __forceinline__ void gemm_chunk(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &Lm, int l0,
                                            const Mat<PREC> &Rm, int r0, int lane, int kb) {
   using G = Geo<TS, PREC>;
-  constexpr int NB = G::NB;
+  constexpr int NI = G::NI, NJ = G::NJ;
   const int li = lane & 31, half = lane >> 5;
   if constexpr (PREC == PREC_F32) {
     constexpr int PF = G::PF;
     const int k = kb + 4 * half;
-    f32x4 lf[NB], rf[NB];
+    f32x4 lf[NI], rf[NJ];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    for (int b = 0; b < NI; ++b) {
       const int m = l0 + b * 32 + li;
       if constexpr (TRANS_L) {
 #pragma unroll
@@ -171,59 +181,57 @@ __device__ __forceinline__ void gemm_chunk(Acc<Geo<TS, PREC>::NB> &acc, const Ma
       } else {
         lf[b] = *reinterpret_cast<const f32x4 *>(Lm.f + m * PF + k);
       }
-      rf[b] = *reinterpret_cast<const f32x4 *>(Rm.f + (r0 + b * 32 + li) * PF + k);
     }
+#pragma unroll
+    for (int b = 0; b < NJ; ++b) rf[b] = *reinterpret_cast<const f32x4 *>(Rm.f + (r0 + b * 32 + li) * PF + k);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
+      for (int bi = 0; bi < NI; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < NB; ++bj)
+        for (int bj = 0; bj < NJ; ++bj)
           acc.b[bi][bj] = mma_f32(lf[bi][e], rf[bj][e], (ZERO && e == 0) ? f32x16{} : acc.b[bi][bj]);
   } else {
-    constexpr int PB = G::PB;
     const int k = kb + 8 * half;
-    bf16x8 lh[NB], rh[NB];
-    bf16x8 ll[NB], rl[NB];
+    bf16x8 lh[NI], rh[NJ];
+    bf16x8 ll[NI], rl[NJ];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    for (int b = 0; b < NI; ++b) {
       const int m = l0 + b * 32 + li;
-      const int n = r0 + b * 32 + li;
       if constexpr (TRANS_L) {
-        lh[b] = tr_frag<PB>(Lm.hi, k, l0 + b * 32, lane);
+        lh[b] = tr_frag<G>(Lm.hi, k, l0 + b * 32, lane);
+        if constexpr (PREC == PREC_BF16X3) ll[b] = tr_frag<G>(Lm.lo, k, l0 + b * 32, lane);
       } else {
-        lh[b] = *reinterpret_cast<const bf16x8 *>(Lm.hi + m * PB + k);
+        lh[b] = *reinterpret_cast<const bf16x8 *>(Lm.hi + G::bidx(m, k));
+        if constexpr (PREC == PREC_BF16X3) ll[b] = *reinterpret_cast<const bf16x8 *>(Lm.lo + G::bidx(m, k));
       }
-      rh[b] = *reinterpret_cast<const bf16x8 *>(Rm.hi + n * PB + k);
-      if constexpr (PREC == PREC_BF16X3) {
-        if constexpr (TRANS_L) {
-          ll[b] = tr_frag<PB>(Lm.lo, k, l0 + b * 32, lane);
-        } else {
-          ll[b] = *reinterpret_cast<const bf16x8 *>(Lm.lo + m * PB + k);
-        }
-        rl[b] = *reinterpret_cast<const bf16x8 *>(Rm.lo + n * PB + k);
-      }
+    }
+#pragma unroll
+    for (int b = 0; b < NJ; ++b) {
+      const int n = r0 + b * 32 + li;
+      rh[b] = *reinterpret_cast<const bf16x8 *>(Rm.hi + G::bidx(n, k));
+      if constexpr (PREC == PREC_BF16X3) rl[b] = *reinterpret_cast<const bf16x8 *>(Rm.lo + G::bidx(n, k));
     }
     if constexpr (PREC == PREC_BF16X3) {
       // small cross terms first: lo * hi + hi * lo + hi * hi
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
+      for (int bi = 0; bi < NI; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < NB; ++bj)
+        for (int bj = 0; bj < NJ; ++bj)
           acc.b[bi][bj] = mma_bf16(ll[bi], rh[bj], ZERO ? f32x16{} : acc.b[bi][bj]);
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
+      for (int bi = 0; bi < NI; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = mma_bf16(lh[bi], rl[bj], acc.b[bi][bj]);
+        for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(lh[bi], rl[bj], acc.b[bi][bj]);
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
+      for (int bi = 0; bi < NI; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < NB; ++bj) acc.b[bi][bj] = mma_bf16(lh[bi], rh[bj], acc.b[bi][bj]);
+        for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(lh[bi], rh[bj], acc.b[bi][bj]);
     } else {
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
+      for (int bi = 0; bi < NI; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < NB; ++bj)
+        for (int bj = 0; bj < NJ; ++bj)
           acc.b[bi][bj] = mma_bf16(lh[bi], rh[bj], ZERO ? f32x16{} : acc.b[bi][bj]);
     }
   }
@@ -231,7 +239,7 @@ __device__ __forceinline__ void gemm_chunk(Acc<Geo<TS, PREC>::NB> &acc, const Ma
 
 // Full K = TS contraction; ZERO: start from zero, else accumulate onto acc.
 template <int TS, int PREC, bool TRANS_L, bool ZERO>
-__device__ __forceinline__ void wave_gemm(Acc<Geo<TS, PREC>::NB> &acc, const Mat<PREC> &Lm, int l0,
+__device__ __forceinline__ void wave_gemm(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &Lm, int l0,
                                           const Mat<PREC> &Rm, int r0, int lane) {
   constexpr int KC = PREC == PREC_F32 ? 8 : 16;
   gemm_chunk<TS, PREC, TRANS_L, ZERO>(acc, Lm, l0, Rm, r0, lane, 0);
@@ -249,15 +257,14 @@ __device__ __forceinline__ void wave_gemm(Acc<Geo<TS, PREC>::NB> &acc, const Mat
 // SCALE: the stored value is s_store * acc; BACK: afterwards acc <- s_back * acc (one pass
 // over the accumulators serves both).
 template <int TS, int PREC, bool SCALE = false, bool BACK = false>
-__device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NB> &acc, const Mat<PREC> &m, int p0, int q0,
+__device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &m, int p0, int q0,
                                             int lane, float s_store = 1.f, float s_back = 1.f) {
   using G = Geo<TS, PREC>;
-  constexpr int NB = G::NB;
   const int li = lane & 31, half = lane >> 5;
 #pragma unroll
-  for (int bi = 0; bi < NB; ++bi)
+  for (int bi = 0; bi < G::NI; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < NB; ++bj)
+    for (int bj = 0; bj < G::NJ; ++bj)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int row = p0 + bi * 32 + 8 * g + 4 * half;
@@ -275,43 +282,45 @@ __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NB> &acc, const M
           bf16x4 hi;
 #pragma unroll
           for (int e = 0; e < 4; ++e) hi[e] = (__bf16)v[e];
-          *reinterpret_cast<bf16x4 *>(m.hi + col * G::PB + row) = hi;
+          *reinterpret_cast<bf16x4 *>(m.hi + G::bidx(col, row)) = hi;
           if constexpr (PREC == PREC_BF16X3) {
             bf16x4 lo;
 #pragma unroll
             for (int e = 0; e < 4; ++e) lo[e] = (__bf16)(v[e] - (float)hi[e]);
-            *reinterpret_cast<bf16x4 *>(m.lo + col * G::PB + row) = lo;
+            *reinterpret_cast<bf16x4 *>(m.lo + G::bidx(col, row)) = lo;
           }
         }
       }
 }
 
-// m[i][i] += d on the diagonal of the wave's block (diagonal blocks only).  Each diagonal
-// element was written by this same wave, and LDS accesses of one wave complete in order.
+// m[i][i] += d for the diagonal elements inside the wave's block (rows p0.., columns
+// q0..).  Each of them was written by this same wave (the block is stored transposed,
+// and (i, i) is its own transpose), and LDS accesses of one wave complete in order.
 template <int TS, int PREC>
 __device__ __forceinline__ void add_diag(const Mat<PREC> &m, int p0, int q0, int lane, float d) {
   using G = Geo<TS, PREC>;
-  if (p0 != q0 || lane >= G::WB) return;
-  const int i = p0 + lane;
+  if (q0 < p0 || q0 >= p0 + G::WBM || lane >= G::WBN) return;
+  const int i = q0 + lane;
   if constexpr (PREC == PREC_F32) {
     m.f[i * G::PF + i] += d;
   } else {
-    const float v = (float)m.hi[i * G::PB + i] + (float)m.lo[i * G::PB + i] + d;
+    const int o = G::bidx(i, i);
+    const float v = (float)m.hi[o] + (float)m.lo[o] + d;
     const __bf16 hi = (__bf16)v;
-    m.hi[i * G::PB + i] = hi;
-    m.lo[i * G::PB + i] = (__bf16)(v - (float)hi);
+    m.hi[o] = hi;
+    m.lo[o] = (__bf16)(v - (float)hi);
   }
 }
 
 // fp32 staging (pitch PF) <-> accumulators, transposed as above; load scales by s.
 template <int TS, int PREC>
-__device__ __forceinline__ void load_acc_t(Acc<Geo<TS, PREC>::NB> &acc, const float *st, int p0, int q0, int lane, float s) {
+__device__ __forceinline__ void load_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const float *st, int p0, int q0, int lane, float s) {
   using G = Geo<TS, PREC>;
   const int li = lane & 31, half = lane >> 5;
 #pragma unroll
-  for (int bi = 0; bi < G::NB; ++bi)
+  for (int bi = 0; bi < G::NI; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < G::NB; ++bj)
+    for (int bj = 0; bj < G::NJ; ++bj)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int row = p0 + bi * 32 + 8 * g + 4 * half;
@@ -323,13 +332,13 @@ __device__ __forceinline__ void load_acc_t(Acc<Geo<TS, PREC>::NB> &acc, const fl
 }
 
 template <int TS, int PREC>
-__device__ __forceinline__ void store_acc_t_f32(const Acc<Geo<TS, PREC>::NB> &acc, float *st, int p0, int q0, int lane) {
+__device__ __forceinline__ void store_acc_t_f32(const Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, float *st, int p0, int q0, int lane) {
   using G = Geo<TS, PREC>;
   const int li = lane & 31, half = lane >> 5;
 #pragma unroll
-  for (int bi = 0; bi < G::NB; ++bi)
+  for (int bi = 0; bi < G::NI; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < G::NB; ++bj)
+    for (int bj = 0; bj < G::NJ; ++bj)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int row = p0 + bi * 32 + 8 * g + 4 * half;
@@ -407,6 +416,31 @@ __device__ __forceinline__ unsigned short to_bf16_bits(float x) {
 
 __device__ __forceinline__ int clamp_n(int n, int hi) { return n < 0 ? 0 : (n > hi ? hi : n); }
 
+// A tile descriptor unpacked into 32-bit scalars (kept in registers, passed by value).
+struct TileView {
+  int layer, row0, col0, h, w;
+};
+__device__ __forceinline__ TileView view_of(const FusedTile *tiles, int64_t i) {
+  // read as four words (h and w share the last one, both non-negative)
+  const int *q = reinterpret_cast<const int *>(tiles + i);
+  const int hw = q[3];
+  return TileView{q[0], q[1], q[2], hw & 0xffff, (int)((unsigned)hw >> 16)};
+}
+
+// A layer descriptor read field by field into scalars.
+struct LayerView {
+  float *w;
+  void *m;
+  const void *g;
+  float *u;
+  int64_t ld_w, ld_m, ld_g, ld_u;
+  int vec_ok, vec_w;
+};
+__device__ __forceinline__ LayerView layer_of(const LayerDesc *layers, int i) {
+  const LayerDesc *d = layers + i;
+  return LayerView{d->w, d->m, d->g, d->u, d->ld_w, d->ld_m, d->ld_g, d->ld_u, d->vec_ok, d->vec_w};
+}
+
 // Per-thread share of one tile's HBM traffic: GM_IT chunks of 8 state elements of G and
 // of M (momentum prologue), W_IT chunks of 4 weights (update epilogue).  Chunk q of a
 // thread covers tile row q / (TS/8), columns 8 (q % (TS/8)) .. +7 (resp. 4-wide for W).
@@ -421,7 +455,7 @@ struct TileRegs {
   // full vector access and the code has no data-dependent branches (a branch merge
   // would make the compiler wait for the loads in flight).
   template <bool DENSE>
-  __device__ __forceinline__ void load_gm(const FusedTile &t, const LayerDesc &L, int gt) {
+  __device__ __forceinline__ void load_gm(TileView t, const LayerView &L, int gt) {
     const S *mb = reinterpret_cast<const S *>(L.m);
     const S *gb = reinterpret_cast<const S *>(L.g);
     if constexpr (DENSE) {
@@ -448,7 +482,7 @@ struct TileRegs {
   }
 
   template <bool DENSE>
-  __device__ __forceinline__ void load_w(const FusedTile &t, const LayerDesc &L, int gt) {
+  __device__ __forceinline__ void load_w(TileView t, const LayerView &L, int gt) {
     if constexpr (DENSE) {
 #pragma unroll
       for (int i = 0; i < W_IT; ++i) {
@@ -481,7 +515,7 @@ struct TileRegs {
   // M <- beta M + G: store the new momentum and stage its values, oriented on the
   // short side and zero padded, as fp32 TS x TS (pitch PF) in LDS.
   template <int PF, bool DENSE>
-  __device__ __forceinline__ void momentum(const FusedTile &t, const LayerDesc &L, int gt, float beta, float *st) const {
+  __device__ __forceinline__ void momentum(TileView t, const LayerView &L, int gt, float beta, float *st) const {
     S *mb = reinterpret_cast<S *>(L.m);
     const bool vec = DENSE || (L.vec_ok && (t.col0 % 8 == 0));
     const bool tall = !DENSE && t.h > t.w;
@@ -537,7 +571,7 @@ struct TileRegs {
 
   // W <- W - lr O (and U <- O) from the staged fp32 output tile.
   template <int PF, bool DENSE>
-  __device__ __forceinline__ void update(const FusedTile &t, const LayerDesc &L, int gt, float lr, bool write_u,
+  __device__ __forceinline__ void update(TileView t, const LayerView &L, int gt, float lr, bool write_u,
                          const float *st) const {
     const bool vec = DENSE || (L.vec_w && (t.col0 % 4 == 0));
     const bool tall = !DENSE && t.h > t.w;
@@ -588,11 +622,11 @@ struct TileRegs {
 // HBM latency hides behind the MFMA work.
 template <int TS, int PREC, typename S, bool DENSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, Geo<TS, PREC>::THREADS)))
-__attribute__((amdgpu_waves_per_eu(1, 2)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__restrict__ tiles,
                        int64_t ntiles, NSParams prm) {
   using G = Geo<TS, PREC>;
-  constexpr int NT = G::NT, NB = G::NB, WB = G::WB, PF = G::PF;
+  constexpr int NT = G::NT, NI = G::NI, NJ = G::NJ, PF = G::PF;
   constexpr bool PREFETCH = sizeof(S) == 2;
   __shared__ __attribute__((aligned(16))) char lds[G::TPB * G::TILE_LDS];
   __shared__ float red[G::TPB][G::WPT];
@@ -609,25 +643,25 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
   float *st = reinterpret_cast<float *>(area);          // fp32 staging, TS x PF
   const Mat<PREC> X = make_mat<TS, PREC>(area);
   const Mat<PREC> AB = make_mat<TS, PREC>(area + G::REGION);
-  const int p0 = (wv / (TS / WB)) * WB;                  // wave block origin
-  const int q0 = (wv % (TS / WB)) * WB;
+  const int p0 = (wv / (TS / G::WBN)) * G::WBM;          // wave block origin (rows)
+  const int q0 = (wv % (TS / G::WBN)) * G::WBN;          //                   (columns)
   const float ca = prm.a, cb = prm.b, cc = prm.c;
 
   TileRegs<TS, NT, S> io;
-  FusedTile t = tiles[tix];
-  LayerDesc L = layers[t.layer];
+  TileView t = view_of(tiles, tix);
+  LayerView L = layer_of(layers, t.layer);
   io.template load_gm<DENSE>(t, L, gt);
 
   while (true) {
     // ---- momentum and staging of the oriented, zero-padded tile -------------
     io.template momentum<PF, DENSE>(t, L, gt, prm.beta, st);
     const int64_t nxt = tix + stride;
-    FusedTile tn = t;
-    LayerDesc Ln = L;
+    TileView tn = t;
+    LayerView Ln = L;
     if constexpr (PREFETCH) {
       if (nxt < ntiles) {
-        tn = tiles[nxt];
-        Ln = layers[tn.layer];
+        tn = view_of(tiles, nxt);
+        Ln = layer_of(layers, tn.layer);
         io.template load_gm<DENSE>(tn, Ln, gt);
       }
     }
@@ -660,7 +694,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     }
 
     // X in registers (fp32, MFMA output layout of the update product: block holds X^T)
-    Acc<NB> xr;
+    Acc<NI, NJ> xr;
     load_acc_t<TS, PREC>(xr, st, p0, q0, lane, inv);
     tile_sync<G::WPT>();
     store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
@@ -672,7 +706,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     // X in fp32 registers and forms a X there, since its LDS copy is bf16-rounded.
     constexpr bool FOLD_A = PREC != PREC_BF16;
     for (int it = 0; it < prm.steps; ++it) {
-      Acc<NB> acc;
+      Acc<NI, NJ> acc;
       wave_gemm<TS, PREC, false, true>(acc, X, p0, X, q0, lane);     // A = X X^T
       if (cc != 0.f) {
         // B = b A + c A^2 = c ((b/c) A + A A^T): accumulate A A^T onto (b/c) A
@@ -688,9 +722,9 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
         add_diag<TS, PREC>(AB, p0, q0, lane, ca);                      // B + a I
       } else {
 #pragma unroll
-        for (int bi = 0; bi < NB; ++bi)
+        for (int bi = 0; bi < NI; ++bi)
 #pragma unroll
-          for (int bj = 0; bj < NB; ++bj)
+          for (int bj = 0; bj < NJ; ++bj)
 #pragma unroll
             for (int e = 0; e < 16; ++e) xr.b[bi][bj][e] *= ca;
       }
@@ -716,8 +750,8 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
       t = tn;
       L = Ln;
     } else {
-      t = tiles[tix];
-      L = layers[t.layer];
+      t = view_of(tiles, tix);
+      L = layer_of(layers, t.layer);
       io.template load_gm<DENSE>(t, L, gt);
     }
   }

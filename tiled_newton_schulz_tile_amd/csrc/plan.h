@@ -7,7 +7,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/himuon.h"
+#include "himuon.h"
 #include "himuon_internal.h"
 
 namespace himuon {
