@@ -266,3 +266,87 @@ def test_plan_stats_and_empty_layer_on_gpu():
     torch.cuda.synchronize()
     assert opt.stats()["tiles"] == 0
     opt.close()
+
+
+# ------------------------------------------------------------------ large tiles and FULL
+def test_single_matrix_fp32_full_matrix_equivalence():
+    # T = 512 >= max(H, W): one tile, i.e. full-matrix Newton-Schulz
+    G = power_law(256, 512, 0)
+    for T in (512, 0):
+        (res,), _ = gpu_step([G], T, state=torch.float32, prec=hm.PREC_F32)
+        W, M, U = res[0]
+        O = oracle.tiled_ns(M.double().numpy(), T, 5, Q)
+        assert_bar(U, O, hm.PREC_F32)
+        np.testing.assert_allclose(W.double().numpy(), -0.02 * O, atol=0.02 * 1e-4 + 1e-7, rtol=0)
+
+
+LARGE = [(300, 170), (170, 300), (520, 260), (129, 700), (1000, 1000), (37, 53)]
+
+
+@pytest.mark.parametrize("T", [200, 256, 0])
+@pytest.mark.parametrize("prec,state", [(0, torch.float32), (2, torch.bfloat16), (1, torch.bfloat16)])
+@pytest.mark.parametrize("coeffs,K", [(Q, 5), (C, 5), (Q, 8)])
+def test_large_tiles_and_full(T, prec, state, coeffs, K):
+    if prec == 1 and coeffs == Q:
+        pytest.skip("plain bf16 operands with quintic coefficients are outside the bf16 bar")
+    mats = [power_law(h, w, 1100 + i) for i, (h, w) in enumerate(LARGE)]
+    (res,), _ = gpu_step(mats, T, K=K, coeffs=coeffs, prec=prec, state=state)
+    for (W, M, U), G in zip(res, mats):
+        O = oracle.tiled_ns(M.double().numpy(), T, K, coeffs)
+        assert_bar(U, O, prec, tight=None if prec != 2 else 5e-3)
+
+
+def test_chunking_is_invisible():
+    # a budget that fits one tile at a time gives bit-identical results to one chunk
+    _need_gpu()
+    mats = [power_law(h, w, 1200 + i) for i, (h, w) in enumerate([(600, 300), (300, 600), (500, 500)])]
+    outs = []
+    for budget in (10 ** 10, 4_200_000):
+        Gs = [g.to(torch.bfloat16).to(DEV) for g in mats]
+        Ms = [torch.zeros_like(g) for g in Gs]
+        Ws = [torch.zeros(g.shape, device=DEV) for g in Gs]
+        Us = [torch.zeros(g.shape, device=DEV) for g in Gs]
+        opt = hm.HiMuon(list(zip(Ws, Ms, Gs, Us)), 0, 5, Q, workspace_budget=budget)
+        st = opt.stats()
+        opt.step(0.02)
+        torch.cuda.synchronize()
+        opt.close()
+        outs.append(([u.cpu() for u in Us], st["chunks"]))
+    assert outs[0][1] == 1 and outs[1][1] == 3
+    for a, b in zip(outs[0][0], outs[1][0]):
+        assert torch.equal(a, b)
+
+
+def test_runtime_tile_schedule_with_carried_momentum():
+    _need_gpu()
+    shapes = [(300, 170), (129, 700), (260, 260)]
+    Gs = [power_law(h, w, 1300 + i).to(torch.bfloat16).to(DEV) for i, (h, w) in enumerate(shapes)]
+    Ms = [torch.zeros_like(g) for g in Gs]
+    Ws = [synth.weights(h, w, 1400 + i).to(DEV) for i, (h, w) in enumerate(shapes)]
+    Us = [torch.zeros(g.shape, device=DEV) for g in Gs]
+    opt = hm.HiMuon(list(zip(Ws, Ms, Gs, Us)), 64, 5, Q, workspace_budget=10 ** 9)
+    for s, T in enumerate([64, 128, 256, 0, 64]):
+        opt.set_tile_schedule(T)
+        assert opt.stats()["tile"] == T
+        for i, (h, w) in enumerate(shapes):
+            Gs[i].copy_(power_law(h, w, 1500 + 10 * s + i).to(torch.bfloat16))
+        Mprev = [m.cpu().float().numpy() for m in Ms]
+        Wprev = [w_.cpu().double().numpy() for w_ in Ws]
+        opt.step(0.02)
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            Mnew = Ms[i].cpu()
+            want = oracle.momentum_stored(Mprev[i], Gs[i].cpu().float().numpy(), 0.95, "bf16")
+            assert np.array_equal(Mnew.float().numpy(), want)
+            O = oracle.tiled_ns(Mnew.double().numpy(), T, 5, Q)
+            assert_bar(Us[i].cpu(), O, hm.PREC_BF16X3, tight=5e-3)
+            np.testing.assert_allclose(Ws[i].cpu().double().numpy(), oracle.apply_update(Wprev[i], O, 0.02),
+                                       atol=0.02 * 5e-3 + 1e-6, rtol=0)
+    opt.close()
+
+
+def test_full_transpose_equivariance_close():
+    G = power_law(300, 520, 17)
+    (a,), _ = gpu_step([G], 0, prec=2)
+    (b,), _ = gpu_step([G.T.contiguous()], 0, prec=2)
+    assert (a[0][2] - b[0][2].T).abs().max() < 1e-3

@@ -2,7 +2,9 @@
 // descriptor tables, and the launches of one step.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstring>
+#include <vector>
 #include <new>
 #include <string>
 
@@ -22,6 +24,7 @@ struct himuon_plan_s {
   bool ev_pending = false;
   bool dirty = true;
   size_t off_ftiles = 0, off_gtiles = 0;
+  size_t off_w[5] = {0, 0, 0, 0, 0};  // work lists: momentum, stage, sym, update, apply
 };
 
 namespace {
@@ -53,7 +56,13 @@ himuon_status ensure_tables(himuon_plan_t *p, hipStream_t stream) {
   const size_t lb = align256(pl.ldesc.size() * sizeof(himuon::LayerDesc));
   const size_t fb = align256(pl.ftiles.size() * sizeof(himuon::FusedTile));
   const size_t gb = align256(pl.gtiles.size() * sizeof(himuon::GemmTile));
-  const size_t total = std::max<size_t>(lb + fb + gb, 256);
+  const std::vector<himuon::GemmWork> *wl[5] = {&pl.wmom, &pl.wstg, &pl.wsym, &pl.wupd, &pl.wapp};
+  size_t wb[5], wtot = 0;
+  for (int k = 0; k < 5; ++k) {
+    wb[k] = align256(wl[k]->size() * sizeof(himuon::GemmWork));
+    wtot += wb[k];
+  }
+  const size_t total = std::max<size_t>(lb + fb + gb + wtot, 256);
   if (!p->ev) {
     if ((e = hipEventCreateWithFlags(&p->ev, hipEventDisableTiming)) != hipSuccess)
       return hip_fail(e, "hipEventCreate");
@@ -91,6 +100,12 @@ himuon_status ensure_tables(himuon_plan_t *p, hipStream_t stream) {
   std::memcpy(p->h_stage, pl.ldesc.data(), pl.ldesc.size() * sizeof(himuon::LayerDesc));
   std::memcpy(p->h_stage + lb, pl.ftiles.data(), pl.ftiles.size() * sizeof(himuon::FusedTile));
   std::memcpy(p->h_stage + lb + fb, pl.gtiles.data(), pl.gtiles.size() * sizeof(himuon::GemmTile));
+  size_t off = lb + fb + gb;
+  for (int k = 0; k < 5; ++k) {
+    std::memcpy(p->h_stage + off, wl[k]->data(), wl[k]->size() * sizeof(himuon::GemmWork));
+    p->off_w[k] = off;
+    off += wb[k];
+  }
   if ((e = hipMemcpyAsync(p->d_buf, p->h_stage, total, hipMemcpyHostToDevice, stream)) != hipSuccess)
     return hip_fail(e, "hipMemcpyAsync of the tile table");
   if ((e = hipEventRecord(p->ev, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -136,8 +151,6 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
   const himuon::Plan &pl = p->plan;
   if (pl.workspace_bytes && (!workspace || ws_bytes < pl.workspace_bytes))
     return fail(HIMUON_EINVAL, "workspace smaller than himuon_workspace_size");
-  if (!pl.gtiles.empty())
-    return fail(HIMUON_EUNSUPPORTED, "tiles larger than 128 need the large-tile path");
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   himuon_status s = ensure_tables(p, stream);
   if (s != HIMUON_OK) return s;
@@ -157,6 +170,29 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
     hipError_t e = himuon::launch_fused(g.ts, (int)c.precision, c.state_dtype == HIMUON_BF16,
                                         g.dense, dl, dft + g.first, g.n, prm, stream);
     if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
+  }
+  if (!pl.chunks.empty()) {
+    const auto *dgt = reinterpret_cast<const himuon::GemmTile *>(p->d_buf + p->off_gtiles);
+    const himuon::GemmWork *dw[5];
+    for (int k = 0; k < 5; ++k) dw[k] = reinterpret_cast<const himuon::GemmWork *>(p->d_buf + p->off_w[k]);
+    for (const himuon::GemmChunk &ch : pl.chunks) {
+      himuon::GemmChunkLaunch cl{};
+      cl.tile_first = ch.first;
+      cl.tile_n = ch.n;
+      cl.mom = dw[0] + ch.mom.first;
+      cl.n_mom = ch.mom.n;
+      cl.stg = dw[1] + ch.stg.first;
+      cl.n_stg = ch.stg.n;
+      cl.sym = dw[2] + ch.sym.first;
+      cl.n_sym = ch.sym.n;
+      cl.upd = dw[3] + ch.upd.first;
+      cl.n_upd = ch.upd.n;
+      cl.app = dw[4] + ch.app.first;
+      cl.n_app = ch.app.n;
+      hipError_t e = himuon::launch_gemm_chunk((int)c.precision, c.state_dtype == HIMUON_BF16, dl, dgt, cl,
+                                               reinterpret_cast<char *>(workspace), prm, stream);
+      if (e != hipSuccess) return hip_fail(e, "large-tile kernel launch");
+    }
   }
   return HIMUON_OK;
 }

@@ -30,16 +30,32 @@ struct FusedTile {
 };
 static_assert(sizeof(FusedTile) == 16, "FusedTile layout");
 
-// One tile (or whole matrix) of the large-tile GEMM path.
+// One tile (or whole matrix) of the large-tile GEMM path.  Its workspace holds the
+// oriented tile X (r x s, two buffers), A and B (r x r) as row-major planes with
+// leading dimensions ldx = roundup(s, 32) and lda = roundup(r, 32) (zero padded):
+// fp32 planes for PREC_F32, else a bf16 "hi" plane followed by a bf16 "lo" plane.
 struct GemmTile {
   int32_t layer;
   int32_t row0, col0;
   int32_t h, w;       // global orientation
   int32_t r, s;       // oriented: r = min(h, w) rows, s = max(h, w) columns
   int32_t tall;       // h > w: the tile is iterated transposed
-  int64_t ws_x0, ws_x1, ws_a, ws_b;  // byte offsets into the workspace (per chunk)
-  int64_t ws_scale;   // byte offset of the tile's fp32 scale / norm accumulator
+  int32_t ldx, lda;   // padded leading dimensions of the X and A/B planes (elements)
+  int32_t nred;       // momentum blocks (partial sums of squares)
+  int32_t pad_;
+  int64_t ws_x0, ws_x1, ws_a, ws_b;  // byte offsets into the workspace
+  int64_t ws_red;     // nred fp32 partial sums, then the tile's 1 / (||Y||_F + eps)
 };
+static_assert(sizeof(GemmTile) == 88, "GemmTile layout");
+
+// One work item of a grouped launch of the GEMM path: tile index (into the plan's
+// GemmTile table) and block coordinates.
+struct GemmWork {
+  int32_t tile, bi, bj;
+};
+
+// Elements per momentum block of the GEMM path.
+constexpr int kGemmMomentumBlock = 8192;
 
 enum Prec : int { PREC_F32 = 0, PREC_BF16 = 1, PREC_BF16X3 = 2 };
 
@@ -60,5 +76,21 @@ hipError_t launch_fused(int ts, int prec, int state_bf16, bool dense, const Laye
 
 // LDS bytes one workgroup of the fused kernel uses (for the planner's stats).
 size_t fused_lds_bytes(int ts, int prec);
+
+// ---- launchers (ns_gemm.hip) ---------------------------------------------------
+// Work lists of one chunk of the GEMM path (device arrays).
+struct GemmChunkLaunch {
+  int64_t tile_first, tile_n;          // tiles [first, first + n) of the table
+  const GemmWork *mom;  int64_t n_mom; // (tile, block, 0): momentum blocks
+  const GemmWork *stg;  int64_t n_stg; // (tile, bi, bj): 64-blocks of the oriented X
+  const GemmWork *sym;  int64_t n_sym; // (tile, bi <= bj): 128-blocks of r x r
+  const GemmWork *upd;  int64_t n_upd; // (tile, bi, bj): 128-blocks of r x s
+  const GemmWork *app;  int64_t n_app; // (tile, bi, bj): 64-blocks of the h x w tile
+};
+// Runs one full step for the tiles of a chunk: momentum and partial norms, norm
+// reduction, staging of X0, K Newton-Schulz steps as grouped MFMA GEMMs, update.
+hipError_t launch_gemm_chunk(int prec, int state_bf16, const LayerDesc *layers, const GemmTile *tiles,
+                             const GemmChunkLaunch &c, char *workspace, const NSParams &p,
+                             hipStream_t stream);
 
 }  // namespace himuon

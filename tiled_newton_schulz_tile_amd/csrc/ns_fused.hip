@@ -29,33 +29,13 @@
 // With fp32 or split (hi + lo) operands, a is added to B's diagonal and the update is
 // one product X^T (a I + B); with plain bf16 operands the update accumulates on top of
 // a X^T held in fp32 registers, so only the product's operands are rounded.
+#include "device_common.h"
 #include "himuon_internal.h"
 
 namespace himuon {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-
-#define GLOBAL_AS __attribute__((address_space(1)))
-#define LDS_AS __attribute__((address_space(3)))
-
-// Global-memory views of the caller's pointers (global_load/store instead of flat).
-template <class T>
-__device__ __forceinline__ GLOBAL_AS T *gmem(T *p) {
-  return (GLOBAL_AS T *)p;
-}
-template <class T>
-__device__ __forceinline__ const GLOBAL_AS T *gmem(const T *p) {
-  return (const GLOBAL_AS T *)p;
-}
+using namespace dev;
 
 // A wave's accumulators: NI x NJ MFMA 32x32 output blocks.
 template <int NI, int NJ>
@@ -122,7 +102,7 @@ __device__ __forceinline__ void tile_sync() {
   if constexpr (WPT > 1) {
     // this wave's LDS traffic is complete, then meet the other waves of the tile;
     // global loads in flight (the next tile's prefetch) are deliberately not waited for
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    lds_barrier();
   } else {
     // one wave per tile: LDS traffic of a wave is processed in order; only the
     // compiler has to be kept from moving LDS accesses across this point
@@ -130,30 +110,6 @@ __device__ __forceinline__ void tile_sync() {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-}
-
-__device__ __forceinline__ f32x16 mma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mma_f32(float a, float b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-
-// MFMA operand of a transposed row-major bf16 matrix (layout G::bidx): lane l receives
-// buf[k .. k+7][m + l % 32] (k already includes the lane half's k offset).
-// ds_read_tr16_b64 works on groups of 16 lanes: lane i of a group receives element
-// i % 4 of the 8-byte chunks read by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.  So lane
-// L reads 4 consecutive columns of row k + L/4 and receives column L of rows k..k+3.
-template <class G>
-__device__ __forceinline__ bf16x8 tr_frag(const __bf16 *buf, int k, int m, int lane) {
-  const int L = lane & 15, g = (lane >> 4) & 1;
-  const int col = m + 16 * g + 4 * (L & 3);
-  const __bf16 *p0 = buf + G::bidx(k + (L >> 2), col);
-  const __bf16 *p1 = buf + G::bidx(k + 4 + (L >> 2), col);
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(p0));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(p1));
-  const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, v);
 }
 
 // ------------------------------------------------------------------ wave GEMM
@@ -199,8 +155,8 @@ __device__ __forceinline__ void gemm_chunk(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>:
     for (int b = 0; b < NI; ++b) {
       const int m = l0 + b * 32 + li;
       if constexpr (TRANS_L) {
-        lh[b] = tr_frag<G>(Lm.hi, k, l0 + b * 32, lane);
-        if constexpr (PREC == PREC_BF16X3) ll[b] = tr_frag<G>(Lm.lo, k, l0 + b * 32, lane);
+        lh[b] = tr_frag(Lm.hi, G::PB, k, l0 + b * 32, lane);
+        if constexpr (PREC == PREC_BF16X3) ll[b] = tr_frag(Lm.lo, G::PB, k, l0 + b * 32, lane);
       } else {
         lh[b] = *reinterpret_cast<const bf16x8 *>(Lm.hi + G::bidx(m, k));
         if constexpr (PREC == PREC_BF16X3) ll[b] = *reinterpret_cast<const bf16x8 *>(Lm.lo + G::bidx(m, k));
@@ -410,9 +366,6 @@ __device__ __forceinline__ Chunk8<S> load_chunk_vec(const S *p) {
   return c;
 }
 
-__device__ __forceinline__ unsigned short to_bf16_bits(float x) {
-  return __builtin_bit_cast(unsigned short, (__bf16)x);
-}
 
 __device__ __forceinline__ int clamp_n(int n, int hi) { return n < 0 ? 0 : (n > hi ? hi : n); }
 

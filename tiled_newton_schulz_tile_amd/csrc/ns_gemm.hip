@@ -1,0 +1,689 @@
+// Large-tile path of the HiMuon step on gfx950: tiles longer than 128 (T > 128) and
+// full matrices (T = FULL, full-matrix Muon).  The same finite Newton-Schulz map as the
+// fused kernel ("Hierarchical Muon: Tiled Newton-Schulz Updates for Efficient Muon
+// Optimization", Abstract), run as grouped GEMMs over every tile of a workspace chunk,
+// with X, A and B resident in HBM between launches (memory-bounded chunking: the host
+// cuts the tile list into chunks whose workspace fits the caller's budget).
+//
+// Per chunk and step:
+//   momentum     M <- beta M + G; per-block partial sums of squares (fixed order)
+//   norm         per tile, the partials summed in a fixed order: 1 / (||Y||_F + eps)
+//   stage        X0 = Y / (||Y|| + eps), oriented on the short side (LDS transpose for
+//                tall tiles), written as planes (fp32, or bf16 hi + lo), zero padded
+//   K times      A = X X^T           (symmetric: upper 128-blocks only, mirrored)
+//                B = b A + c A A^T   (symmetric, epilogue adds b A; skipped when c = 0)
+//                X <- (a I + B) X    (a on B's diagonal; plain bf16 adds a X in fp32)
+//   apply        W <- W - lr O, O reoriented (LDS transpose for tall tiles)
+// GEMM blocks are 128 x 128 with K steps of 32 staged through LDS (register
+// double buffering); four waves each own a 64 x 64 block (2 x 2 MFMA 32x32 tiles).
+#include "device_common.h"
+#include "himuon_internal.h"
+
+namespace himuon {
+namespace {
+
+using namespace dev;
+
+constexpr int BM = 128, BK = 32;
+constexpr int THREADS = 256;
+
+enum Mode : int { MODE_GRAM = 0, MODE_SQUARE = 1, MODE_UPDATE = 2 };
+
+struct GemmParams {
+  float a, b, c;
+  int xsel;      // X buffer read this step (0: ws_x0, 1: ws_x1); the other is written
+  int fold;      // a added to B's diagonal (fp32, bf16x3); plain bf16 adds a X in fp32
+};
+
+// Scalar copies of one GemmTile (read word by word so nothing lands in private memory).
+struct TileG {
+  int layer, row0, col0, h, w, r, s, tall, ldx, lda, nred;
+  int64_t x0, x1, a, b, red;
+};
+__device__ __forceinline__ TileG tile_of(const GemmTile *tiles, int i) {
+  const GemmTile *t = tiles + i;
+  return TileG{t->layer, t->row0, t->col0, t->h,   t->w,    t->r,   t->s, t->tall,
+               t->ldx,   t->lda,  t->nred, t->ws_x0, t->ws_x1, t->ws_a, t->ws_b, t->ws_red};
+}
+
+// A matrix of `rows` rows and leading dimension ld in the workspace, in the
+// precision's plane format.
+template <int PREC>
+struct Planes {
+  char *base;
+  int rows, ld;
+  __device__ __bf16 *hi() const { return reinterpret_cast<__bf16 *>(base); }
+  __device__ __bf16 *lo() const { return reinterpret_cast<__bf16 *>(base + (int64_t)rows * ld * 2); }
+  __device__ float *f() const { return reinterpret_cast<float *>(base); }
+  // fp32 value of element (i, j)
+  __device__ __forceinline__ float get(int i, int j) const {
+    const int64_t o = (int64_t)i * ld + j;
+    if constexpr (PREC == PREC_F32) {
+      return gmem(f())[o];
+    } else {
+      const unsigned short h = gmem(reinterpret_cast<const unsigned short *>(hi()))[o];
+      const unsigned short l = gmem(reinterpret_cast<const unsigned short *>(lo()))[o];
+      return bf16_bits_to_f32(h) + bf16_bits_to_f32(l);
+    }
+  }
+  // store 16 consecutive values of row i starting at column j (j multiple of 16,
+  // j + 16 <= ld)
+  __device__ __forceinline__ void put16(int i, int j, const float (&v)[16]) const {
+    const int64_t o = (int64_t)i * ld + j;
+    if constexpr (PREC == PREC_F32) {
+      GLOBAL_AS f32x4 *d = reinterpret_cast<GLOBAL_AS f32x4 *>(gmem(f() + o));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    } else {
+      unsigned short hb[16], lb[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        hb[q] = to_bf16_bits(v[q]);
+        lb[q] = to_bf16_bits(v[q] - bf16_bits_to_f32(hb[q]));
+      }
+      GLOBAL_AS u32x4 *dh = reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(hi() + o));
+      GLOBAL_AS u32x4 *dl = reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(lo() + o));
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        dh[q] = u32x4{hb[8 * q] | (unsigned)hb[8 * q + 1] << 16, hb[8 * q + 2] | (unsigned)hb[8 * q + 3] << 16,
+                      hb[8 * q + 4] | (unsigned)hb[8 * q + 5] << 16, hb[8 * q + 6] | (unsigned)hb[8 * q + 7] << 16};
+        if constexpr (PREC == PREC_BF16X3 || PREC == PREC_BF16)
+          dl[q] = u32x4{lb[8 * q] | (unsigned)lb[8 * q + 1] << 16, lb[8 * q + 2] | (unsigned)lb[8 * q + 3] << 16,
+                        lb[8 * q + 4] | (unsigned)lb[8 * q + 5] << 16, lb[8 * q + 6] | (unsigned)lb[8 * q + 7] << 16};
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Fixed-order workgroup sum (4 waves); every thread gets the result.
+__device__ __forceinline__ float block_sum(float v, float *red4) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float s = (red4[0] + red4[1]) + (red4[2] + red4[3]);
+  __syncthreads();
+  return s;
+}
+
+// ------------------------------------------------------------------ momentum
+// Work item (tile, block, -): elements [block * 8192, +8192) of the tile, row-major in
+// its own orientation.  Stores the new momentum and the block's sum of squares of the
+// stored values.
+template <typename S>
+__global__ __launch_bounds__(THREADS) void gemm_momentum_kernel(const LayerDesc *__restrict__ layers,
+                                                                const GemmTile *__restrict__ tiles,
+                                                                const GemmWork *__restrict__ work, char *ws,
+                                                                float beta) {
+  __shared__ float red4[4];
+  const GemmWork wk = work[blockIdx.x];
+  const TileG t = tile_of(tiles, wk.tile);
+  const LayerDesc *L = layers + t.layer;
+  S *mb = reinterpret_cast<S *>(L->m);
+  const S *gb = reinterpret_cast<const S *>(L->g);
+  const int64_t ldm = L->ld_m, ldg = L->ld_g;
+  const bool vec = L->vec_ok;
+  const int64_t total = (int64_t)t.h * t.w;
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kGemmMomentumBlock / (8 * THREADS); ++c) {
+    const int64_t e0 = ((int64_t)wk.bi * (kGemmMomentumBlock / 8) + c * THREADS + threadIdx.x) * 8;
+    if (e0 >= total) continue;
+    const int i0 = (int)(e0 / t.w), j0 = (int)(e0 % t.w);
+    if (vec && j0 + 8 <= t.w && ((t.col0 + j0) & 7) == 0) {
+      const int64_t om = (int64_t)(t.row0 + i0) * ldm + t.col0 + j0;
+      const int64_t og = (int64_t)(t.row0 + i0) * ldg + t.col0 + j0;
+      if constexpr (sizeof(S) == 2) {
+        const u32x4 m = __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(mb + om)));
+        const u32x4 g = __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(gb + og)));
+        unsigned short code[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const unsigned mw = m[q >> 1], gw = g[q >> 1];
+          const float mv = __builtin_bit_cast(float, (q & 1) ? (mw & 0xffff0000u) : (mw << 16));
+          const float gv = __builtin_bit_cast(float, (q & 1) ? (gw & 0xffff0000u) : (gw << 16));
+          code[q] = to_bf16_bits(__builtin_fmaf(beta, mv, gv));
+          const float v = bf16_bits_to_f32(code[q]);
+          ss = __builtin_fmaf(v, v, ss);
+        }
+        *reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(mb + om)) =
+            u32x4{code[0] | (unsigned)code[1] << 16, code[2] | (unsigned)code[3] << 16,
+                  code[4] | (unsigned)code[5] << 16, code[6] | (unsigned)code[7] << 16};
+      } else {
+        const GLOBAL_AS f32x4 *pm = reinterpret_cast<const GLOBAL_AS f32x4 *>(gmem(mb + om));
+        const GLOBAL_AS f32x4 *pg = reinterpret_cast<const GLOBAL_AS f32x4 *>(gmem(gb + og));
+        f32x4 m0 = pm[0], m1 = pm[1];
+        const f32x4 g0 = pg[0], g1 = pg[1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          m0[q] = __builtin_fmaf(beta, m0[q], g0[q]);
+          ss = __builtin_fmaf(m0[q], m0[q], ss);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          m1[q] = __builtin_fmaf(beta, m1[q], g1[q]);
+          ss = __builtin_fmaf(m1[q], m1[q], ss);
+        }
+        GLOBAL_AS f32x4 *dm = reinterpret_cast<GLOBAL_AS f32x4 *>(gmem(mb + om));
+        dm[0] = m0;
+        dm[1] = m1;
+      }
+    } else {
+      for (int q = 0; q < 8; ++q) {
+        const int64_t e = e0 + q;
+        if (e >= total) break;
+        const int i = (int)(e / t.w), j = (int)(e % t.w);
+        const int64_t om = (int64_t)(t.row0 + i) * ldm + t.col0 + j;
+        const int64_t og = (int64_t)(t.row0 + i) * ldg + t.col0 + j;
+        float v;
+        if constexpr (sizeof(S) == 2) {
+          const float mv = bf16_bits_to_f32(gmem(reinterpret_cast<const unsigned short *>(mb))[om]);
+          const float gv = bf16_bits_to_f32(gmem(reinterpret_cast<const unsigned short *>(gb))[og]);
+          const unsigned short code = to_bf16_bits(__builtin_fmaf(beta, mv, gv));
+          gmem(reinterpret_cast<unsigned short *>(mb))[om] = code;
+          v = bf16_bits_to_f32(code);
+        } else {
+          v = __builtin_fmaf(beta, gmem(mb)[om], gmem(gb)[og]);
+          gmem(mb)[om] = v;
+        }
+        ss = __builtin_fmaf(v, v, ss);
+      }
+    }
+  }
+  ss = block_sum(ss, red4);
+  if (threadIdx.x == 0) gmem(reinterpret_cast<float *>(ws + t.red))[wk.bi] = ss;
+}
+
+// ------------------------------------------------------------------ norm
+// One workgroup per tile: the partial sums in a fixed order; stores 1 / (sqrt(ss) + eps).
+__global__ __launch_bounds__(THREADS) void gemm_norm_kernel(const GemmTile *__restrict__ tiles, int first,
+                                                            char *ws, float eps) {
+  __shared__ float red4[4];
+  const TileG t = tile_of(tiles, first + (int)blockIdx.x);
+  GLOBAL_AS float *p = gmem(reinterpret_cast<float *>(ws + t.red));
+  float ss = 0.f;
+  for (int q = threadIdx.x; q < t.nred; q += THREADS) ss += p[q];
+  ss = block_sum(ss, red4);
+  if (threadIdx.x == 0) p[t.nred] = 1.0f / (__builtin_sqrtf(ss) + eps);
+}
+
+// ------------------------------------------------------------------ stage / apply
+// 64 x 64 blocks through an LDS tile (pitch 65): thread t covers row t / 4, columns
+// 16 (t % 4) .. +15 of the block.
+constexpr int SB = 64, SBP = 65;
+
+// Work item (tile, bi, bj): oriented block rows [64 bi, +64), columns [64 bj, +64) of
+// X0 (r x ldx); zeros outside the r x s tile.
+template <typename S, int PREC>
+__global__ __launch_bounds__(THREADS) void gemm_stage_kernel(const LayerDesc *__restrict__ layers,
+                                                             const GemmTile *__restrict__ tiles,
+                                                             const GemmWork *__restrict__ work, char *ws) {
+  __shared__ float blk[SB * SBP];
+  const GemmWork wk = work[blockIdx.x];
+  const TileG t = tile_of(tiles, wk.tile);
+  const LayerDesc *L = layers + t.layer;
+  const float inv = gmem(reinterpret_cast<const float *>(ws + t.red))[t.nred];
+  const S *mb = reinterpret_cast<const S *>(L->m);
+  const int64_t ldm = L->ld_m;
+  const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 16;
+  // the global block this oriented block comes from
+  const int gr0 = t.tall ? wk.bj * SB : wk.bi * SB;
+  const int gc0 = t.tall ? wk.bi * SB : wk.bj * SB;
+  {
+    const int gi = gr0 + lr;
+    const int gj = gc0 + lc;
+    float v[16];
+    if (gi < t.h && gj + 16 <= t.w && L->vec_ok && ((t.col0 + gj) & 7) == 0) {
+      const int64_t o = (int64_t)(t.row0 + gi) * ldm + t.col0 + gj;
+      if constexpr (sizeof(S) == 2) {
+        const GLOBAL_AS u32x4 *p = reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(mb + o));
+        const u32x4 a = p[0], b = p[1];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const unsigned wa = a[q >> 1], wb = b[q >> 1];
+          v[q] = __builtin_bit_cast(float, (q & 1) ? (wa & 0xffff0000u) : (wa << 16));
+          v[q + 8] = __builtin_bit_cast(float, (q & 1) ? (wb & 0xffff0000u) : (wb << 16));
+        }
+      } else {
+        const GLOBAL_AS f32x4 *p = reinterpret_cast<const GLOBAL_AS f32x4 *>(gmem(mb + o));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 x = p[q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        float x = 0.f;
+        if (gi < t.h && gj + q < t.w) {
+          const int64_t o = (int64_t)(t.row0 + gi) * ldm + t.col0 + gj + q;
+          if constexpr (sizeof(S) == 2)
+            x = bf16_bits_to_f32(gmem(reinterpret_cast<const unsigned short *>(mb))[o]);
+          else
+            x = gmem(mb)[o];
+        }
+        v[q] = x;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) blk[lr * SBP + lc + q] = v[q] * inv;
+  }
+  __syncthreads();
+  const int orow = wk.bi * SB + lr, ocol = wk.bj * SB + lc;
+  if (orow < t.r && ocol < t.ldx) {
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = t.tall ? blk[(lc + q) * SBP + lr] : blk[lr * SBP + lc + q];
+    const Planes<PREC> X{ws + t.x0, t.r, t.ldx};
+    X.put16(orow, ocol, v);
+  }
+}
+
+// Work item (tile, bi, bj): global block rows [64 bi, +64), columns [64 bj, +64) of the
+// h x w tile.  O comes from the X buffer the last step wrote.
+template <int PREC>
+__global__ __launch_bounds__(THREADS) void gemm_apply_kernel(const LayerDesc *__restrict__ layers,
+                                                             const GemmTile *__restrict__ tiles,
+                                                             const GemmWork *__restrict__ work, char *ws,
+                                                             int xsel, float lr_, int write_u) {
+  __shared__ float blk[SB * SBP];
+  const GemmWork wk = work[blockIdx.x];
+  const TileG t = tile_of(tiles, wk.tile);
+  const LayerDesc *L = layers + t.layer;
+  const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 16;
+  const int or0 = t.tall ? wk.bj * SB : wk.bi * SB;   // oriented block holding this block
+  const int oc0 = t.tall ? wk.bi * SB : wk.bj * SB;
+  const Planes<PREC> X{ws + (xsel ? t.x1 : t.x0), t.r, t.ldx};
+  {
+    const int oi = or0 + lr, oj = oc0 + lc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      blk[lr * SBP + lc + q] = (oi < t.r && oj + q < t.s) ? X.get(oi, oj + q) : 0.f;
+  }
+  __syncthreads();
+  const int gi = wk.bi * SB + lr, gj = wk.bj * SB + lc;
+  if (gi >= t.h || gj >= t.w) return;
+  float o[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) o[q] = t.tall ? blk[(lc + q) * SBP + lr] : blk[lr * SBP + lc + q];
+  const int n = t.w - gj < 16 ? t.w - gj : 16;
+  float *wrow = L->w + (int64_t)(t.row0 + gi) * L->ld_w + t.col0 + gj;
+  const float nlr = -lr_;
+  if (n == 16 && L->vec_w && ((t.col0 + gj) & 3) == 0) {
+    GLOBAL_AS f32x4 *p = reinterpret_cast<GLOBAL_AS f32x4 *>(gmem(wrow));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 x = p[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(nlr, o[4 * q + e], x[e]);
+      p[q] = x;
+    }
+    if (write_u) {
+      GLOBAL_AS f32x4 *u = reinterpret_cast<GLOBAL_AS f32x4 *>(
+          gmem(L->u + (int64_t)(t.row0 + gi) * L->ld_u + t.col0 + gj));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) u[q] = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+    }
+  } else {
+    GLOBAL_AS float *p = gmem(wrow);
+    for (int q = 0; q < n; ++q) p[q] = __builtin_fmaf(nlr, o[q], p[q]);
+    if (write_u) {
+      GLOBAL_AS float *u = gmem(L->u + (int64_t)(t.row0 + gi) * L->ld_u + t.col0 + gj);
+      for (int q = 0; q < n; ++q) u[q] = o[q];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ grouped GEMMs
+// LDS tile of one operand for one K step, per plane: [rows][BK + pad] (row operand) or
+// [BK][BM + pad] (column operand of the update, read with ds_read_tr).
+template <int PREC>
+struct GemmLds {
+  static constexpr bool F32 = PREC == PREC_F32;
+  static constexpr int NPL = PREC == PREC_BF16X3 ? 2 : 1;     // planes staged
+  static constexpr int RP = F32 ? BK + 4 : BK + 8;            // row-operand pitch (elements)
+  static constexpr int CP = F32 ? BM + 4 : BM + 8;            // column-operand pitch
+  static constexpr int ES = F32 ? 4 : 2;                      // element bytes
+  static constexpr int ROWT = BM * RP * ES;                   // one plane of a row tile
+  static constexpr int COLT = BK * CP * ES;                   // one plane of a column tile
+  static constexpr int STAGE = NPL * (ROWT + (ROWT > COLT ? ROWT : COLT));
+  static constexpr int SP = BM + 4;                           // fp32 staging pitch
+  static constexpr int BYTES = 2 * STAGE > BM * SP * 4 ? 2 * STAGE : BM * SP * 4;
+};
+
+// Per-thread registers of one K step's global loads (both operands, all planes).
+template <int PREC>
+struct KRegs {
+  static constexpr int N = PREC == PREC_F32 ? 4 : (PREC == PREC_BF16X3 ? 4 : 2);
+  u32x4 l[N], r[N];
+};
+
+template <int PREC, int MODE>
+__device__ __forceinline__ void gemm_load(KRegs<PREC> &kr, const Planes<PREC> &Lp, int i0,
+                                          const Planes<PREC> &Rp, int j0, int kb) {
+  const int tid = threadIdx.x;
+  if constexpr (PREC == PREC_F32) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + q * THREADS;
+      const int row = idx >> 3, ch = idx & 7;       // 128 rows x 8 chunks of 4 floats
+      const int gi = i0 + row;
+      kr.l[q] = gi < Lp.rows ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
+                                   gmem(Lp.f() + (int64_t)gi * Lp.ld + kb + ch * 4)))
+                             : u32x4{0, 0, 0, 0};
+      if constexpr (MODE == MODE_UPDATE) {
+        const int kr_ = idx >> 5, cc = idx & 31;    // 32 k-rows x 32 chunks of 4 floats
+        const int gk = kb + kr_, gj = j0 + cc * 4;
+        kr.r[q] = (gk < Rp.rows && gj < Rp.ld) ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
+                                                     gmem(Rp.f() + (int64_t)gk * Rp.ld + gj)))
+                                               : u32x4{0, 0, 0, 0};
+      } else {
+        const int gj = j0 + row;
+        kr.r[q] = gj < Rp.rows ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
+                                     gmem(Rp.f() + (int64_t)gj * Rp.ld + kb + ch * 4)))
+                               : u32x4{0, 0, 0, 0};
+      }
+    }
+  } else {
+    constexpr int NPL = GemmLds<PREC>::NPL;
+#pragma unroll
+    for (int pl = 0; pl < NPL; ++pl) {
+      const __bf16 *lb = pl ? Lp.lo() : Lp.hi();
+      const __bf16 *rb = pl ? Rp.lo() : Rp.hi();
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int idx = tid + q * THREADS;
+        const int row = idx >> 2, ch = idx & 3;     // 128 rows x 4 chunks of 8 bf16
+        const int gi = i0 + row;
+        kr.l[pl * 2 + q] = gi < Lp.rows ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
+                                               gmem(lb + (int64_t)gi * Lp.ld + kb + ch * 8)))
+                                         : u32x4{0, 0, 0, 0};
+        if constexpr (MODE == MODE_UPDATE) {
+          const int kr_ = idx >> 4, cc = idx & 15;  // 32 k-rows x 16 chunks of 8 bf16
+          const int gk = kb + kr_, gj = j0 + cc * 8;
+          kr.r[pl * 2 + q] = (gk < Rp.rows && gj < Rp.ld)
+                                 ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
+                                       gmem(rb + (int64_t)gk * Rp.ld + gj)))
+                                 : u32x4{0, 0, 0, 0};
+        } else {
+          const int gj = j0 + row;
+          kr.r[pl * 2 + q] = gj < Rp.rows ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
+                                                gmem(rb + (int64_t)gj * Rp.ld + kb + ch * 8)))
+                                          : u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+  }
+}
+
+template <int PREC, int MODE>
+__device__ __forceinline__ void gemm_store_lds(const KRegs<PREC> &kr, char *stage) {
+  using LD = GemmLds<PREC>;
+  const int tid = threadIdx.x;
+  char *lt = stage;                         // row tiles of L: NPL planes
+  char *rt = stage + LD::NPL * LD::ROWT;    // then the R tiles
+  if constexpr (PREC == PREC_F32) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + q * THREADS;
+      const int row = idx >> 3, ch = idx & 7;
+      *reinterpret_cast<u32x4 *>(reinterpret_cast<float *>(lt) + row * LD::RP + ch * 4) = kr.l[q];
+      if constexpr (MODE == MODE_UPDATE) {
+        const int kr_ = idx >> 5, cc = idx & 31;
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<float *>(rt) + kr_ * LD::CP + cc * 4) = kr.r[q];
+      } else {
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<float *>(rt) + row * LD::RP + ch * 4) = kr.r[q];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int pl = 0; pl < LD::NPL; ++pl) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int idx = tid + q * THREADS;
+        const int row = idx >> 2, ch = idx & 3;
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<__bf16 *>(lt + pl * LD::ROWT) + row * LD::RP + ch * 8) =
+            kr.l[pl * 2 + q];
+        if constexpr (MODE == MODE_UPDATE) {
+          const int kr_ = idx >> 4, cc = idx & 15;
+          *reinterpret_cast<u32x4 *>(reinterpret_cast<__bf16 *>(rt + pl * LD::COLT) + kr_ * LD::CP + cc * 8) =
+              kr.r[pl * 2 + q];
+        } else {
+          *reinterpret_cast<u32x4 *>(reinterpret_cast<__bf16 *>(rt + pl * LD::ROWT) + row * LD::RP + ch * 8) =
+              kr.r[pl * 2 + q];
+        }
+      }
+    }
+  }
+}
+
+// MFMAs of one K step from an LDS stage; wave block rows wm*64.., columns wn*64...
+template <int PREC, int MODE>
+__device__ __forceinline__ void gemm_compute(f32x16 (&acc)[2][2], const char *stage, int wm, int wn, int lane) {
+  using LD = GemmLds<PREC>;
+  const int li = lane & 31, half = lane >> 5;
+  const char *lt = stage;
+  const char *rt = stage + LD::NPL * LD::ROWT;
+  if constexpr (PREC == PREC_F32) {
+    const float *L = reinterpret_cast<const float *>(lt);
+    const float *R = reinterpret_cast<const float *>(rt);
+#pragma unroll
+    for (int kc = 0; kc < BK; kc += 8) {
+      const int k = kc + 4 * half;
+      f32x4 lf[2], rf[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        lf[b] = *reinterpret_cast<const f32x4 *>(L + (wm * 64 + b * 32 + li) * LD::RP + k);
+        if constexpr (MODE == MODE_UPDATE) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rf[b][e] = R[(k + e) * LD::CP + wn * 64 + b * 32 + li];
+        } else {
+          rf[b] = *reinterpret_cast<const f32x4 *>(R + (wn * 64 + b * 32 + li) * LD::RP + k);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mma_f32(lf[bi][e], rf[bj][e], acc[bi][bj]);
+    }
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < BK; kc += 16) {
+      const int k = kc + 8 * half;
+      bf16x8 lh[2], ll[2], rh[2], rl[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const __bf16 *L0 = reinterpret_cast<const __bf16 *>(lt);
+        lh[b] = *reinterpret_cast<const bf16x8 *>(L0 + (wm * 64 + b * 32 + li) * LD::RP + k);
+        if constexpr (MODE == MODE_UPDATE) {
+          rh[b] = tr_frag(reinterpret_cast<const __bf16 *>(rt), LD::CP, k, wn * 64 + b * 32, lane);
+        } else {
+          rh[b] = *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const __bf16 *>(rt) +
+                                                    (wn * 64 + b * 32 + li) * LD::RP + k);
+        }
+        if constexpr (PREC == PREC_BF16X3) {
+          const __bf16 *L1 = reinterpret_cast<const __bf16 *>(lt + LD::ROWT);
+          ll[b] = *reinterpret_cast<const bf16x8 *>(L1 + (wm * 64 + b * 32 + li) * LD::RP + k);
+          if constexpr (MODE == MODE_UPDATE) {
+            rl[b] = tr_frag(reinterpret_cast<const __bf16 *>(rt + LD::COLT), LD::CP, k, wn * 64 + b * 32, lane);
+          } else {
+            rl[b] = *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const __bf16 *>(rt + LD::ROWT) +
+                                                      (wn * 64 + b * 32 + li) * LD::RP + k);
+          }
+        }
+      }
+      if constexpr (PREC == PREC_BF16X3) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mma_bf16(ll[bi], rh[bj], acc[bi][bj]);
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mma_bf16(lh[bi], rl[bj], acc[bi][bj]);
+      }
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mma_bf16(lh[bi], rh[bj], acc[bi][bj]);
+    }
+  }
+}
+
+// One 128 x 128 output block of a NS product for one work item.
+//   GRAM    D = X X^T over the tile's X (upper blocks); writes A, or B = b A (+ a I) if c = 0
+//   SQUARE  D = A A^T; writes B = b A + c D (+ a I)
+//   UPDATE  D = B X;   writes X_next = D (+ a X for plain bf16)
+template <int PREC, int MODE>
+__global__ __launch_bounds__(THREADS) void gemm_ns_kernel(const GemmTile *__restrict__ tiles,
+                                                          const GemmWork *__restrict__ work, char *ws,
+                                                          GemmParams gp) {
+  using LD = GemmLds<PREC>;
+  __shared__ __attribute__((aligned(16))) char lds[LD::BYTES];
+  const GemmWork wk = work[blockIdx.x];
+  const TileG t = tile_of(tiles, wk.tile);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int i0 = wk.bi * BM, j0 = wk.bj * BM;
+
+  const Planes<PREC> Xc{ws + (gp.xsel ? t.x1 : t.x0), t.r, t.ldx};
+  const Planes<PREC> Xn{ws + (gp.xsel ? t.x0 : t.x1), t.r, t.ldx};
+  const Planes<PREC> A{ws + t.a, t.r, t.lda};
+  const Planes<PREC> B{ws + t.b, t.r, t.lda};
+  const Planes<PREC> Lp = MODE == MODE_GRAM ? Xc : (MODE == MODE_SQUARE ? A : B);
+  const Planes<PREC> Rp = MODE == MODE_GRAM ? Xc : (MODE == MODE_SQUARE ? A : Xc);
+  const int kdim = MODE == MODE_GRAM ? t.ldx : t.lda;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = f32x16{};
+
+  KRegs<PREC> kr;
+  gemm_load<PREC, MODE>(kr, Lp, i0, Rp, j0, 0);
+  gemm_store_lds<PREC, MODE>(kr, lds);
+  __syncthreads();
+  int cur = 0;
+  for (int kb = 0; kb < kdim; kb += BK) {
+    const bool more = kb + BK < kdim;
+    if (more) gemm_load<PREC, MODE>(kr, Lp, i0, Rp, j0, kb + BK);
+    gemm_compute<PREC, MODE>(acc, lds + cur * LD::STAGE, wm, wn, lane);
+    if (more) gemm_store_lds<PREC, MODE>(kr, lds + (cur ^ 1) * LD::STAGE);
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  // ---- epilogue: stage D^T in LDS (fp32), then write rows with 16-element stores
+  float *st = reinterpret_cast<float *>(lds);
+  {
+    const int li = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int il = wm * 64 + bi * 32 + 8 * g + 4 * half;
+          const int jl = wn * 64 + bj * 32 + li;
+          *reinterpret_cast<f32x4 *>(st + jl * LD::SP + il) =
+              f32x4{acc[bi][bj][4 * g], acc[bi][bj][4 * g + 1], acc[bi][bj][4 * g + 2], acc[bi][bj][4 * g + 3]};
+        }
+  }
+  __syncthreads();
+  const float a = gp.a, b = gp.b, c = gp.c;
+  const bool fold = gp.fold != 0;
+  // value of the product element (i, j) as stored
+  auto finish = [&](float d, int i, int j) -> float {
+    if constexpr (MODE == MODE_GRAM) {
+      if (c != 0.f) return d;
+      return b * d + ((fold && i == j) ? a : 0.f);
+    } else if constexpr (MODE == MODE_SQUARE) {
+      return __builtin_fmaf(c, d, b * A.get(i, j)) + ((fold && i == j) ? a : 0.f);
+    } else {
+      return fold ? d : __builtin_fmaf(a, Xc.get(i, j), d);
+    }
+  };
+  const Planes<PREC> O = MODE == MODE_GRAM ? (c != 0.f ? A : B) : (MODE == MODE_SQUARE ? B : Xn);
+  const int valid = MODE == MODE_UPDATE ? t.s : t.r;   // valid columns; the rest up to ld is 0
+  const int ldo = O.ld;
+  // (1) D rows: row i = i0 + il, columns j0 + jl .. +15 (staging columns)
+  for (int u = threadIdx.x; u < BM * (BM / 16); u += THREADS) {
+    const int il = u >> 3, jl = (u & 7) * 16;
+    const int i = i0 + il, j = j0 + jl;
+    if (i >= t.r || j >= ldo) continue;
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = j + q < valid ? finish(st[(jl + q) * LD::SP + il], i, j + q) : 0.f;
+    O.put16(i, j, v);
+  }
+  // (2) symmetric products: the mirrored block D^T at rows j0 + jl, columns i0 + il
+  if constexpr (MODE != MODE_UPDATE) {
+    if (wk.bi != wk.bj) {
+      for (int u = threadIdx.x; u < BM * (BM / 16); u += THREADS) {
+        const int jl = u >> 3, il = (u & 7) * 16;
+        const int j = j0 + jl, i = i0 + il;
+        if (j >= t.r || i >= ldo) continue;
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = i + q < valid ? finish(st[jl * LD::SP + il + q], i + q, j) : 0.f;
+        O.put16(j, i, v);
+      }
+    }
+  }
+}
+
+template <typename S, int PREC>
+hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmChunkLaunch &c, char *ws,
+                     const NSParams &p, hipStream_t stream) {
+  auto grid = [](int64_t n) { return dim3((unsigned)n); };
+  if (c.n_mom > 0x7fffffff || c.n_stg > 0x7fffffff || c.n_sym > 0x7fffffff || c.n_upd > 0x7fffffff ||
+      c.n_app > 0x7fffffff)
+    return hipErrorInvalidValue;
+  if (c.n_mom) hipLaunchKernelGGL(gemm_momentum_kernel<S>, grid(c.n_mom), dim3(THREADS), 0, stream, layers, tiles, c.mom, ws, p.beta);
+  if (c.tile_n) hipLaunchKernelGGL(gemm_norm_kernel, grid(c.tile_n), dim3(THREADS), 0, stream, tiles, (int)c.tile_first, ws, p.eps);
+  if (c.n_stg) hipLaunchKernelGGL((gemm_stage_kernel<S, PREC>), grid(c.n_stg), dim3(THREADS), 0, stream, layers, tiles, c.stg, ws);
+  GemmParams gp{p.a, p.b, p.c, 0, PREC != PREC_BF16};
+  for (int it = 0; it < p.steps; ++it) {
+    gp.xsel = it & 1;
+    hipLaunchKernelGGL((gemm_ns_kernel<PREC, MODE_GRAM>), grid(c.n_sym), dim3(THREADS), 0, stream, tiles, c.sym, ws, gp);
+    if (p.c != 0.f)
+      hipLaunchKernelGGL((gemm_ns_kernel<PREC, MODE_SQUARE>), grid(c.n_sym), dim3(THREADS), 0, stream, tiles, c.sym, ws, gp);
+    hipLaunchKernelGGL((gemm_ns_kernel<PREC, MODE_UPDATE>), grid(c.n_upd), dim3(THREADS), 0, stream, tiles, c.upd, ws, gp);
+  }
+  if (c.n_app)
+    hipLaunchKernelGGL((gemm_apply_kernel<PREC>), grid(c.n_app), dim3(THREADS), 0, stream, layers, tiles, c.app, ws,
+                       p.steps & 1, p.lr, p.write_update);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_chunk(int prec, int state_bf16, const LayerDesc *layers, const GemmTile *tiles,
+                             const GemmChunkLaunch &c, char *ws, const NSParams &p, hipStream_t stream) {
+  if (c.tile_n <= 0) return hipSuccess;
+  switch (prec) {
+    case PREC_F32:
+      return state_bf16 ? run_chunk<__bf16, PREC_F32>(layers, tiles, c, ws, p, stream)
+                        : run_chunk<float, PREC_F32>(layers, tiles, c, ws, p, stream);
+    case PREC_BF16:
+      return state_bf16 ? run_chunk<__bf16, PREC_BF16>(layers, tiles, c, ws, p, stream)
+                        : run_chunk<float, PREC_BF16>(layers, tiles, c, ws, p, stream);
+    case PREC_BF16X3:
+      return state_bf16 ? run_chunk<__bf16, PREC_BF16X3>(layers, tiles, c, ws, p, stream)
+                        : run_chunk<float, PREC_BF16X3>(layers, tiles, c, ws, p, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace himuon

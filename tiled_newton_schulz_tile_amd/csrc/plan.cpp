@@ -32,10 +32,33 @@ int fused_edge_for(int64_t e) {
   return 0;
 }
 
-size_t gemm_tile_workspace(int64_t r, int64_t s, int prec) {
-  (void)prec;
-  // X (double buffered, fp32), A and B (fp32, r x r), scale slot
-  return 2 * align256((size_t)r * s * 4) + 2 * align256((size_t)r * r * 4) + 256;
+namespace {
+int64_t roundup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+// byte sizes of the planes of one GEMM tile (4 bytes per element in every precision:
+// one fp32 plane, or bf16 hi and lo planes)
+struct GemmSizes {
+  int64_t r, s, ldx, lda, nred;
+  size_t x, ab, red;
+};
+GemmSizes gemm_sizes(int64_t h, int64_t w) {
+  GemmSizes z;
+  z.r = std::min(h, w);
+  z.s = std::max(h, w);
+  z.ldx = roundup(z.s, 32);
+  z.lda = roundup(z.r, 32);
+  z.nred = cdiv(h * w, kGemmMomentumBlock);
+  z.x = align256((size_t)z.r * z.ldx * 4);
+  z.ab = align256((size_t)z.r * z.lda * 4);
+  z.red = align256((size_t)(z.nred + 1) * 4);
+  return z;
+}
+}  // namespace
+
+size_t gemm_tile_workspace(int64_t h, int64_t w) {
+  const GemmSizes z = gemm_sizes(h, w);
+  return 2 * z.x + 2 * z.ab + z.red;
 }
 
 himuon_status plan_init(Plan &p, const himuon_layer *layers, int32_t n, const himuon_config *cfg,
@@ -163,6 +186,7 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
               FusedTile{(int32_t)li, (int32_t)r0, (int32_t)c0, (int16_t)h, (int16_t)w});
           issued += (double)K * split * 2.0 * e * e * e * (quintic ? 3.0 : 2.0);
         } else {
+          const GemmSizes z = gemm_sizes(h, w);
           GemmTile g{};
           g.layer = (int32_t)li;
           g.row0 = (int32_t)r0;
@@ -172,9 +196,19 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
           g.r = (int32_t)r;
           g.s = (int32_t)s;
           g.tall = h > w;
+          g.ldx = (int32_t)z.ldx;
+          g.lda = (int32_t)z.lda;
+          g.nred = (int32_t)z.nred;
           gt.push_back(g);
-          max_ws = std::max(max_ws, gemm_tile_workspace(r, s, prec));
-          issued += (double)K * split * (4.0 * r * r * s + (quintic ? 2.0 * r * r * r : 0.0));
+          max_ws = std::max(max_ws, gemm_tile_workspace(h, w));
+          {
+            // 128-blocks as launched: symmetric products on the upper blocks only, K
+            // padded to 32; the update over all blocks
+            const double nb = (double)cdiv(r, 128), nbs = (double)cdiv(z.ldx, 128);
+            const double sym = nb * (nb + 1) / 2 * 2.0 * 128 * 128;
+            issued += (double)K * split * (sym * z.ldx + (quintic ? sym * z.lda : 0.0) +
+                                           2.0 * 128 * 128 * nb * nbs * z.lda);
+          }
         }
       }
     }
@@ -186,34 +220,62 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
     err = m.str();
     return HIMUON_EBUDGET;
   }
-  // chunks: consecutive GEMM tiles whose workspaces fit the budget together
+  // chunks: consecutive GEMM tiles whose workspaces fit the budget together; each chunk
+  // gets the work lists of its grouped launches
   std::vector<GemmChunk> chunks;
+  std::vector<GemmWork> wmom, wstg, wsym, wupd, wapp;
   size_t ws_max = 0;
   {
     size_t cur = 0;
     int64_t first = 0;
+    auto close_chunk = [&](int64_t end) {
+      GemmChunk ch{};
+      ch.first = first;
+      ch.n = end - first;
+      ch.ws_bytes = cur;
+      ch.mom.first = (int64_t)wmom.size();
+      ch.stg.first = (int64_t)wstg.size();
+      ch.sym.first = (int64_t)wsym.size();
+      ch.upd.first = (int64_t)wupd.size();
+      ch.app.first = (int64_t)wapp.size();
+      for (int64_t i = first; i < end; ++i) {
+        const GemmTile &g = gt[(size_t)i];
+        const int32_t ti = (int32_t)i;
+        for (int32_t b = 0; b < g.nred; ++b) wmom.push_back(GemmWork{ti, b, 0});
+        for (int32_t bi = 0; bi < (int32_t)cdiv(g.r, 64); ++bi)
+          for (int32_t bj = 0; bj < (int32_t)cdiv(g.ldx, 64); ++bj) wstg.push_back(GemmWork{ti, bi, bj});
+        const int32_t nb = (int32_t)cdiv(g.r, 128);
+        for (int32_t bi = 0; bi < nb; ++bi)
+          for (int32_t bj = bi; bj < nb; ++bj) wsym.push_back(GemmWork{ti, bi, bj});
+        for (int32_t bi = 0; bi < nb; ++bi)
+          for (int32_t bj = 0; bj < (int32_t)cdiv(g.ldx, 128); ++bj) wupd.push_back(GemmWork{ti, bi, bj});
+        for (int32_t bi = 0; bi < (int32_t)cdiv(g.h, 64); ++bi)
+          for (int32_t bj = 0; bj < (int32_t)cdiv(g.w, 64); ++bj) wapp.push_back(GemmWork{ti, bi, bj});
+      }
+      ch.mom.n = (int64_t)wmom.size() - ch.mom.first;
+      ch.stg.n = (int64_t)wstg.size() - ch.stg.first;
+      ch.sym.n = (int64_t)wsym.size() - ch.sym.first;
+      ch.upd.n = (int64_t)wupd.size() - ch.upd.first;
+      ch.app.n = (int64_t)wapp.size() - ch.app.first;
+      chunks.push_back(ch);
+      ws_max = std::max(ws_max, cur);
+    };
     for (size_t i = 0; i < gt.size(); ++i) {
-      const size_t need = gemm_tile_workspace(gt[i].r, gt[i].s, prec);
+      const size_t need = gemm_tile_workspace(gt[i].h, gt[i].w);
       if (cur + need > c.workspace_budget && i > (size_t)first) {
-        chunks.push_back(GemmChunk{first, (int64_t)i - first, cur});
-        ws_max = std::max(ws_max, cur);
+        close_chunk((int64_t)i);
         first = (int64_t)i;
         cur = 0;
       }
-      const size_t base = cur;
-      const size_t xb = align256((size_t)gt[i].r * gt[i].s * 4);
-      const size_t ab = align256((size_t)gt[i].r * gt[i].r * 4);
-      gt[i].ws_x0 = (int64_t)base;
-      gt[i].ws_x1 = (int64_t)(base + xb);
-      gt[i].ws_a = (int64_t)(base + 2 * xb);
-      gt[i].ws_b = (int64_t)(base + 2 * xb + ab);
-      gt[i].ws_scale = (int64_t)(base + 2 * xb + 2 * ab);
+      const GemmSizes z = gemm_sizes(gt[i].h, gt[i].w);
+      gt[i].ws_x0 = (int64_t)cur;
+      gt[i].ws_x1 = (int64_t)(cur + z.x);
+      gt[i].ws_a = (int64_t)(cur + 2 * z.x);
+      gt[i].ws_b = (int64_t)(cur + 2 * z.x + z.ab);
+      gt[i].ws_red = (int64_t)(cur + 2 * z.x + 2 * z.ab);
       cur += need;
     }
-    if (!gt.empty()) {
-      chunks.push_back(GemmChunk{first, (int64_t)gt.size() - first, cur});
-      ws_max = std::max(ws_max, cur);
-    }
+    if (!gt.empty()) close_chunk((int64_t)gt.size());
   }
 
   p.tile = tile;
@@ -230,6 +292,11 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
   }
   p.gtiles = std::move(gt);
   p.chunks = std::move(chunks);
+  p.wmom = std::move(wmom);
+  p.wstg = std::move(wstg);
+  p.wsym = std::move(wsym);
+  p.wupd = std::move(wupd);
+  p.wapp = std::move(wapp);
   p.order = std::move(order);
   p.workspace_bytes = ws_max;
 
@@ -249,7 +316,9 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
   st.chunks = (int64_t)p.chunks.size();
   st.workspace_bytes = ws_max;
   st.table_bytes = p.ldesc.size() * sizeof(LayerDesc) + p.ftiles.size() * sizeof(FusedTile) +
-                   p.gtiles.size() * sizeof(GemmTile);
+                   p.gtiles.size() * sizeof(GemmTile) +
+                   (p.wmom.size() + p.wstg.size() + p.wsym.size() + p.wupd.size() + p.wapp.size()) *
+                       sizeof(GemmWork);
   st.ns_flops = ns_flops;
   st.issued_flops = issued;
   st.step_bytes = bytes;

@@ -22,9 +22,14 @@ struct FusedGroup {
   int64_t first, n;   // range in Plan::ftiles
 };
 
+struct Range {
+  int64_t first = 0, n = 0;
+};
+
 struct GemmChunk {
   int64_t first, n;   // range in Plan::gtiles
   size_t ws_bytes;    // workspace the chunk uses
+  Range mom, stg, sym, upd, app;  // ranges in the work lists
 };
 
 struct Plan {
@@ -36,6 +41,8 @@ struct Plan {
   std::vector<FusedGroup> fgroups;
   std::vector<GemmTile> gtiles;
   std::vector<GemmChunk> chunks;
+  // work lists of the GEMM path, concatenated over chunks
+  std::vector<GemmWork> wmom, wstg, wsym, wupd, wapp;
   std::vector<himuon_tile> order;   // every tile in table order (layer, row-major)
   himuon_stats stats{};
   size_t workspace_bytes = 0;
@@ -49,7 +56,7 @@ himuon_status plan_init(Plan &p, const himuon_layer *layers, int32_t n, const hi
 // (Re)builds the partition for tile size T (0 = FULL).
 himuon_status plan_partition(Plan &p, int32_t tile, std::string &err);
 
-// Workspace bytes the GEMM path needs for one tile with short side r, long side s.
-size_t gemm_tile_workspace(int64_t r, int64_t s, int prec);
+// Workspace bytes the GEMM path needs for one h x w tile.
+size_t gemm_tile_workspace(int64_t h, int64_t w);
 
 }  // namespace himuon
