@@ -28,20 +28,59 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
 METRIC = "HiMuon step ms & NS TFLOP/s (% MFMA peak) vs T, 8B-shaped stack"
 
+# HBM bytes of one launch of the T=128 fused kernel on this workload, from two
+# rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), scaled by the
+# readings of a 1 GiB elementwise copy (x2.0 read, x1.0 write).  Valid only for the
+# kernel source it was measured on (sha256 prefix of ns_fused.hip).
+TRAFFIC_T128 = {"source_sha256_16": "21f62614b97de32e", "fetch_kib": 27291104.0625,
+                "write_kib": 40894464.0, "fetch_scale": 2.0, "write_scale": 1.0}
+
+
+def measured_traffic():
+    import hashlib
+    src = os.path.join(ROOT, "tiled_newton_schulz_tile_amd", "csrc", "ns_fused.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    t = TRAFFIC_T128
+    if sha != t["source_sha256_16"]:
+        return None
+    return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_inputs(shapes, device, seed0=3000):
+def build_inputs(shapes, device, seed0=3000, kind="power-law"):
+    """Seeded inputs.  power-law: the recipe of the synth module (Haar factors shared per
+    shape).  randn: G = 0.01 N(0, 1), used for counter runs, where the QR of the recipe
+    cannot run under the profiler; the kernels' traffic does not depend on the values."""
     import synth
     import torch
     t0 = time.time()
-    layers = synth.stack_inputs(shapes, seed0, device=device, state_dtype=torch.bfloat16,
-                                share_factors=True)
+    if kind == "randn":
+        g = torch.Generator(device=device).manual_seed(seed0)
+        layers = []
+        for h, w in shapes:
+            G = (0.01 * torch.randn(h, w, device=device, generator=g)).to(torch.bfloat16)
+            layers.append((synth.weights(h, w, seed0, device), torch.zeros_like(G), G))
+    else:
+        layers = synth.stack_inputs(shapes, seed0, device=device, state_dtype=torch.bfloat16,
+                                    share_factors=True)
     torch.cuda.synchronize()
-    log(f"[bench] generated {len(layers)} matrices in {time.time() - t0:.1f}s")
+    log(f"[bench] generated {len(layers)} matrices ({kind}) in {time.time() - t0:.1f}s")
     return layers
+
+
+def copy_calibration(device, nbytes=1 << 30):
+    """A plain elementwise copy of known size (nbytes read, nbytes written) whose
+    FETCH_SIZE / WRITE_SIZE readings scale the counters of the HiMuon kernels."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=device)
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {nbytes} B read, {nbytes} B written")
 
 
 def time_steps(opt, steps, warmup, lr=0.02):
@@ -94,10 +133,12 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tile", type=int, default=128)
-    ap.add_argument("--sweep", type=str, default="32,64")
+    ap.add_argument("--sweep", type=str, default="32,64,256,full")
     ap.add_argument("--sweep-steps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--workload", type=str, default="llama3-8b-32L")
+    ap.add_argument("--inputs", choices=["power-law", "randn"], default="power-law")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the HiMuon step is tile-local and this build runs on "
@@ -113,7 +154,7 @@ def main():
     dev = torch.device("cuda:0")
     shapes = synth.STACKS[args.workload]
     K, coeffs = 5, hm.QUINTIC
-    layers = build_inputs(shapes, dev)
+    layers = build_inputs(shapes, dev, kind=args.inputs)
     opt = hm.HiMuon(layers, args.tile, K, coeffs, beta=0.95, eps=1e-7,
                     workspace_budget=4 * 10 ** 9, precision=hm.PREC_BF16X3)
     st = opt.stats()
@@ -145,6 +186,8 @@ def main():
             sweep.append({"tile": tok, "error": str(e)})
             log(f"[bench] sweep T={tok}: {e}")
     opt.close()
+    if args.copy_calibration:
+        copy_calibration(dev)
 
     cpu = None
     if not args.no_cpu:
@@ -167,8 +210,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "precision": "bf16x3: operands split hi+lo bf16, 3 MFMA products, fp32 accumulate",
-        "data": "synthetic: G = U diag(1/i) V^T + 0.01 N(0,1) per matrix (Haar U, V shared per "
-                "shape), M0 = 0, W0 = 0.02 N(0,1); seeded",
+        "data": ("synthetic: G = U diag(1/i) V^T + 0.01 N(0,1) per matrix (Haar U, V shared per "
+                 "shape), M0 = 0, W0 = 0.02 N(0,1); seeded") if args.inputs == "power-law" else
+                "synthetic: G = 0.01 N(0,1), M0 = 0, W0 = 0.02 N(0,1); seeded (counter run)",
         "config": {"workload": f"{args.workload} HiMuon step (Llama-3-8B-shaped stack, 224 "
                                f"matrices, 6.98e9 params), T={args.tile}, K={K}, quintic",
                    "tile": args.tile, "ns_steps": K, "coeffs": "quintic", "state_dtype": "bf16",
@@ -179,7 +223,9 @@ def main():
         "hbm_gbps": round(gbps, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic() if (args.tile == 128 and args.workload == "llama3-8b-32L")
+                     else None,
                      "kernel": "fused_step_kernel<128, bf16x3, bf16 state>",
                      "launches_per_step": 1, "algorithmic_flops_per_launch": st["ns_flops"],
                      "issued_flops_per_launch": st["issued_flops"],
