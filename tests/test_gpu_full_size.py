@@ -1,0 +1,158 @@
+"""Parity at the full sizes of the layer stacks, in the launch configuration bench.py
+times (MI355X only).  The oracle recomputes sampled tiles one by one from the momentum
+the GPU stored; O is recovered from the weight change, O = (W0 - W1) / lr, so the
+measured configuration (no update output) is the one checked.  Bars: bf16 path max-abs
+<= 2e-2 and relative Frobenius <= 1e-2 per tile sample; momentum bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+hm = pytest.importorskip("tiled_newton_schulz_tile_amd")
+Q, C = oracle.COEFFS_QUINTIC, oracle.COEFFS_CUBIC
+LR = 0.02
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def sample_tiles(shapes, T, n, seed, whole=()):
+    """n random (layer, r0, c0, h, w) tiles plus every tile of the layers in `whole`."""
+    rng = np.random.default_rng(seed)
+    picks = []
+    for li in whole:
+        H, W = shapes[li]
+        picks += [(li,) + t for t in oracle.tiles(H, W, T)]
+    for _ in range(n):
+        li = int(rng.integers(len(shapes)))
+        H, W = shapes[li]
+        tl = oracle.tiles(H, W, T)
+        picks.append((li,) + tl[int(rng.integers(len(tl)))])
+    return picks
+
+
+def grab(layers, picks, idx):
+    """CPU copies of tensor `idx` of each picked tile."""
+    return [layers[li][idx][r0:r0 + h, c0:c0 + w].cpu() for li, r0, c0, h, w in picks]
+
+
+def check_step(picks, W0, W1, M1, T, K, coeffs, tol=(2e-2, 1e-2)):
+    worst = [0.0, 0.0]
+    O_ref = [oracle.ns_tile(m.double().numpy(), K, coeffs) for m in M1]
+    num = den = 0.0
+    for w0, w1, o in zip(W0, W1, O_ref):
+        o_gpu = (w0.double().numpy() - w1.double().numpy()) / LR
+        d = o_gpu - o
+        worst[0] = max(worst[0], float(np.abs(d).max()))
+        num += float(np.sum(d * d))
+        den += float(np.sum(o * o))
+        worst[1] = max(worst[1], float(np.linalg.norm(d) / max(np.linalg.norm(o), 1e-300)))
+    assert worst[0] <= tol[0] and worst[1] <= tol[1], worst
+    return worst, (num / den) ** 0.5
+
+
+def test_llama3_8b_stack_t128_bench_configuration():
+    _need_gpu()
+    shapes = synth.STACKS["llama3-8b-32L"]
+    import bench
+    layers = bench.build_inputs(shapes, torch.device("cuda:0"))
+    # two complete matrices (a 4096x14336 gate and the 14336x4096 down of layer 0) + 1000 tiles
+    picks = sample_tiles(shapes, 128, 1000, 7, whole=(4, 6))
+    W0 = grab(layers, picks, 0)
+    G = grab(layers, picks, 2)
+    opt = hm.HiMuon(layers, 128, 5, hm.QUINTIC, workspace_budget=4 * 10 ** 9, precision=hm.PREC_BF16X3)
+    opt.step(LR)
+    torch.cuda.synchronize()
+    opt.close()
+    W1 = grab(layers, picks, 0)
+    M1 = grab(layers, picks, 1)
+    for g, m in zip(G, M1):
+        assert torch.equal(g, m)           # M0 = 0: the stored momentum is G exactly
+    worst, rf = check_step(picks, W0, W1, M1, 128, 5, Q)
+    print(f"\n8B stack T=128: {len(picks)} tiles, worst max-abs {worst[0]:.2e}, "
+          f"worst tile rel-F {worst[1]:.2e}, pooled rel-F {rf:.2e}")
+    assert worst[0] < 2e-3                 # bf16x3 is fp32-class
+
+
+def test_gpt2_stack_every_tile():
+    _need_gpu()
+    shapes = synth.STACKS["gpt2-small-12L"]
+    layers = synth.stack_inputs(shapes, 500, device="cuda", state_dtype=torch.bfloat16, share_factors=True)
+    U = [torch.zeros(h, w, device="cuda") for h, w in shapes]
+    opt = hm.HiMuon([l + (u,) for l, u in zip(layers, U)], 128, 5, hm.QUINTIC)
+    opt.step(LR)
+    torch.cuda.synchronize()
+    opt.close()
+    worst = [0.0, 0.0]
+    for (Wt, M, G), u in zip(layers, U):
+        O = oracle.tiled_ns(M.double().cpu().numpy(), 128, 5, Q)
+        d = u.double().cpu().numpy() - O
+        worst[0] = max(worst[0], float(np.abs(d).max()))
+        worst[1] = max(worst[1], float(np.linalg.norm(d) / np.linalg.norm(O)))
+    print(f"\nGPT-2 stack every tile: max-abs {worst[0]:.2e} rel-F {worst[1]:.2e}")
+    assert worst[0] <= 2e-3 and worst[1] <= 1e-3
+
+
+@pytest.mark.parametrize("T", [32, 64, 128, 256, 0])
+def test_decoder_1b_stack_sweep(T):
+    _need_gpu()
+    shapes = synth.STACKS["decoder-1b-16L"]
+    layers = synth.stack_inputs(shapes, 800, device="cuda", state_dtype=torch.bfloat16, share_factors=True)
+    if T == 0:
+        picks = [(0, 0, 0, 2048, 2048)]      # one full 2048x2048 matrix
+    else:
+        picks = sample_tiles(shapes, T, 300, 11)
+    W0 = grab(layers, picks, 0)
+    opt = hm.HiMuon(layers, T, 5, hm.QUINTIC, workspace_budget=4 * 10 ** 9)
+    opt.step(LR)
+    torch.cuda.synchronize()
+    opt.close()
+    W1 = grab(layers, picks, 0)
+    M1 = grab(layers, picks, 1)
+    worst, rf = check_step(picks, W0, W1, M1, T, 5, Q)
+    print(f"\n1B stack T={T}: {len(picks)} tiles, worst max-abs {worst[0]:.2e}, pooled rel-F {rf:.2e}")
+
+
+@pytest.mark.parametrize("coeffs,K", [(C, 5), (C, 8), (Q, 5), (Q, 8)])
+def test_ragged_stack_runtime_schedule(coeffs, K):
+    """24 ragged matrices (H, W uniform in [100, 6000]); T = 64 -> 128 -> 256 -> FULL,
+    three steps each (the full schedule runs ten), a fresh gradient per step, momentum
+    carried over.  Each step is checked on sampled tiles from the GPU's pre-step state
+    (FULL steps on the matrices up to 1500 on their longer side)."""
+    _need_gpu()
+    shapes = synth.ragged_shapes()
+    n = len(shapes)
+    Gs = [torch.zeros(h, w, dtype=torch.bfloat16, device="cuda") for h, w in shapes]
+    Ms = [torch.zeros_like(g) for g in Gs]
+    Ws = [synth.weights(h, w, 4100 + i, "cuda") for i, (h, w) in enumerate(shapes)]
+    opt = hm.HiMuon(list(zip(Ws, Ms, Gs)), 64, K, coeffs, workspace_budget=4 * 10 ** 9)
+    small = [i for i, (h, w) in enumerate(shapes) if max(h, w) <= 1500]
+    step = 0
+    for T in (64, 128, 256, 0):
+        opt.set_tile_schedule(T)
+        for _ in range(3):
+            for i, (h, w) in enumerate(shapes):
+                Gs[i].copy_(0.3 * torch.randn(h, w, device="cuda", generator=torch.Generator(device="cuda").manual_seed(5000 + 97 * step + i)))
+            if T == 0:
+                picks = [(i, 0, 0) + shapes[i] for i in small[:3]]
+            else:
+                picks = sample_tiles(shapes, T, 40, 600 + step)
+            layers = [(Ws[i], Ms[i], Gs[i]) for i in range(n)]
+            W0 = grab(layers, picks, 0)
+            Mprev = grab(layers, picks, 1)
+            Gcur = grab(layers, picks, 2)
+            opt.step(LR)
+            torch.cuda.synchronize()
+            W1 = grab(layers, picks, 0)
+            M1 = grab(layers, picks, 1)
+            for mp, g, m in zip(Mprev, Gcur, M1):
+                want = oracle.momentum_stored(mp.float().numpy(), g.float().numpy(), 0.95, "bf16")
+                assert np.array_equal(m.float().numpy(), want)
+            check_step(picks, W0, W1, M1, T, K, coeffs)
+            step += 1
+    opt.close()
