@@ -54,13 +54,28 @@ struct Geo {
   static constexpr int TPB = WPT == 1 ? 4 : 1;        // tiles per workgroup
   static constexpr int NT = 64 * WPT;                 // threads per tile
   static constexpr int THREADS = NT * TPB;
-  static constexpr int PB = TS + 8;                   // bf16 row pitch (elements)
+  // bf16 rows of 128-tiles are 256 bytes, unpadded, with their 16-byte chunks permuted
+  // (chunk c of row r is stored at c ^ swz(r)): sixteen consecutive rows reading one
+  // chunk, and four rows reading four adjacent chunks (transposing reads), then touch
+  // sixteen distinct chunks.  Other tiles use a padded pitch.
+  static constexpr bool SWZ = TS == 128;
+  static constexpr int PB = SWZ ? TS : TS + 8;        // bf16 row pitch (elements)
   static constexpr int PF = TS + 4;                   // fp32 row pitch (elements)
   static constexpr int REGION = PREC == PREC_F32 ? TS * PF * 4
                               : PREC == PREC_BF16 ? TS * PB * 2 : TS * PB * 4;
   static constexpr int TILE_LDS = 2 * REGION > TS * PF * 4 ? 2 * REGION : TS * PF * 4;
+  // the chunk permutation of row r: the two 2-bit halves of r % 16 swapped
+  static __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+  // column c of a row congruent to r16 modulo 16, as stored
+  static __device__ __forceinline__ int bcol(int r16, int c) {
+    if constexpr (SWZ) {
+      return c ^ (swz(r16) << 3);
+    } else {
+      return c;
+    }
+  }
   // element offset of (r, c) in a bf16 matrix
-  static __device__ __forceinline__ int bidx(int r, int c) { return r * PB + c; }
+  static __device__ __forceinline__ int bidx(int r, int c) { return r * PB + bcol(r & 15, c); }
   // workgroup barriers synchronise one tile: several tiles per workgroup only with
   // one wave per tile
   static_assert(WPT == 1 || TPB == 1, "tile groups must not share s_barrier");
@@ -112,6 +127,22 @@ __device__ __forceinline__ void tile_sync() {
   }
 }
 
+// Transposing operand read (see dev::tr_frag) in the tile's bf16 layout G::bidx.  The
+// 8-byte pieces stay inside one 16-byte chunk, so the chunk permutation moves them whole.
+template <class G>
+__device__ __forceinline__ bf16x8 tr_frag_g(const __bf16 *buf, int k, int m, int lane) {
+  // k = (multiple of 16) + 8 * (lane / 32): the rows' residues modulo 16 depend on the
+  // lane only
+  const int L = lane & 15, g = (lane >> 4) & 1, h8 = (lane >> 5) * 8;
+  const int col = m + 16 * g + 4 * (L & 3);
+  const __bf16 *p0 = buf + (k + (L >> 2)) * G::PB + G::bcol(h8 + (L >> 2), col);
+  const __bf16 *p1 = buf + (k + 4 + (L >> 2)) * G::PB + G::bcol(h8 + 4 + (L >> 2), col);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(p0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(p1));
+  const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // ------------------------------------------------------------------ wave GEMM
 // acc.b[bi][bj] (+)= sum_k L(m, k) R(n, k) for m in the wave's L block, n in its R block.
 // L(m, k) = Lmat[m][k] (TRANS_L false) or Lmat[k][m] (TRANS_L true); R(n, k) = Rmat[n][k].
@@ -149,24 +180,31 @@ __device__ __forceinline__ void gemm_chunk(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>:
           acc.b[bi][bj] = mma_f32(lf[bi][e], rf[bj][e], (ZERO && e == 0) ? f32x16{} : acc.b[bi][bj]);
   } else {
     const int k = kb + 8 * half;
+    // the operands' rows are all congruent to lane % 16 modulo 16, so one column offset
+    // serves every plain read of this chunk; kept opaque so that it is formed here,
+    // once per chunk, rather than hoisted for every chunk of the loop
+    int ko = G::bcol(li & 15, k);
+    if constexpr (G::SWZ) asm("" : "+v"(ko));
     bf16x8 lh[NI], rh[NJ];
     bf16x8 ll[NI], rl[NJ];
 #pragma unroll
     for (int b = 0; b < NI; ++b) {
       const int m = l0 + b * 32 + li;
       if constexpr (TRANS_L) {
-        lh[b] = tr_frag(Lm.hi, G::PB, k, l0 + b * 32, lane);
-        if constexpr (PREC == PREC_BF16X3) ll[b] = tr_frag(Lm.lo, G::PB, k, l0 + b * 32, lane);
+        lh[b] = tr_frag_g<G>(Lm.hi, k, l0 + b * 32, lane);
+        if constexpr (PREC == PREC_BF16X3) ll[b] = tr_frag_g<G>(Lm.lo, k, l0 + b * 32, lane);
       } else {
-        lh[b] = *reinterpret_cast<const bf16x8 *>(Lm.hi + G::bidx(m, k));
-        if constexpr (PREC == PREC_BF16X3) ll[b] = *reinterpret_cast<const bf16x8 *>(Lm.lo + G::bidx(m, k));
+        const int o = m * G::PB + ko;
+        lh[b] = *reinterpret_cast<const bf16x8 *>(Lm.hi + o);
+        if constexpr (PREC == PREC_BF16X3) ll[b] = *reinterpret_cast<const bf16x8 *>(Lm.lo + o);
       }
     }
 #pragma unroll
     for (int b = 0; b < NJ; ++b) {
       const int n = r0 + b * 32 + li;
-      rh[b] = *reinterpret_cast<const bf16x8 *>(Rm.hi + G::bidx(n, k));
-      if constexpr (PREC == PREC_BF16X3) rl[b] = *reinterpret_cast<const bf16x8 *>(Rm.lo + G::bidx(n, k));
+      const int o = n * G::PB + ko;
+      rh[b] = *reinterpret_cast<const bf16x8 *>(Rm.hi + o);
+      if constexpr (PREC == PREC_BF16X3) rl[b] = *reinterpret_cast<const bf16x8 *>(Rm.lo + o);
     }
     if constexpr (PREC == PREC_BF16X3) {
       // small cross terms first: lo * hi + hi * lo + hi * hi
@@ -238,12 +276,14 @@ __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>
           bf16x4 hi;
 #pragma unroll
           for (int e = 0; e < 4; ++e) hi[e] = (__bf16)v[e];
-          *reinterpret_cast<bf16x4 *>(m.hi + G::bidx(col, row)) = hi;
+          // col = (multiple of 32) + lane % 32
+          const int o = col * G::PB + G::bcol(li & 15, row);
+          *reinterpret_cast<bf16x4 *>(m.hi + o) = hi;
           if constexpr (PREC == PREC_BF16X3) {
             bf16x4 lo;
 #pragma unroll
             for (int e = 0; e < 4; ++e) lo[e] = (__bf16)(v[e] - (float)hi[e]);
-            *reinterpret_cast<bf16x4 *>(m.lo + G::bidx(col, row)) = lo;
+            *reinterpret_cast<bf16x4 *>(m.lo + o) = lo;
           }
         }
       }
