@@ -44,6 +44,12 @@ struct Acc {
 };
 
 // ------------------------------------------------------------------ geometry
+#ifndef HIMUON_SCHED_GEMM
+#define HIMUON_SCHED_GEMM 1
+#endif
+// order the GEMM loops' LDS reads and MFMAs explicitly (reads one chunk ahead)
+constexpr bool SCHED_GEMM = HIMUON_SCHED_GEMM != 0;
+
 template <int TS, int PREC>
 struct Geo {
   // each wave owns a WBM x WBN block of every product; two waves share a SIMD
@@ -148,36 +154,37 @@ __device__ __forceinline__ bf16x8 tr_frag_g(const __bf16 *buf, int k, int m, int
 // L(m, k) = Lmat[m][k] (TRANS_L false) or Lmat[k][m] (TRANS_L true); R(n, k) = Rmat[n][k].
 // MFMA lane layout (32x32): operand lane l holds row (l % 32) of its 32-block and a
 // run of contiguous k selected by l / 32; both operands use the same k runs.
-// ZERO: this chunk starts the sum (the accumulators are not read).
-template <int TS, int PREC, bool TRANS_L, bool ZERO>
-__device__ __forceinline__ void gemm_chunk(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &Lm, int l0,
-                                           const Mat<PREC> &Rm, int r0, int lane, int kb) {
+
+// One k-chunk of operand fragments (16 k for bf16 operands, 8 for fp32).
+template <int TS, int PREC>
+struct Frags {
+  static constexpr int NI = Geo<TS, PREC>::NI, NJ = Geo<TS, PREC>::NJ;
+  f32x4 lf[NI], rf[NJ];     // fp32
+  bf16x8 lh[NI], rh[NJ];    // bf16 (hi parts)
+  bf16x8 ll[NI], rl[NJ];    // bf16x3 lo parts
+};
+
+template <int TS, int PREC, bool TRANS_L>
+__device__ __forceinline__ void load_frags(Frags<TS, PREC> &f, const Mat<PREC> &Lm, int l0, const Mat<PREC> &Rm,
+                                           int r0, int lane, int kb) {
   using G = Geo<TS, PREC>;
   constexpr int NI = G::NI, NJ = G::NJ;
   const int li = lane & 31, half = lane >> 5;
   if constexpr (PREC == PREC_F32) {
     constexpr int PF = G::PF;
     const int k = kb + 4 * half;
-    f32x4 lf[NI], rf[NJ];
 #pragma unroll
     for (int b = 0; b < NI; ++b) {
       const int m = l0 + b * 32 + li;
       if constexpr (TRANS_L) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lf[b][e] = Lm.f[(k + e) * PF + m];
+        for (int e = 0; e < 4; ++e) f.lf[b][e] = Lm.f[(k + e) * PF + m];
       } else {
-        lf[b] = *reinterpret_cast<const f32x4 *>(Lm.f + m * PF + k);
+        f.lf[b] = *reinterpret_cast<const f32x4 *>(Lm.f + m * PF + k);
       }
     }
 #pragma unroll
-    for (int b = 0; b < NJ; ++b) rf[b] = *reinterpret_cast<const f32x4 *>(Rm.f + (r0 + b * 32 + li) * PF + k);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int bi = 0; bi < NI; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < NJ; ++bj)
-          acc.b[bi][bj] = mma_f32(lf[bi][e], rf[bj][e], (ZERO && e == 0) ? f32x16{} : acc.b[bi][bj]);
+    for (int b = 0; b < NJ; ++b) f.rf[b] = *reinterpret_cast<const f32x4 *>(Rm.f + (r0 + b * 32 + li) * PF + k);
   } else {
     const int k = kb + 8 * half;
     // the operands' rows are all congruent to lane % 16 modulo 16, so one column offset
@@ -185,60 +192,115 @@ __device__ __forceinline__ void gemm_chunk(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>:
     // once per chunk, rather than hoisted for every chunk of the loop
     int ko = G::bcol(li & 15, k);
     if constexpr (G::SWZ) asm("" : "+v"(ko));
-    bf16x8 lh[NI], rh[NJ];
-    bf16x8 ll[NI], rl[NJ];
-#pragma unroll
-    for (int b = 0; b < NI; ++b) {
-      const int m = l0 + b * 32 + li;
+    // issued in the order the MFMAs consume them (see mma_frags)
+    auto lread = [&](const __bf16 *plane, int b) -> bf16x8 {
       if constexpr (TRANS_L) {
-        lh[b] = tr_frag_g<G>(Lm.hi, k, l0 + b * 32, lane);
-        if constexpr (PREC == PREC_BF16X3) ll[b] = tr_frag_g<G>(Lm.lo, k, l0 + b * 32, lane);
+        return tr_frag_g<G>(plane, k, l0 + b * 32, lane);
       } else {
-        const int o = m * G::PB + ko;
-        lh[b] = *reinterpret_cast<const bf16x8 *>(Lm.hi + o);
-        if constexpr (PREC == PREC_BF16X3) ll[b] = *reinterpret_cast<const bf16x8 *>(Lm.lo + o);
+        return *reinterpret_cast<const bf16x8 *>(plane + (l0 + b * 32 + li) * G::PB + ko);
       }
-    }
+    };
+    auto rread = [&](const __bf16 *plane, int b) -> bf16x8 {
+      return *reinterpret_cast<const bf16x8 *>(plane + (r0 + b * 32 + li) * G::PB + ko);
+    };
 #pragma unroll
-    for (int b = 0; b < NJ; ++b) {
-      const int n = r0 + b * 32 + li;
-      const int o = n * G::PB + ko;
-      rh[b] = *reinterpret_cast<const bf16x8 *>(Rm.hi + o);
-      if constexpr (PREC == PREC_BF16X3) rl[b] = *reinterpret_cast<const bf16x8 *>(Rm.lo + o);
-    }
+    for (int b = 0; b < NJ; ++b) f.rh[b] = rread(Rm.hi, b);
     if constexpr (PREC == PREC_BF16X3) {
-      // small cross terms first: lo * hi + hi * lo + hi * hi
 #pragma unroll
-      for (int bi = 0; bi < NI; ++bi)
+      for (int b = 0; b < NI; ++b) f.ll[b] = lread(Lm.lo, b);
 #pragma unroll
-        for (int bj = 0; bj < NJ; ++bj)
-          acc.b[bi][bj] = mma_bf16(ll[bi], rh[bj], ZERO ? f32x16{} : acc.b[bi][bj]);
-#pragma unroll
-      for (int bi = 0; bi < NI; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(lh[bi], rl[bj], acc.b[bi][bj]);
-#pragma unroll
-      for (int bi = 0; bi < NI; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(lh[bi], rh[bj], acc.b[bi][bj]);
-    } else {
-#pragma unroll
-      for (int bi = 0; bi < NI; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < NJ; ++bj)
-          acc.b[bi][bj] = mma_bf16(lh[bi], rh[bj], ZERO ? f32x16{} : acc.b[bi][bj]);
+      for (int b = 0; b < NJ; ++b) f.rl[b] = rread(Rm.lo, b);
     }
+#pragma unroll
+    for (int b = 0; b < NI; ++b) f.lh[b] = lread(Lm.hi, b);
   }
 }
 
-// Full K = TS contraction; ZERO: start from zero, else accumulate onto acc.
+// The MFMAs of one chunk; zero: this chunk starts the sum (the accumulators are not read).
+template <int TS, int PREC>
+__device__ __forceinline__ void mma_frags(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Frags<TS, PREC> &f,
+                                          bool zero) {
+  constexpr int NI = Geo<TS, PREC>::NI, NJ = Geo<TS, PREC>::NJ;
+  if constexpr (PREC == PREC_F32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int bi = 0; bi < NI; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NJ; ++bj)
+          acc.b[bi][bj] = mma_f32(f.lf[bi][e], f.rf[bj][e], (zero && e == 0) ? f32x16{} : acc.b[bi][bj]);
+  } else if constexpr (PREC == PREC_BF16X3) {
+    // small cross terms first: lo * hi + hi * lo + hi * hi
+#pragma unroll
+    for (int bi = 0; bi < NI; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(f.ll[bi], f.rh[bj], zero ? f32x16{} : acc.b[bi][bj]);
+#pragma unroll
+    for (int bi = 0; bi < NI; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(f.lh[bi], f.rl[bj], acc.b[bi][bj]);
+#pragma unroll
+    for (int bi = 0; bi < NI; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(f.lh[bi], f.rh[bj], acc.b[bi][bj]);
+  } else {
+#pragma unroll
+    for (int bi = 0; bi < NI; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(f.lh[bi], f.rh[bj], zero ? f32x16{} : acc.b[bi][bj]);
+  }
+}
+
+// reads of the next chunk go out during the first half of a chunk's MFMAs
+template <int NM, int NR>
+constexpr int reads_per_mfma() {
+  return (NR + (NM + 1) / 2 - 1) / ((NM + 1) / 2);
+}
+
+// Instruction-scheduler directives: NM MFMAs, each followed by up to RPM LDS reads,
+// until NR reads are placed.
+template <int NM, int NR, int RPM>
+__device__ __forceinline__ void sched_mfma_reads() {
+  if constexpr (NM > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NR < RPM ? NR : RPM, 0);
+    sched_mfma_reads<NM - 1, (NR > RPM ? NR - RPM : 0), RPM>();
+  }
+}
+template <int NC, int NM, int NR>
+__device__ __forceinline__ void sched_chunks() {
+  if constexpr (NC > 1) {
+    sched_mfma_reads<NM, NR, reads_per_mfma<NM, NR>()>();
+    sched_chunks<NC - 1, NM, NR>();
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+  }
+}
+
+// Full K = TS contraction; ZERO: start from zero, else accumulate onto acc.  The
+// fragments of chunk c + 1 are read from LDS while the MFMAs of chunk c run.
 template <int TS, int PREC, bool TRANS_L, bool ZERO>
 __device__ __forceinline__ void wave_gemm(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &Lm, int l0,
                                           const Mat<PREC> &Rm, int r0, int lane) {
+  using G = Geo<TS, PREC>;
   constexpr int KC = PREC == PREC_F32 ? 8 : 16;
-  gemm_chunk<TS, PREC, TRANS_L, ZERO>(acc, Lm, l0, Rm, r0, lane, 0);
-#pragma unroll 2
-  for (int kb = KC; kb < TS; kb += KC) gemm_chunk<TS, PREC, TRANS_L, false>(acc, Lm, l0, Rm, r0, lane, kb);
+  constexpr int NC = TS / KC;
+  // LDS read and MFMA instructions per chunk
+  constexpr int PLANES = PREC == PREC_BF16X3 ? 2 : 1;
+  constexpr int LREADS = PREC == PREC_F32 ? (TRANS_L ? 4 : 1) : (TRANS_L ? 2 : 1);
+  constexpr int NR = PLANES * (G::NI * LREADS + G::NJ);
+  constexpr int NM = (PREC == PREC_F32 ? 4 : PREC == PREC_BF16X3 ? 3 : 1) * G::NI * G::NJ;
+  Frags<TS, PREC> f[2];
+  load_frags<TS, PREC, TRANS_L>(f[0], Lm, l0, Rm, r0, lane, 0);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if (c + 1 < NC) load_frags<TS, PREC, TRANS_L>(f[(c + 1) & 1], Lm, l0, Rm, r0, lane, (c + 1) * KC);
+    mma_frags<TS, PREC>(acc, f[c & 1], ZERO && c == 0);
+  }
+  if constexpr (SCHED_GEMM) {
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    sched_chunks<NC, NM, NR>();
+  }
 }
 
 // Element (bi, bj, r) of a wave's accumulators sits at
