@@ -66,6 +66,12 @@ __device__ __forceinline__ unsigned short to_bf16_bits(float x) {
 __device__ __forceinline__ float bf16_bits_to_f32(unsigned short b) {
   return __builtin_bit_cast(float, (unsigned)b << 16);
 }
+// two floats rounded to bf16 (nearest even), a in the low half (one v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
 
 // LDS-only workgroup barrier: this wave's LDS traffic is complete, then all waves
 // meet; global loads in flight are not waited for.

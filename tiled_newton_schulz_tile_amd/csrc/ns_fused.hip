@@ -29,6 +29,8 @@
 // With fp32 or split (hi + lo) operands, a is added to B's diagonal and the update is
 // one product X^T (a I + B); with plain bf16 operands the update accumulates on top of
 // a X^T held in fp32 registers, so only the product's operands are rounded.
+#include <type_traits>
+
 #include "device_common.h"
 #include "himuon_internal.h"
 
@@ -335,17 +337,18 @@ __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>
         if constexpr (PREC == PREC_F32) {
           *reinterpret_cast<f32x4 *>(m.f + col * G::PF + row) = v;
         } else {
-          bf16x4 hi;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) hi[e] = (__bf16)v[e];
           // col = (multiple of 32) + lane % 32
           const int o = col * G::PB + G::bcol(li & 15, row);
-          *reinterpret_cast<bf16x4 *>(m.hi + o) = hi;
+          const u32x2 hi = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2 *>(m.hi + o) = hi;
           if constexpr (PREC == PREC_BF16X3) {
-            bf16x4 lo;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) lo[e] = (__bf16)(v[e] - (float)hi[e]);
-            *reinterpret_cast<bf16x4 *>(m.lo + o) = lo;
+            // the residuals v - hi are exact in fp32; hi is read back from the packed
+            // pair (low half: shift up, high half: mask), not converted again
+            const u32x2 lo = {pack_bf16x2(v[0] - __builtin_bit_cast(float, hi[0] << 16),
+                                          v[1] - __builtin_bit_cast(float, hi[0] & 0xffff0000u)),
+                              pack_bf16x2(v[2] - __builtin_bit_cast(float, hi[1] << 16),
+                                          v[3] - __builtin_bit_cast(float, hi[1] & 0xffff0000u))};
+            *reinterpret_cast<u32x2 *>(m.lo + o) = lo;
           }
         }
       }
@@ -760,7 +763,12 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     // LDS copy of X (fp32, or hi + lo bf16) carries X between steps.  Plain bf16 keeps
     // X in fp32 registers and forms a X there, since its LDS copy is bf16-rounded.
     constexpr bool FOLD_A = PREC != PREC_BF16;
-    for (int it = 0; it < prm.steps; ++it) {
+    // LASTC: the final step issues the loads of W for the update (dense tiles: the
+    // other variants lack the registers), so that their HBM latency passes while its
+    // last product runs
+    constexpr bool EARLY_W = DENSE;
+    auto ns_step = [&](auto LASTC) {
+      constexpr bool LAST = decltype(LASTC)::value;
       Acc<NI, NJ> acc;
       wave_gemm<TS, PREC, false, true>(acc, X, p0, X, q0, lane);     // A = X X^T
       if (cc != 0.f) {
@@ -784,16 +792,21 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
             for (int e = 0; e < 16; ++e) xr.b[bi][bj][e] *= ca;
       }
       tile_sync<G::WPT>();
+      if constexpr (LAST && EARLY_W) io.template load_w<DENSE>(t, L, gt);
       wave_gemm<TS, PREC, true, FOLD_A>(xr, X, p0, AB, q0, lane);     // X^T <- X^T (aI + B)
       tile_sync<G::WPT>();
-      if (it + 1 < prm.steps) {
+      if constexpr (!LAST) {
         store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
         tile_sync<G::WPT>();
       }
+    };
+    if (prm.steps > 0) {
+      for (int it = 0; it + 1 < prm.steps; ++it) ns_step(std::false_type{});
+      ns_step(std::true_type{});
     }
+    if (!EARLY_W || prm.steps == 0) io.template load_w<DENSE>(t, L, gt);
 
     // ---- reassembly and weight update ------------------------------------------
-    io.template load_w<DENSE>(t, L, gt);
     tile_sync<G::WPT>();
     store_acc_t_f32<TS, PREC>(xr, st, p0, q0, lane);
     tile_sync<G::WPT>();
