@@ -156,6 +156,8 @@ __device__ __forceinline__ bf16x8 tr_frag_g(const __bf16 *buf, int k, int m, int
 // L(m, k) = Lmat[m][k] (TRANS_L false) or Lmat[k][m] (TRANS_L true); R(n, k) = Rmat[n][k].
 // MFMA lane layout (32x32): operand lane l holds row (l % 32) of its 32-block and a
 // run of contiguous k selected by l / 32; both operands use the same k runs.
+// NB <= NI: only the first NB 32-row blocks of the L block take part.  RALIAS: the R
+// block is L's first block (same matrix, same rows), so its fragments are not read again.
 
 // One k-chunk of operand fragments (16 k for bf16 operands, 8 for fp32).
 template <int TS, int PREC>
@@ -166,17 +168,18 @@ struct Frags {
   bf16x8 ll[NI], rl[NJ];    // bf16x3 lo parts
 };
 
-template <int TS, int PREC, bool TRANS_L>
+template <int TS, int PREC, bool TRANS_L, int NB, bool RALIAS>
 __device__ __forceinline__ void load_frags(Frags<TS, PREC> &f, const Mat<PREC> &Lm, int l0, const Mat<PREC> &Rm,
                                            int r0, int lane, int kb) {
   using G = Geo<TS, PREC>;
-  constexpr int NI = G::NI, NJ = G::NJ;
+  constexpr int NJ = G::NJ;
+  static_assert(!RALIAS || (NJ == 1 && !TRANS_L), "aliased operands are one plain block");
   const int li = lane & 31, half = lane >> 5;
   if constexpr (PREC == PREC_F32) {
     constexpr int PF = G::PF;
     const int k = kb + 4 * half;
 #pragma unroll
-    for (int b = 0; b < NI; ++b) {
+    for (int b = 0; b < NB; ++b) {
       const int m = l0 + b * 32 + li;
       if constexpr (TRANS_L) {
 #pragma unroll
@@ -185,8 +188,12 @@ __device__ __forceinline__ void load_frags(Frags<TS, PREC> &f, const Mat<PREC> &
         f.lf[b] = *reinterpret_cast<const f32x4 *>(Lm.f + m * PF + k);
       }
     }
+    if constexpr (RALIAS) {
+      f.rf[0] = f.lf[0];
+    } else {
 #pragma unroll
-    for (int b = 0; b < NJ; ++b) f.rf[b] = *reinterpret_cast<const f32x4 *>(Rm.f + (r0 + b * 32 + li) * PF + k);
+      for (int b = 0; b < NJ; ++b) f.rf[b] = *reinterpret_cast<const f32x4 *>(Rm.f + (r0 + b * 32 + li) * PF + k);
+    }
   } else {
     const int k = kb + 8 * half;
     // the operands' rows are all congruent to lane % 16 modulo 16, so one column offset
@@ -205,49 +212,61 @@ __device__ __forceinline__ void load_frags(Frags<TS, PREC> &f, const Mat<PREC> &
     auto rread = [&](const __bf16 *plane, int b) -> bf16x8 {
       return *reinterpret_cast<const bf16x8 *>(plane + (r0 + b * 32 + li) * G::PB + ko);
     };
+    if constexpr (RALIAS) {
+      f.lh[0] = lread(Lm.hi, 0);
+      if constexpr (PREC == PREC_BF16X3) f.ll[0] = lread(Lm.lo, 0);
 #pragma unroll
-    for (int b = 0; b < NJ; ++b) f.rh[b] = rread(Rm.hi, b);
-    if constexpr (PREC == PREC_BF16X3) {
+      for (int b = 1; b < NB; ++b) {
+        if constexpr (PREC == PREC_BF16X3) f.ll[b] = lread(Lm.lo, b);
+        f.lh[b] = lread(Lm.hi, b);
+      }
+      f.rh[0] = f.lh[0];
+      if constexpr (PREC == PREC_BF16X3) f.rl[0] = f.ll[0];
+    } else {
 #pragma unroll
-      for (int b = 0; b < NI; ++b) f.ll[b] = lread(Lm.lo, b);
+      for (int b = 0; b < NJ; ++b) f.rh[b] = rread(Rm.hi, b);
+      if constexpr (PREC == PREC_BF16X3) {
 #pragma unroll
-      for (int b = 0; b < NJ; ++b) f.rl[b] = rread(Rm.lo, b);
+        for (int b = 0; b < NB; ++b) f.ll[b] = lread(Lm.lo, b);
+#pragma unroll
+        for (int b = 0; b < NJ; ++b) f.rl[b] = rread(Rm.lo, b);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) f.lh[b] = lread(Lm.hi, b);
     }
-#pragma unroll
-    for (int b = 0; b < NI; ++b) f.lh[b] = lread(Lm.hi, b);
   }
 }
 
 // The MFMAs of one chunk; zero: this chunk starts the sum (the accumulators are not read).
-template <int TS, int PREC>
+template <int TS, int PREC, int NB>
 __device__ __forceinline__ void mma_frags(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Frags<TS, PREC> &f,
                                           bool zero) {
-  constexpr int NI = Geo<TS, PREC>::NI, NJ = Geo<TS, PREC>::NJ;
+  constexpr int NJ = Geo<TS, PREC>::NJ;
   if constexpr (PREC == PREC_F32) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
 #pragma unroll
-      for (int bi = 0; bi < NI; ++bi)
+      for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
         for (int bj = 0; bj < NJ; ++bj)
           acc.b[bi][bj] = mma_f32(f.lf[bi][e], f.rf[bj][e], (zero && e == 0) ? f32x16{} : acc.b[bi][bj]);
   } else if constexpr (PREC == PREC_BF16X3) {
     // small cross terms first: lo * hi + hi * lo + hi * hi
 #pragma unroll
-    for (int bi = 0; bi < NI; ++bi)
+    for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
       for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(f.ll[bi], f.rh[bj], zero ? f32x16{} : acc.b[bi][bj]);
 #pragma unroll
-    for (int bi = 0; bi < NI; ++bi)
+    for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
       for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(f.lh[bi], f.rl[bj], acc.b[bi][bj]);
 #pragma unroll
-    for (int bi = 0; bi < NI; ++bi)
+    for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
       for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(f.lh[bi], f.rh[bj], acc.b[bi][bj]);
   } else {
 #pragma unroll
-    for (int bi = 0; bi < NI; ++bi)
+    for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
       for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(f.lh[bi], f.rh[bj], zero ? f32x16{} : acc.b[bi][bj]);
   }
@@ -281,27 +300,86 @@ __device__ __forceinline__ void sched_chunks() {
 
 // Full K = TS contraction; ZERO: start from zero, else accumulate onto acc.  The
 // fragments of chunk c + 1 are read from LDS while the MFMAs of chunk c run.
-template <int TS, int PREC, bool TRANS_L, bool ZERO>
+template <int TS, int PREC, bool TRANS_L, bool ZERO, int NB = Geo<TS, PREC>::NI, bool RALIAS = false>
 __device__ __forceinline__ void wave_gemm(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &Lm, int l0,
                                           const Mat<PREC> &Rm, int r0, int lane) {
   using G = Geo<TS, PREC>;
+  static_assert(NB >= 1 && NB <= G::NI, "row blocks");
   constexpr int KC = PREC == PREC_F32 ? 8 : 16;
   constexpr int NC = TS / KC;
   // LDS read and MFMA instructions per chunk
   constexpr int PLANES = PREC == PREC_BF16X3 ? 2 : 1;
   constexpr int LREADS = PREC == PREC_F32 ? (TRANS_L ? 4 : 1) : (TRANS_L ? 2 : 1);
-  constexpr int NR = PLANES * (G::NI * LREADS + G::NJ);
-  constexpr int NM = (PREC == PREC_F32 ? 4 : PREC == PREC_BF16X3 ? 3 : 1) * G::NI * G::NJ;
+  constexpr int NR = PLANES * (NB * LREADS + (RALIAS ? 0 : G::NJ));
+  constexpr int NM = (PREC == PREC_F32 ? 4 : PREC == PREC_BF16X3 ? 3 : 1) * NB * G::NJ;
   Frags<TS, PREC> f[2];
-  load_frags<TS, PREC, TRANS_L>(f[0], Lm, l0, Rm, r0, lane, 0);
+  load_frags<TS, PREC, TRANS_L, NB, RALIAS>(f[0], Lm, l0, Rm, r0, lane, 0);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    if (c + 1 < NC) load_frags<TS, PREC, TRANS_L>(f[(c + 1) & 1], Lm, l0, Rm, r0, lane, (c + 1) * KC);
-    mma_frags<TS, PREC>(acc, f[c & 1], ZERO && c == 0);
+    if (c + 1 < NC) load_frags<TS, PREC, TRANS_L, NB, RALIAS>(f[(c + 1) & 1], Lm, l0, Rm, r0, lane, (c + 1) * KC);
+    mma_frags<TS, PREC, NB>(acc, f[c & 1], ZERO && c == 0);
   }
   if constexpr (SCHED_GEMM) {
     __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
     sched_chunks<NC, NM, NR>();
+  }
+}
+
+// ------------------------------------------------------------------ symmetric products
+// A = X X^T and A^2 are symmetric: of the (TS/32)^2 32x32 blocks only those on and
+// above the diagonal are computed, each off-diagonal block written to both of its
+// positions.  A job is the part one wave computes: NB row blocks from row p0 against
+// the column block q0 (nb = 0: the wave computes none).  For 128-tiles the ten blocks
+// fall on the four SIMDs (waves w and w + 4 share one) as 3 + 3 + 2 + 2 instead of
+// 4 + 4 + 4 + 4.
+struct SymJob {
+  int p0, q0, nb;
+  bool alias;  // q0 == p0: the column block is the first row block
+};
+
+template <int TS>
+__device__ __forceinline__ SymJob sym_job(int wv) {
+  if constexpr (TS == 128) {
+    // w0: (0,0) (1,0)   w1: (0,2) (1,2)   w2: (0,3) (1,3)   w3: (2,2) (3,2)
+    // w4: (1,1)         w5: (3,3)         w6, w7: none
+    switch (wv) {
+      case 0: return {0, 0, 2, true};
+      case 1: return {0, 64, 2, false};
+      case 2: return {0, 96, 2, false};
+      case 3: return {64, 64, 2, true};
+      case 4: return {32, 32, 1, true};
+      case 5: return {96, 96, 1, true};
+      default: return {0, 0, 0, false};
+    }
+  } else if constexpr (TS == 64) {
+    // w0: (0,0) (1,0)   w1: (1,1)
+    return wv == 0 ? SymJob{0, 0, 2, true} : SymJob{32, 32, 1, true};
+  } else {
+    return {0, 0, 1, true};
+  }
+}
+
+// Runs f(NB, RALIAS) (as integral constants) for the wave's job; idle waves skip it.
+template <int TS, class F>
+__device__ __forceinline__ void with_job(const SymJob &jb, F &&f) {
+  if constexpr (TS == 128) {
+    if (jb.nb == 2) {
+      if (jb.alias) {
+        f(std::integral_constant<int, 2>{}, std::true_type{});
+      } else {
+        f(std::integral_constant<int, 2>{}, std::false_type{});
+      }
+    } else if (jb.nb == 1) {
+      f(std::integral_constant<int, 1>{}, std::true_type{});
+    }
+  } else if constexpr (TS == 64) {
+    if (jb.nb == 2) {
+      f(std::integral_constant<int, 2>{}, std::true_type{});
+    } else {
+      f(std::integral_constant<int, 1>{}, std::true_type{});
+    }
+  } else {
+    f(std::integral_constant<int, 1>{}, std::true_type{});
   }
 }
 
@@ -311,18 +389,20 @@ __device__ __forceinline__ void wave_gemm(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::
 // from position [col][row..row+3] of a row-major LDS matrix, i.e. they store the
 // transpose of the accumulator block.
 
-// Store the transpose of the accumulators into a matrix in the precision's format.
-// SCALE: the stored value is s_store * acc; BACK: afterwards acc <- s_back * acc (one pass
-// over the accumulators serves both).
-template <int TS, int PREC, bool SCALE = false, bool BACK = false>
+// Store the transpose of the accumulators' first NB row blocks into a matrix in the
+// precision's format.  SCALE: the stored value is s_store * acc; BACK: afterwards acc <-
+// s_back * acc (one pass over the accumulators serves both).  MIRROR (symmetric
+// results): blocks off the diagonal are also stored untransposed, at [row][col].
+template <int TS, int PREC, bool SCALE = false, bool BACK = false, int NB = Geo<TS, PREC>::NI, bool MIRROR = false>
 __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &m, int p0, int q0,
                                             int lane, float s_store = 1.f, float s_back = 1.f) {
   using G = Geo<TS, PREC>;
   const int li = lane & 31, half = lane >> 5;
 #pragma unroll
-  for (int bi = 0; bi < G::NI; ++bi)
+  for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < G::NJ; ++bj)
+    for (int bj = 0; bj < G::NJ; ++bj) {
+      const bool mirror = MIRROR && p0 + bi * 32 != q0 + bj * 32;   // wave-uniform
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int row = p0 + bi * 32 + 8 * g + 4 * half;
@@ -336,31 +416,62 @@ __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>
         }
         if constexpr (PREC == PREC_F32) {
           *reinterpret_cast<f32x4 *>(m.f + col * G::PF + row) = v;
+          if (mirror) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m.f[(row + e) * G::PF + col] = v[e];
+          }
         } else {
           // col = (multiple of 32) + lane % 32
           const int o = col * G::PB + G::bcol(li & 15, row);
           const u32x2 hi = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *reinterpret_cast<u32x2 *>(m.hi + o) = hi;
+          u32x2 lo;
           if constexpr (PREC == PREC_BF16X3) {
             // the residuals v - hi are exact in fp32; hi is read back from the packed
             // pair (low half: shift up, high half: mask), not converted again
-            const u32x2 lo = {pack_bf16x2(v[0] - __builtin_bit_cast(float, hi[0] << 16),
-                                          v[1] - __builtin_bit_cast(float, hi[0] & 0xffff0000u)),
-                              pack_bf16x2(v[2] - __builtin_bit_cast(float, hi[1] << 16),
-                                          v[3] - __builtin_bit_cast(float, hi[1] & 0xffff0000u))};
+            lo = u32x2{pack_bf16x2(v[0] - __builtin_bit_cast(float, hi[0] << 16),
+                                   v[1] - __builtin_bit_cast(float, hi[0] & 0xffff0000u)),
+                       pack_bf16x2(v[2] - __builtin_bit_cast(float, hi[1] << 16),
+                                   v[3] - __builtin_bit_cast(float, hi[1] & 0xffff0000u))};
             *reinterpret_cast<u32x2 *>(m.lo + o) = lo;
+          }
+          if (mirror) {
+            // element e of the four goes to row + e: 16-bit halves of the packed pairs.
+            // With the chunk permutation, (row + e) % 16 = 8 (g % 2) + 4 half + e, so the
+            // stored column is (q0 ^ 32 e) + (lane % 32 ^ (16 (g % 2) + 8 half)): a
+            // wave-uniform part plus one of two per-lane offsets.
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              int od;
+              if constexpr (G::SWZ) {
+                static_assert(G::NJ == 1, "one column block");
+                int lo16 = 4 * half * G::PB + (li ^ (16 * (g & 1) + 8 * half));
+                asm("" : "+v"(lo16));   // formed here, not kept live across the loop
+                od = (p0 + bi * 32 + 8 * g + e) * G::PB + (q0 ^ (32 * e)) + lo16;
+              } else {
+                od = (row + e) * G::PB + col;
+              }
+              const unsigned hw = hi[e >> 1];
+              reinterpret_cast<unsigned short *>(m.hi)[od] = (unsigned short)((e & 1) ? hw >> 16 : hw);
+              if constexpr (PREC == PREC_BF16X3) {
+                const unsigned lw = lo[e >> 1];
+                reinterpret_cast<unsigned short *>(m.lo)[od] = (unsigned short)((e & 1) ? lw >> 16 : lw);
+              }
+            }
           }
         }
       }
+    }
 }
 
-// m[i][i] += d for the diagonal elements inside the wave's block (rows p0.., columns
-// q0..).  Each of them was written by this same wave (the block is stored transposed,
-// and (i, i) is its own transpose), and LDS accesses of one wave complete in order.
-template <int TS, int PREC>
+// m[i][i] += d for the diagonal elements inside the first NB row blocks of the block
+// at (p0, q0).  Each of them was written by this same wave (the block is stored
+// transposed, and (i, i) is its own transpose), and LDS accesses of one wave complete
+// in order.
+template <int TS, int PREC, int NB = Geo<TS, PREC>::NI>
 __device__ __forceinline__ void add_diag(const Mat<PREC> &m, int p0, int q0, int lane, float d) {
   using G = Geo<TS, PREC>;
-  if (q0 < p0 || q0 >= p0 + G::WBM || lane >= G::WBN) return;
+  if (q0 < p0 || q0 >= p0 + NB * 32 || lane >= G::WBN) return;
   const int i = q0 + lane;
   if constexpr (PREC == PREC_F32) {
     m.f[i * G::PF + i] += d;
@@ -763,46 +874,64 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     // LDS copy of X (fp32, or hi + lo bf16) carries X between steps.  Plain bf16 keeps
     // X in fp32 registers and forms a X there, since its LDS copy is bf16-rounded.
     constexpr bool FOLD_A = PREC != PREC_BF16;
-    // LASTC: the final step issues the loads of W for the update (dense tiles: the
-    // other variants lack the registers), so that their HBM latency passes while its
-    // last product runs
+    // Dense tiles issue the loads of W before the last update product, so that their
+    // HBM latency passes while it runs (the other variants lack the registers).
     constexpr bool EARLY_W = DENSE;
-    auto ns_step = [&](auto LASTC) {
-      constexpr bool LAST = decltype(LASTC)::value;
+    const SymJob jb = sym_job<TS>(wv);
+    // The symmetric part of a step, on the wave's job: B (with a on its diagonal when
+    // folded) ends up in AB.
+    auto sym_part = [&]() {
       Acc<NI, NJ> acc;
-      wave_gemm<TS, PREC, false, true>(acc, X, p0, X, q0, lane);     // A = X X^T
+      with_job<TS>(jb, [&](auto NBC, auto ALC) {
+        constexpr int NB = decltype(NBC)::value;
+        constexpr bool AL = decltype(ALC)::value;
+        wave_gemm<TS, PREC, false, true, NB, AL>(acc, X, jb.p0, X, jb.q0, lane);   // A = X X^T
+        if (cc != 0.f) {
+          // B = b A + c A^2 = c ((b/c) A + A A^T): accumulate A A^T onto (b/c) A
+          store_acc_t<TS, PREC, false, true, NB, true>(acc, AB, jb.p0, jb.q0, lane, 1.f, cb / cc);
+        } else {
+          store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cb);   // B = b A
+          if constexpr (FOLD_A) add_diag<TS, PREC, NB>(AB, jb.p0, jb.q0, lane, ca);       // B + a I
+        }
+      });
       if (cc != 0.f) {
-        // B = b A + c A^2 = c ((b/c) A + A A^T): accumulate A A^T onto (b/c) A
-        store_acc_t<TS, PREC, false, true>(acc, AB, p0, q0, lane, 1.f, cb / cc);  // A (symmetric)
         tile_sync<G::WPT>();
-        wave_gemm<TS, PREC, false, false>(acc, AB, p0, AB, q0, lane);
+        with_job<TS>(jb, [&](auto NBC, auto ALC) {
+          constexpr int NB = decltype(NBC)::value;
+          constexpr bool AL = decltype(ALC)::value;
+          wave_gemm<TS, PREC, false, false, NB, AL>(acc, AB, jb.p0, AB, jb.q0, lane);
+        });
         tile_sync<G::WPT>();                                             // A fully read
-        store_acc_t<TS, PREC, true>(acc, AB, p0, q0, lane, cc);        // B (symmetric)
-      } else {
-        store_acc_t<TS, PREC, true>(acc, AB, p0, q0, lane, cb);        // B = b A
-      }
-      if constexpr (FOLD_A) {
-        add_diag<TS, PREC>(AB, p0, q0, lane, ca);                      // B + a I
-      } else {
-#pragma unroll
-        for (int bi = 0; bi < NI; ++bi)
-#pragma unroll
-          for (int bj = 0; bj < NJ; ++bj)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) xr.b[bi][bj][e] *= ca;
-      }
-      tile_sync<G::WPT>();
-      if constexpr (LAST && EARLY_W) io.template load_w<DENSE>(t, L, gt);
-      wave_gemm<TS, PREC, true, FOLD_A>(xr, X, p0, AB, q0, lane);     // X^T <- X^T (aI + B)
-      tile_sync<G::WPT>();
-      if constexpr (!LAST) {
-        store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
-        tile_sync<G::WPT>();
+        with_job<TS>(jb, [&](auto NBC, auto) {
+          constexpr int NB = decltype(NBC)::value;
+          store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cc);   // B
+          if constexpr (FOLD_A) add_diag<TS, PREC, NB>(AB, jb.p0, jb.q0, lane, ca);       // B + a I
+        });
       }
     };
     if (prm.steps > 0) {
-      for (int it = 0; it + 1 < prm.steps; ++it) ns_step(std::false_type{});
-      ns_step(std::true_type{});
+      for (int it = 0;; ++it) {
+        sym_part();
+        if constexpr (!FOLD_A) {
+#pragma unroll
+          for (int bi = 0; bi < NI; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < NJ; ++bj)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) xr.b[bi][bj][e] *= ca;
+        }
+        tile_sync<G::WPT>();
+        if (it + 1 == prm.steps) {
+          if constexpr (EARLY_W) io.template load_w<DENSE>(t, L, gt);
+          wave_gemm<TS, PREC, true, FOLD_A>(xr, X, p0, AB, q0, lane);   // X^T <- X^T (aI + B)
+          tile_sync<G::WPT>();
+          break;
+        }
+        wave_gemm<TS, PREC, true, FOLD_A>(xr, X, p0, AB, q0, lane);     // X^T <- X^T (aI + B)
+        tile_sync<G::WPT>();
+        store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
+        tile_sync<G::WPT>();
+      }
     }
     if (!EARLY_W || prm.steps == 0) io.template load_w<DENSE>(t, L, gt);
 
