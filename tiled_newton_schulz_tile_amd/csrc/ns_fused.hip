@@ -402,7 +402,6 @@ __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>
   for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
     for (int bj = 0; bj < G::NJ; ++bj) {
-      const bool mirror = MIRROR && p0 + bi * 32 != q0 + bj * 32;   // wave-uniform
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int row = p0 + bi * 32 + 8 * g + 4 * half;
@@ -416,7 +415,7 @@ __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>
         }
         if constexpr (PREC == PREC_F32) {
           *reinterpret_cast<f32x4 *>(m.f + col * G::PF + row) = v;
-          if (mirror) {
+          if (MIRROR && p0 + bi * 32 != q0 + bj * 32) {   // off the diagonal (wave-uniform)
 #pragma unroll
             for (int e = 0; e < 4; ++e) m.f[(row + e) * G::PF + col] = v[e];
           }
@@ -425,43 +424,45 @@ __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>
           const int o = col * G::PB + G::bcol(li & 15, row);
           const u32x2 hi = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *reinterpret_cast<u32x2 *>(m.hi + o) = hi;
-          u32x2 lo;
           if constexpr (PREC == PREC_BF16X3) {
             // the residuals v - hi are exact in fp32; hi is read back from the packed
             // pair (low half: shift up, high half: mask), not converted again
-            lo = u32x2{pack_bf16x2(v[0] - __builtin_bit_cast(float, hi[0] << 16),
+            const u32x2 lo = u32x2{pack_bf16x2(v[0] - __builtin_bit_cast(float, hi[0] << 16),
                                    v[1] - __builtin_bit_cast(float, hi[0] & 0xffff0000u)),
                        pack_bf16x2(v[2] - __builtin_bit_cast(float, hi[1] << 16),
                                    v[3] - __builtin_bit_cast(float, hi[1] & 0xffff0000u))};
             *reinterpret_cast<u32x2 *>(m.lo + o) = lo;
           }
-          if (mirror) {
-            // element e of the four goes to row + e: 16-bit halves of the packed pairs.
-            // With the chunk permutation, (row + e) % 16 = 8 (g % 2) + 4 half + e, so the
-            // stored column is (q0 ^ 32 e) + (lane % 32 ^ (16 (g % 2) + 8 half)): a
-            // wave-uniform part plus one of two per-lane offsets.
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              int od;
-              if constexpr (G::SWZ) {
-                static_assert(G::NJ == 1, "one column block");
-                int lo16 = 4 * half * G::PB + (li ^ (16 * (g & 1) + 8 * half));
-                asm("" : "+v"(lo16));   // formed here, not kept live across the loop
-                od = (p0 + bi * 32 + 8 * g + e) * G::PB + (q0 ^ (32 * e)) + lo16;
-              } else {
-                od = (row + e) * G::PB + col;
-              }
-              const unsigned hw = hi[e >> 1];
-              reinterpret_cast<unsigned short *>(m.hi)[od] = (unsigned short)((e & 1) ? hw >> 16 : hw);
-              if constexpr (PREC == PREC_BF16X3) {
-                const unsigned lw = lo[e >> 1];
-                reinterpret_cast<unsigned short *>(m.lo)[od] = (unsigned short)((e & 1) ? lw >> 16 : lw);
-              }
-            }
-          }
         }
       }
     }
+  if constexpr (MIRROR && PREC != PREC_F32) {
+    // Off-diagonal blocks: read the block just stored (this wave's own LDS writes,
+    // processed in order) back with transposing reads, which hand each lane eight
+    // consecutive columns of one row of the untransposed block, and store those as one
+    // 16-byte chunk at [row][col].
+    // (the lane index is made opaque here so that the lane-dependent addresses are
+    // formed at this point instead of being kept live across the whole iteration)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lr = ln & 31, lh = ln >> 5;
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi) {
+      if (p0 + bi * 32 == q0) continue;   // wave-uniform
+      const int r = p0 + bi * 32 + lr;
+#pragma unroll
+      for (int ks = 0; ks < 32; ks += 16) {
+        const int k = q0 + ks + 8 * lh;
+        const int od = G::bidx(r, k);
+        const bf16x8 vh = tr_frag_g<G>(m.hi, k, p0 + bi * 32, ln);
+        if constexpr (PREC == PREC_BF16X3) {
+          const bf16x8 vl = tr_frag_g<G>(m.lo, k, p0 + bi * 32, ln);
+          *reinterpret_cast<bf16x8 *>(m.lo + od) = vl;
+        }
+        *reinterpret_cast<bf16x8 *>(m.hi + od) = vh;
+      }
+    }
+  }
 }
 
 // m[i][i] += d for the diagonal elements inside the first NB row blocks of the block
