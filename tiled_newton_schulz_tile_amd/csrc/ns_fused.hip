@@ -682,6 +682,39 @@ struct TileRegs {
     }
   }
 
+  // Dense tiles: M <- beta M + G, stored, with the new values (as stored) left in v and
+  // the sum of their squares (this thread's share, fixed order) returned.
+  __device__ __forceinline__ float momentum_dense(TileView t, const LayerView &L, int gt, float beta,
+                                                  float (&v)[GM_IT][8]) const {
+    S *mb = reinterpret_cast<S *>(L.m);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < GM_IT; ++i) {
+      const int q = gt + i * NT;
+      const int r = q / CPR, c = (q % CPR) * 8;
+      S *dst = mb + (int64_t)(t.row0 + r) * L.ld_m + t.col0 + c;
+      if constexpr (sizeof(S) == 2) {
+        unsigned code[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          code[e / 2] = pack_bf16x2(__builtin_fmaf(beta, m[i].get(e), g[i].get(e)),
+                                    __builtin_fmaf(beta, m[i].get(e + 1), g[i].get(e + 1)));
+          v[i][e] = __builtin_bit_cast(float, code[e / 2] << 16);
+          v[i][e + 1] = __builtin_bit_cast(float, code[e / 2] & 0xffff0000u);
+        }
+        *gmem(reinterpret_cast<u32x4 *>(dst)) = u32x4{code[0], code[1], code[2], code[3]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] = __builtin_fmaf(beta, m[i].get(e), g[i].get(e));
+        gmem(reinterpret_cast<f32x4 *>(dst))[0] = f32x4{v[i][0], v[i][1], v[i][2], v[i][3]};
+        gmem(reinterpret_cast<f32x4 *>(dst))[1] = f32x4{v[i][4], v[i][5], v[i][6], v[i][7]};
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(v[i][e], v[i][e], ss);
+    }
+    return ss;
+  }
+
   // M <- beta M + G: store the new momentum and stage its values, oriented on the
   // short side and zero padded, as fp32 TS x TS (pitch PF) in LDS.
   template <int PF, bool DENSE>
@@ -823,8 +856,20 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
   io.template load_gm<DENSE>(t, L, gt);
 
   while (true) {
-    // ---- momentum and staging of the oriented, zero-padded tile -------------
-    io.template momentum<PF, DENSE>(t, L, gt, prm.beta, st);
+    // ---- momentum, Frobenius norm, X0 -------------------------------------------
+    // DIRECT (dense tiles, a folded into B): each thread keeps its new momentum values in
+    // registers, the norm comes from their squares, and X0 = M / (|M| + eps) is written
+    // to the LDS copy of X straight from them.  Otherwise the tile is staged in fp32,
+    // oriented on its short side and zero padded, and X0 formed from the staging copy.
+    // (The summation order is fixed either way.)
+    constexpr bool DIRECT = DENSE && PREC != PREC_BF16;
+    float vd[DIRECT ? TileRegs<TS, NT, S>::GM_IT : 1][8];
+    float ss = 0.f;
+    if constexpr (DIRECT) {
+      ss = io.momentum_dense(t, L, gt, prm.beta, vd);
+    } else {
+      io.template momentum<PF, DENSE>(t, L, gt, prm.beta, st);
+    }
     const int64_t nxt = tix + stride;
     TileView tn = t;
     LayerView Ln = L;
@@ -835,12 +880,8 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
         io.template load_gm<DENSE>(tn, Ln, gt);
       }
     }
-    tile_sync<G::WPT>();
-
-    // ---- Frobenius norm of the oriented tile, fixed summation order ---------
-    float inv;
-    {
-      float ss = 0.f;
+    if constexpr (!DIRECT) {
+      tile_sync<G::WPT>();
       constexpr int C4 = TS * TS / 4;
 #pragma unroll 4
       for (int q = gt; q < C4; q += NT) {
@@ -851,6 +892,9 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
         ss = __builtin_fmaf(v[2], v[2], ss);
         ss = __builtin_fmaf(v[3], v[3], ss);
       }
+    }
+    float inv;
+    {
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
       if constexpr (G::WPT > 1) {
@@ -865,10 +909,46 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
 
     // X in registers (fp32, MFMA output layout of the update product: block holds X^T)
     Acc<NI, NJ> xr;
-    load_acc_t<TS, PREC>(xr, st, p0, q0, lane, inv);
-    tile_sync<G::WPT>();
-    store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
-    tile_sync<G::WPT>();
+    if constexpr (DIRECT) {
+      constexpr int CPR = TS / 8;
+#pragma unroll
+      for (int i = 0; i < TileRegs<TS, NT, S>::GM_IT; ++i) {
+        const int q = gt + i * NT;
+        const int r = q / CPR, c = (q % CPR) * 8;
+        if (prm.steps == 0) {
+          // no iteration: the output is X0 itself, staged for the update in fp32
+#pragma unroll
+          for (int e = 0; e < 8; ++e) st[r * PF + c + e] = vd[i][e] * inv;
+        } else if constexpr (PREC == PREC_F32) {
+          f32x4 a, b;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = vd[i][e] * inv;
+            b[e] = vd[i][e + 4] * inv;
+          }
+          *reinterpret_cast<f32x4 *>(X.f + r * PF + c) = a;
+          *reinterpret_cast<f32x4 *>(X.f + r * PF + c + 4) = b;
+        } else {
+          u32x4 hi, lo;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float x0 = vd[i][e] * inv, x1 = vd[i][e + 1] * inv;
+            hi[e / 2] = pack_bf16x2(x0, x1);
+            lo[e / 2] = pack_bf16x2(__builtin_fmaf(vd[i][e], inv, -__builtin_bit_cast(float, hi[e / 2] << 16)),
+                                    __builtin_fmaf(vd[i][e + 1], inv, -__builtin_bit_cast(float, hi[e / 2] & 0xffff0000u)));
+          }
+          const int o = G::bidx(r, c);
+          *reinterpret_cast<u32x4 *>(X.hi + o) = hi;
+          *reinterpret_cast<u32x4 *>(X.lo + o) = lo;
+        }
+      }
+      tile_sync<G::WPT>();
+    } else {
+      load_acc_t<TS, PREC>(xr, st, p0, q0, lane, inv);
+      tile_sync<G::WPT>();
+      store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
+      tile_sync<G::WPT>();
+    }
 
     // ---- K Newton-Schulz steps ------------------------------------------------
     // FOLD_A (fp32 and bf16x3): X <- (a I + B) X with a folded into B's diagonal; the
@@ -937,8 +1017,10 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     if (!EARLY_W || prm.steps == 0) io.template load_w<DENSE>(t, L, gt);
 
     // ---- reassembly and weight update ------------------------------------------
-    tile_sync<G::WPT>();
-    store_acc_t_f32<TS, PREC>(xr, st, p0, q0, lane);
+    if (!DIRECT || prm.steps > 0) {
+      tile_sync<G::WPT>();
+      store_acc_t_f32<TS, PREC>(xr, st, p0, q0, lane);
+    }
     tile_sync<G::WPT>();
     io.template update<PF, DENSE>(t, L, gt, prm.lr, prm.write_update != 0, st);
     if (nxt >= ntiles) break;
