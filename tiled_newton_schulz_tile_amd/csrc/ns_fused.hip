@@ -329,9 +329,9 @@ __device__ __forceinline__ void wave_gemm(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::
 // A = X X^T and A^2 are symmetric: of the (TS/32)^2 32x32 blocks only those on and
 // above the diagonal are computed, each off-diagonal block written to both of its
 // positions.  A job is the part one wave computes: NB row blocks from row p0 against
-// the column block q0 (nb = 0: the wave computes none).  For 128-tiles the ten blocks
-// fall on the four SIMDs (waves w and w + 4 share one) as 3 + 3 + 2 + 2 instead of
-// 4 + 4 + 4 + 4.
+// the column block q0.  For 128-tiles the ten blocks fall on the four SIMDs (waves w and
+// w + 4 share one) as 3 + 3 + 2 + 2 instead of 4 + 4 + 4 + 4, and each of the two busier
+// SIMDs holds one off-diagonal block (the one that needs the second, untransposed copy).
 struct SymJob {
   int p0, q0, nb;
   bool alias;  // q0 == p0: the column block is the first row block
@@ -340,16 +340,17 @@ struct SymJob {
 template <int TS>
 __device__ __forceinline__ SymJob sym_job(int wv) {
   if constexpr (TS == 128) {
-    // w0: (0,0) (1,0)   w1: (0,2) (1,2)   w2: (0,3) (1,3)   w3: (2,2) (3,2)
-    // w4: (1,1)         w5: (3,3)         w6, w7: none
+    // w0: (0,0) (1,0)   w1: (2,2) (3,2)   w2: (0,2)   w3: (0,3)
+    // w4: (1,1)         w5: (3,3)         w6: (1,2)   w7: (1,3)
     switch (wv) {
       case 0: return {0, 0, 2, true};
-      case 1: return {0, 64, 2, false};
-      case 2: return {0, 96, 2, false};
-      case 3: return {64, 64, 2, true};
+      case 1: return {64, 64, 2, true};
+      case 2: return {0, 64, 1, false};
+      case 3: return {0, 96, 1, false};
       case 4: return {32, 32, 1, true};
       case 5: return {96, 96, 1, true};
-      default: return {0, 0, 0, false};
+      case 6: return {32, 64, 1, false};
+      default: return {32, 96, 1, false};
     }
   } else if constexpr (TS == 64) {
     // w0: (0,0) (1,0)   w1: (1,1)
@@ -359,18 +360,16 @@ __device__ __forceinline__ SymJob sym_job(int wv) {
   }
 }
 
-// Runs f(NB, RALIAS) (as integral constants) for the wave's job; idle waves skip it.
+// Runs f(NB, RALIAS) (as integral constants) for the wave's job.
 template <int TS, class F>
 __device__ __forceinline__ void with_job(const SymJob &jb, F &&f) {
   if constexpr (TS == 128) {
     if (jb.nb == 2) {
-      if (jb.alias) {
-        f(std::integral_constant<int, 2>{}, std::true_type{});
-      } else {
-        f(std::integral_constant<int, 2>{}, std::false_type{});
-      }
-    } else if (jb.nb == 1) {
+      f(std::integral_constant<int, 2>{}, std::true_type{});
+    } else if (jb.alias) {
       f(std::integral_constant<int, 1>{}, std::true_type{});
+    } else {
+      f(std::integral_constant<int, 1>{}, std::false_type{});
     }
   } else if constexpr (TS == 64) {
     if (jb.nb == 2) {
