@@ -32,7 +32,7 @@ METRIC = "HiMuon step ms & NS TFLOP/s (% MFMA peak) vs T, 8B-shaped stack"
 # rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), scaled by the
 # readings of a 1 GiB elementwise copy (x2.0 read, x1.0 write).  Valid only for the
 # kernel source it was measured on (sha256 prefix of ns_fused.hip).
-TRAFFIC_T128 = {"source_sha256_16": "21f62614b97de32e", "fetch_kib": 27291104.0625,
+TRAFFIC_T128 = {"source_sha256_16": "6f2c270c3c2a7de5", "fetch_kib": 27291182.1875,
                 "write_kib": 40894464.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -100,10 +100,10 @@ def time_steps(opt, steps, warmup, lr=0.02):
     return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
 
 
-def cpu_baseline(K, coeffs, tile):
-    """The fp64 oracle on the host, on a bounded sample of the workload: one
-    4096 x 14336 matrix of the stack (3,584 tiles at T = 128), momentum + tiled NS +
-    update.  Throughput in algorithmic NS TFLOP/s."""
+def cpu_baseline(K, coeffs, tile, shapes):
+    """The fp64 oracle on the host, on a bounded sample of the workload: the seven
+    matrices of one decoder layer of the stack (momentum + tiled NS + update; about
+    10-15 s of CPU work).  Throughput in algorithmic NS TFLOP/s."""
     import numpy as np
     import oracle
     try:
@@ -111,19 +111,21 @@ def cpu_baseline(K, coeffs, tile):
         cores = max((i.get("num_threads") or 0) for i in threadpool_info()) or os.cpu_count()
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
+    layer = list(shapes[:7])
     rng = np.random.default_rng(0)
-    H, W = 4096, 14336
-    G = rng.standard_normal((H, W), dtype=np.float32) * 0.01
-    M = np.zeros((H, W), dtype=np.float32)
-    Wt = np.zeros((H, W), dtype=np.float32)
+    mats = []
+    for H, W in layer:
+        G = rng.standard_normal((H, W), dtype=np.float32) * 0.01
+        mats.append((np.zeros((H, W), dtype=np.float32), np.zeros((H, W), dtype=np.float32), G))
     t0 = time.time()
-    oracle.step([(Wt, M, G)], tile, K, coeffs)
+    oracle.step(mats, tile, K, coeffs)
     dt = time.time() - t0
-    fl = oracle.ns_flops([(H, W)], tile, K, coeffs)
+    fl = oracle.ns_flops(layer, tile, K, coeffs)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"one 4096x14336 matrix of the stack (T={tile}, K={K}, quintic, fp64 numpy), "
-                      f"{dt:.1f} s for {fl:.3e} NS flops; whole-step time at this rate "
-                      f"scales by the flop ratio",
+            "sample": f"one decoder layer of the stack ({len(layer)} matrices, "
+                      f"{sum(h * w for h, w in layer)} params; T={tile}, K={K}, quintic, fp64 numpy), "
+                      f"{dt:.1f} s for {fl:.3e} NS flops; whole-step time at this rate scales "
+                      f"by the flop ratio",
             "seconds": dt}
 
 
@@ -192,7 +194,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         log("[bench] timing the oracle on the host (bounded sample)")
-        cpu = cpu_baseline(K, coeffs, args.tile)
+        cpu = cpu_baseline(K, coeffs, args.tile, shapes)
         log(f"[bench] oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads "
             f"({cpu['seconds']:.1f}s)")
         cpu.pop("seconds", None)

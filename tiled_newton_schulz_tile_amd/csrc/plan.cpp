@@ -184,7 +184,12 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
           const bool dense = h == e && w == e && d.vec_ok && d.vec_w && c0 % 8 == 0;
           by_edge[e == 32 ? 0 : (e == 64 ? 1 : 2)][dense ? 1 : 0].push_back(
               FusedTile{(int32_t)li, (int32_t)r0, (int32_t)c0, (int16_t)h, (int16_t)w});
-          issued += (double)K * split * 2.0 * e * e * e * (quintic ? 3.0 : 2.0);
+          {
+            // the symmetric products (X X^T, A^2) run on the (nb + 1) / (2 nb) share of
+            // 32x32 blocks on and above the diagonal; the update on all blocks
+            const double nb = e / 32.0, f = (nb + 1.0) / (2.0 * nb);
+            issued += (double)K * split * 2.0 * e * e * e * (1.0 + f * (quintic ? 2.0 : 1.0));
+          }
         } else {
           const GemmSizes z = gemm_sizes(h, w);
           GemmTile g{};
