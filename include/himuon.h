@@ -69,6 +69,13 @@ typedef enum {
 
 #define HIMUON_TILE_FULL 0            /* one tile per matrix: full-matrix Muon        */
 #define HIMUON_FLAG_WRITE_UPDATE 1u   /* also store O (fp32) to layer.update          */
+/* Test mode: the step runs the momentum update, the gather of every tile (oriented on its
+   short side) and the scatter back, with no normalisation and no Newton-Schulz step, so
+   O = M as stored.  O, W <- W - lr O and, with HIMUON_FLAG_WRITE_UPDATE, U = O are
+   bit-exact copies of the stored momentum whenever the path holds X in fp32
+   (HIMUON_PREC_F32) or the state is bf16; it checks tile indexing and reassembly.  The
+   plan's steps and coefficients are ignored while it is set.                          */
+#define HIMUON_FLAG_IDENTITY_MAP 2u
 
 typedef struct { double a, b, c; } himuon_coeffs;
 

@@ -81,6 +81,12 @@ def test_stats_match_oracle_counts(name, T, coeffs):
         hm.himuon_plan_destroy(p)
 
 
+def test_identity_flag_accepted_with_and_without_update():
+    for flags in (hm.FLAG_IDENTITY_MAP, hm.FLAG_IDENTITY_MAP | hm.FLAG_WRITE_UPDATE):
+        p = plan_for([(300, 170), (64, 64)], 128, flags=flags)
+        hm.himuon_plan_destroy(p)
+
+
 def test_llama_stack_tile_count_and_work():
     p = plan_for(synth.STACKS["llama3-8b-32L"], 128)
     st = hm.himuon_plan_stats(p)

@@ -27,7 +27,7 @@ def _need_gpu():
 
 
 def gpu_step(mats, T, K=5, coeffs=Q, prec=None, state=torch.bfloat16, beta=0.95, lr=0.02,
-             eps=1e-7, M0=None, W0=None, steps=1, grads=None):
+             eps=1e-7, M0=None, W0=None, steps=1, grads=None, identity=False):
     """Run `steps` HiMuon steps on the GPU.  mats: list of CPU G matrices (any float dtype).
     Returns per step a list of (W, M, U) CPU tensors and the pre-step M of each step."""
     _need_gpu()
@@ -38,7 +38,7 @@ def gpu_step(mats, T, K=5, coeffs=Q, prec=None, state=torch.bfloat16, beta=0.95,
           for i, g in enumerate(Gs)]
     Us = [torch.full(g.shape, float("nan"), dtype=torch.float32, device=DEV) for g in Gs]
     opt = hm.HiMuon([(Ws[i], Ms[i], Gs[i], Us[i]) for i in range(n)], T, K, coeffs, beta, eps,
-                    precision=prec)
+                    precision=prec, identity=identity)
     out, pre = [], []
     for s in range(steps):
         if s > 0 and grads is not None:
@@ -143,6 +143,27 @@ def test_reassembly_bit_exact(shape):
     U = res[0][2]
     O = oracle.tiled_ns(G.double().numpy(), 64, 0, Q, eps=0.0).astype(np.float32)
     assert np.array_equal(U.numpy(), O)
+
+
+IDENTITY_SHAPES = [(100, 113), (113, 100), (300, 170), (170, 300), (1, 257), (257, 1), (513, 129)]
+
+
+@pytest.mark.parametrize("T", [1, 7, 32, 64, 100, 128, 200, 256, 0])
+@pytest.mark.parametrize("state,prec", [(torch.float32, 0), (torch.bfloat16, 2), (torch.bfloat16, 1)])
+def test_identity_map_bit_exact(T, state, prec):
+    """HIMUON_FLAG_IDENTITY_MAP: gather (oriented on the short side) and scatter only, so
+    O is the stored momentum bit for bit at every tile size, on both the fused path
+    (T <= 128) and the large-tile path, and W moves by exactly -lr O (one rounding)."""
+    mats = [power_law(h, w, 300 + i) for i, (h, w) in enumerate(IDENTITY_SHAPES)]
+    M0 = [0.5 * power_law(h, w, 400 + i) for i, (h, w) in enumerate(IDENTITY_SHAPES)]
+    W0 = [torch.randn(h, w, generator=torch.Generator().manual_seed(500 + i)) for i, (h, w) in
+          enumerate(IDENTITY_SHAPES)]
+    (res,), _ = gpu_step(mats, T, prec=prec, state=state, M0=M0, W0=W0, identity=True)
+    lr = np.float32(0.02)
+    for (W, M, U), w0 in zip(res, W0):
+        assert torch.equal(U, M.float())
+        want = (w0.double() - float(lr) * U.double()).float()
+        assert (W.view(torch.int32) - want.view(torch.int32)).abs().max().item() <= 1
 
 
 @pytest.mark.parametrize("state,prec", [(torch.float32, 0), (torch.bfloat16, 2)])

@@ -18,7 +18,7 @@ __all__ = [
     "himuon_plan", "himuon_workspace_size", "himuon_step", "himuon_set_tile_schedule",
     "himuon_plan_stats", "himuon_plan_tiles", "himuon_plan_destroy", "himuon_last_error",
     "HiMuon", "CUBIC", "QUINTIC", "TILE_FULL", "F32", "BF16", "PREC_F32", "PREC_BF16",
-    "PREC_BF16X3", "FLAG_WRITE_UPDATE", "library_path", "EXPORTED",
+    "PREC_BF16X3", "FLAG_WRITE_UPDATE", "FLAG_IDENTITY_MAP", "library_path", "EXPORTED",
 ]
 
 CUBIC = (1.5, -0.5, 0.0)
@@ -27,6 +27,7 @@ TILE_FULL = 0
 F32, BF16 = 0, 1
 PREC_F32, PREC_BF16, PREC_BF16X3 = 0, 1, 2
 FLAG_WRITE_UPDATE = 1
+FLAG_IDENTITY_MAP = 2
 
 STATUS = {0: "HIMUON_OK", -1: "HIMUON_EINVAL", -2: "HIMUON_EBUDGET", -3: "HIMUON_ENOMEM",
           -4: "HIMUON_EDEVICE", -5: "HIMUON_EUNSUPPORTED"}
@@ -187,11 +188,13 @@ class HiMuon:
     layers: list of (W fp32, M, G) or (W, M, G, U) device tensors; M and G share
     one dtype (torch.float32 or torch.bfloat16).  U (fp32) receives the NS output O
     when given (HIMUON_FLAG_WRITE_UPDATE).  The workspace of the large-tile path is
-    a torch byte tensor on the layers' device.
+    a torch byte tensor on the layers' device.  identity=True sets
+    HIMUON_FLAG_IDENTITY_MAP (gather -> scatter only, O = M; a test mode).
     """
 
     def __init__(self, layers, tile: int, steps: int = 5, coeffs=QUINTIC, beta: float = 0.95,
-                 eps: float = 1e-7, workspace_budget: int = 4 * 10 ** 9, precision=None):
+                 eps: float = 1e-7, workspace_budget: int = 4 * 10 ** 9, precision=None,
+                 identity: bool = False):
         import torch
         self._torch = torch
         if not layers:
@@ -208,7 +211,8 @@ class HiMuon:
         self.layers = list(layers)
         self.cfg = make_config(tile, steps, coeffs, beta, eps, workspace_budget,
                                F32 if sd == torch.float32 else BF16, precision,
-                               FLAG_WRITE_UPDATE if write_u else 0)
+                               (FLAG_WRITE_UPDATE if write_u else 0) |
+                               (FLAG_IDENTITY_MAP if identity else 0))
         self._c_layers = [layer_from_tensors(*l[:3], l[3] if write_u else None) for l in layers]
         self.plan = himuon_plan(self._c_layers, self.cfg)
         self.device = layers[0][0].device

@@ -162,7 +162,8 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
   prm.beta = c.beta;
   prm.eps = c.eps;
   prm.lr = lr;
-  prm.steps = c.steps;
+  prm.identity = (c.flags & HIMUON_FLAG_IDENTITY_MAP) ? 1 : 0;
+  prm.steps = prm.identity ? 0 : c.steps;
   prm.write_update = (c.flags & HIMUON_FLAG_WRITE_UPDATE) ? 1 : 0;
   const auto *dl = reinterpret_cast<const himuon::LayerDesc *>(p->d_buf);
   const auto *dft = reinterpret_cast<const himuon::FusedTile *>(p->d_buf + p->off_ftiles);

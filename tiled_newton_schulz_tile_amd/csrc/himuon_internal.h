@@ -64,6 +64,7 @@ struct NSParams {
   float beta, eps, lr;
   int32_t steps;
   int32_t write_update;
+  int32_t identity;  // gather -> scatter only: no normalisation (steps is 0 then)
 };
 
 // ---- launchers (ns_fused.hip) --------------------------------------------------

@@ -903,7 +903,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
 #pragma unroll
         for (int i = 1; i < G::WPT; ++i) ss += red[grp][i];
       }
-      inv = 1.0f / (__builtin_sqrtf(ss) + prm.eps);
+      inv = prm.identity ? 1.0f : 1.0f / (__builtin_sqrtf(ss) + prm.eps);
     }
 
     // X in registers (fp32, MFMA output layout of the update product: block holds X^T)

@@ -200,16 +200,17 @@ __global__ __launch_bounds__(THREADS) void gemm_momentum_kernel(const LayerDesc 
 }
 
 // ------------------------------------------------------------------ norm
-// One workgroup per tile: the partial sums in a fixed order; stores 1 / (sqrt(ss) + eps).
+// One workgroup per tile: the partial sums in a fixed order; stores 1 / (sqrt(ss) + eps)
+// (1 in the identity test mode).
 __global__ __launch_bounds__(THREADS) void gemm_norm_kernel(const GemmTile *__restrict__ tiles, int first,
-                                                            char *ws, float eps) {
+                                                            char *ws, float eps, int identity) {
   __shared__ float red4[4];
   const TileG t = tile_of(tiles, first + (int)blockIdx.x);
   GLOBAL_AS float *p = gmem(reinterpret_cast<float *>(ws + t.red));
   float ss = 0.f;
   for (int q = threadIdx.x; q < t.nred; q += THREADS) ss += p[q];
   ss = block_sum(ss, red4);
-  if (threadIdx.x == 0) p[t.nred] = 1.0f / (__builtin_sqrtf(ss) + eps);
+  if (threadIdx.x == 0) p[t.nred] = identity ? 1.0f : 1.0f / (__builtin_sqrtf(ss) + eps);
 }
 
 // ------------------------------------------------------------------ stage / apply
@@ -650,7 +651,7 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
       c.n_app > 0x7fffffff)
     return hipErrorInvalidValue;
   if (c.n_mom) hipLaunchKernelGGL(gemm_momentum_kernel<S>, grid(c.n_mom), dim3(THREADS), 0, stream, layers, tiles, c.mom, ws, p.beta);
-  if (c.tile_n) hipLaunchKernelGGL(gemm_norm_kernel, grid(c.tile_n), dim3(THREADS), 0, stream, tiles, (int)c.tile_first, ws, p.eps);
+  if (c.tile_n) hipLaunchKernelGGL(gemm_norm_kernel, grid(c.tile_n), dim3(THREADS), 0, stream, tiles, (int)c.tile_first, ws, p.eps, p.identity);
   if (c.n_stg) hipLaunchKernelGGL((gemm_stage_kernel<S, PREC>), grid(c.n_stg), dim3(THREADS), 0, stream, layers, tiles, c.stg, ws);
   GemmParams gp{p.a, p.b, p.c, 0, PREC != PREC_BF16};
   for (int it = 0; it < p.steps; ++it) {

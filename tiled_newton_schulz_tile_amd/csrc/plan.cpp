@@ -95,7 +95,7 @@ himuon_status plan_init(Plan &p, const himuon_layer *layers, int32_t n, const hi
     err = "precision must be HIMUON_PREC_F32, HIMUON_PREC_BF16 or HIMUON_PREC_BF16X3";
     return HIMUON_EINVAL;
   }
-  if (c.flags & ~HIMUON_FLAG_WRITE_UPDATE) {
+  if (c.flags & ~(HIMUON_FLAG_WRITE_UPDATE | HIMUON_FLAG_IDENTITY_MAP)) {
     err = "unknown flag bits";
     return HIMUON_EINVAL;
   }
