@@ -66,6 +66,33 @@ struct Planes {
       return bf16_bits_to_f32(h) + bf16_bits_to_f32(l);
     }
   }
+  // fp32 values of 16 consecutive elements of row i from column j (j multiple of 16,
+  // j + 16 <= ld): two 16-byte loads per plane
+  __device__ __forceinline__ void get16(int i, int j, float (&v)[16]) const {
+    const int64_t o = (int64_t)i * ld + j;
+    if constexpr (PREC == PREC_F32) {
+      const GLOBAL_AS f32x4 *s = reinterpret_cast<const GLOBAL_AS f32x4 *>(gmem(f() + o));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 x = s[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+      }
+    } else {
+      const GLOBAL_AS u32x4 *sh = reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(hi() + o));
+      const GLOBAL_AS u32x4 *sl = reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(lo() + o));
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const u32x4 h = sh[q], l = sl[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[8 * q + 2 * e] = __builtin_bit_cast(float, h[e] << 16) + __builtin_bit_cast(float, l[e] << 16);
+          v[8 * q + 2 * e + 1] = __builtin_bit_cast(float, h[e] & 0xffff0000u) +
+                                 __builtin_bit_cast(float, l[e] & 0xffff0000u);
+        }
+      }
+    }
+  }
   // store 16 consecutive values of row i starting at column j (j multiple of 16,
   // j + 16 <= ld)
   __device__ __forceinline__ void put16(int i, int j, const float (&v)[16]) const {
@@ -304,9 +331,15 @@ __global__ __launch_bounds__(THREADS) void gemm_apply_kernel(const LayerDesc *__
   const Planes<PREC> X{ws + (xsel ? t.x1 : t.x0), t.r, t.ldx};
   {
     const int oi = or0 + lr, oj = oc0 + lc;
+    float v[16];
+    if (oi < t.r && oj < t.s) {
+      X.get16(oi, oj, v);   // oj + 16 <= ldx: ldx is a multiple of 32 and oj of 16
+    } else {
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      blk[lr * SBP + lc + q] = (oi < t.r && oj + q < t.s) ? X.get(oi, oj + q) : 0.f;
+      for (int q = 0; q < 16; ++q) v[q] = 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) blk[lr * SBP + lc + q] = oj + q < t.s ? v[q] : 0.f;
   }
   __syncthreads();
   const int gi = wk.bi * SB + lr, gj = wk.bj * SB + lc;
@@ -343,6 +376,16 @@ __global__ __launch_bounds__(THREADS) void gemm_apply_kernel(const LayerDesc *__
 }
 
 // ------------------------------------------------------------------ grouped GEMMs
+// Workgroups are dispatched to the eight XCDs round robin (block b on XCD b % 8).  The
+// work list holds the blocks of one tile next to each other, so each XCD takes one
+// contiguous run of it: the blocks that read the same tile's operands then share that
+// XCD's L2.
+__device__ __forceinline__ int xcd_work_index() {
+  const int nb = (int)gridDim.x, b = (int)blockIdx.x;
+  const int per = nb / 8, rem = nb % 8, x = b % 8;
+  return x * per + (x < rem ? x : rem) + b / 8;
+}
+
 // LDS tile of one operand for one K step, per plane: [rows][BK + pad] (row operand) or
 // [BK][BM + pad] (column operand of the update, read with ds_read_tr).
 template <int PREC>
@@ -550,7 +593,7 @@ __global__ __launch_bounds__(THREADS) void gemm_ns_kernel(const GemmTile *__rest
                                                           GemmParams gp) {
   using LD = GemmLds<PREC>;
   __shared__ __attribute__((aligned(16))) char lds[LD::BYTES];
-  const GemmWork wk = work[blockIdx.x];
+  const GemmWork wk = work[xcd_work_index()];
   const TileG t = tile_of(tiles, wk.tile);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -603,15 +646,31 @@ __global__ __launch_bounds__(THREADS) void gemm_ns_kernel(const GemmTile *__rest
   __syncthreads();
   const float a = gp.a, b = gp.b, c = gp.c;
   const bool fold = gp.fold != 0;
-  // value of the product element (i, j) as stored
-  auto finish = [&](float d, int i, int j) -> float {
+  // value of the product element (i, j) as stored; e is element (i, j) of the matrix the
+  // epilogue adds (A for the square, X for an update without a folded into B)
+  auto finish = [&](float d, float e, int i, int j) -> float {
     if constexpr (MODE == MODE_GRAM) {
       if (c != 0.f) return d;
       return b * d + ((fold && i == j) ? a : 0.f);
     } else if constexpr (MODE == MODE_SQUARE) {
-      return __builtin_fmaf(c, d, b * A.get(i, j)) + ((fold && i == j) ? a : 0.f);
+      return __builtin_fmaf(c, d, b * e) + ((fold && i == j) ? a : 0.f);
     } else {
-      return fold ? d : __builtin_fmaf(a, Xc.get(i, j), d);
+      return fold ? d : __builtin_fmaf(a, e, d);
+    }
+  };
+  // the 16 elements of that matrix at row i from column j (coalesced loads)
+  auto addend16 = [&](int i, int j, float (&e)[16]) {
+    if constexpr (MODE == MODE_SQUARE) {
+      A.get16(i, j, e);
+    } else if constexpr (MODE == MODE_UPDATE) {
+      if (!fold) {
+        Xc.get16(i, j, e);
+        return;
+      }
+    }
+    if constexpr (MODE != MODE_SQUARE) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) e[q] = 0.f;
     }
   };
   const Planes<PREC> O = MODE == MODE_GRAM ? (c != 0.f ? A : B) : (MODE == MODE_SQUARE ? B : Xn);
@@ -622,9 +681,10 @@ __global__ __launch_bounds__(THREADS) void gemm_ns_kernel(const GemmTile *__rest
     const int il = u >> 3, jl = (u & 7) * 16;
     const int i = i0 + il, j = j0 + jl;
     if (i >= t.r || j >= ldo) continue;
-    float v[16];
+    float v[16], e[16];
+    addend16(i, j, e);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = j + q < valid ? finish(st[(jl + q) * LD::SP + il], i, j + q) : 0.f;
+    for (int q = 0; q < 16; ++q) v[q] = j + q < valid ? finish(st[(jl + q) * LD::SP + il], e[q], i, j + q) : 0.f;
     O.put16(i, j, v);
   }
   // (2) symmetric products: the mirrored block D^T at rows j0 + jl, columns i0 + il
@@ -634,9 +694,11 @@ __global__ __launch_bounds__(THREADS) void gemm_ns_kernel(const GemmTile *__rest
         const int jl = u >> 3, il = (u & 7) * 16;
         const int j = j0 + jl, i = i0 + il;
         if (j >= t.r || i >= ldo) continue;
-        float v[16];
+        // element (i + q, j) of the symmetric A equals (j, i + q): a contiguous row
+        float v[16], e[16];
+        addend16(j, i, e);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) v[q] = i + q < valid ? finish(st[jl * LD::SP + il + q], i + q, j) : 0.f;
+        for (int q = 0; q < 16; ++q) v[q] = i + q < valid ? finish(st[jl * LD::SP + il + q], e[q], i + q, j) : 0.f;
         O.put16(j, i, v);
       }
     }
