@@ -129,6 +129,47 @@ def cpu_baseline(K, coeffs, tile, shapes):
             "seconds": dt}
 
 
+def run_diagnostics(args):
+    """Matrix-function diagnostics sweep (not the step benchmark): the three distinct
+    matrix shapes of the 1B-shaped stack, power-law inputs, bf16 state, bf16x3, K=5
+    quintic; per T the deviation from the FULL map, the alignment with the polar factor,
+    the extreme singular values of O_T and the device time of the NS step.  The fp64
+    oracle computes the same diagnostics of one 512 x 512 matrix beside it."""
+    import torch
+    import synth
+    import tiled_newton_schulz_tile_amd as hm
+    from tiled_newton_schulz_tile_amd import diagnostics as dg
+    tiles = [32, 64, 128, 256, 0]
+    shapes = sorted(set(synth.STACKS["decoder-1b-16L"]))
+    res = {}
+    for i, (H, W) in enumerate(shapes):
+        M = synth.power_law_matrix(H, W, 7000 + i, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        rep = dg.report(M, tiles, 5, hm.QUINTIC, precision=hm.PREC_BF16X3, spectrum=False)
+        res[f"{H}x{W}"] = {("full" if T == 0 else str(T)): {k: round(v, 6) for k, v in rep[T].items()}
+                           for T in tiles}
+        log(f"[diag] {H}x{W}: " + "  ".join(
+            f"T={'full' if T == 0 else T}: dev {rep[T]['deviation']:.4f} cos {rep[T]['cosine']:.4f} "
+            f"align {rep[T]['alignment']:.4f} dual {rep[T]['dual_alignment']:.4f} "
+            f"sv [{rep[T]['sv_min']:.3f}, {rep[T]['sv_max']:.3f}] {rep[T]['ms']:.2f} ms" for T in tiles))
+    cpu = None
+    if not args.no_cpu:
+        import oracle.diagnostics as odg
+        M = synth.power_law_matrix(512, 512, 7100, dtype=torch.float32).to(torch.bfloat16)
+        t0 = time.time()
+        odg.report(M.double().numpy(), tiles, 5, hm.QUINTIC)
+        cpu = {"sample": "512x512 power-law matrix, the same five T", "seconds": round(time.time() - t0, 3),
+               "kind": "oracle"}
+        t0 = time.time()
+        dg.report(M.cuda(), tiles, 5, hm.QUINTIC, precision=hm.PREC_BF16X3)
+        cpu["gpu_seconds_same_sample"] = round(time.time() - t0, 3)
+    print(json.dumps({"metric": "matrix-function diagnostics vs T (deviation and cosine against FULL, "
+                                "alignment and dual alignment with the polar factor, singular values of O_T)",
+                      "data": "synthetic: G = U diag(1/i) V^T + 0.01 N(0,1), Haar U, V; seeded",
+                      "config": {"workload": "decoder-1b-16L distinct shapes", "ns_steps": 5,
+                                 "coeffs": "quintic", "state_dtype": "bf16", "precision": "bf16x3"},
+                      "results": res, "cpu_baseline": cpu}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +182,8 @@ def main():
     ap.add_argument("--workload", type=str, default="llama3-8b-32L")
     ap.add_argument("--inputs", choices=["power-law", "randn"], default="power-law")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="run the matrix-function diagnostics sweep instead of the step benchmark")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the HiMuon step is tile-local and this build runs on "
@@ -153,6 +196,9 @@ def main():
     import tiled_newton_schulz_tile_amd as hm
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.diagnostics:
+        run_diagnostics(args)
+        return
     dev = torch.device("cuda:0")
     shapes = synth.STACKS[args.workload]
     K, coeffs = 5, hm.QUINTIC

@@ -4,3 +4,4 @@ from .himuon_oracle import (  # noqa: F401
     ns_tile, tiled_ns, tiled_ns_loop, tiles_ns_sample, phi, phi_iterate, momentum,
     bf16_round, momentum_stored, apply_update, step, tile_flops, ns_flops, step_bytes,
 )
+from . import diagnostics  # noqa: F401,E402
