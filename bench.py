@@ -170,6 +170,66 @@ def run_diagnostics(args):
                       "results": res, "cpu_baseline": cpu}), flush=True)
 
 
+def run_sign(args):
+    """Sign-Muon local kernels on 2^28 entries (a 16384 x 16384 fp32 direction): sign +
+    1-bit pack, and the majority vote of 8 workers' packed buffers into bf16.  Both are
+    HBM streams; algorithmic bytes: pack 4 B read + 1/8 B written per entry, vote 1/8 B read
+    per worker + 2 B written per entry.  The numpy oracle does the same on 2^22 entries."""
+    import numpy as np
+    import torch
+    from tiled_newton_schulz_tile_amd import signmuon as sm
+    rows = cols = 16384
+    n, workers = rows * cols, 8
+    g = torch.Generator(device="cuda").manual_seed(0)
+    O = torch.randn(rows, cols, device="cuda", generator=g)
+    bits = torch.zeros(sm.packed_bytes(n), dtype=torch.uint8, device="cuda")
+    gathered = torch.randint(0, 256, (workers, sm.packed_bytes(n)), dtype=torch.uint8, device="cuda", generator=g)
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_pack = timed(lambda: sm.sign_pack(O, out=bits), args.steps)
+    ms_vote = timed(lambda: sm.sign_vote(gathered, n, torch.bfloat16, out=out), args.steps)
+    b_pack = n * 4 + (n + 7) // 8
+    b_vote = workers * ((n + 7) // 8) + 2 * n
+    res = {}
+    for name, ms, b in (("sign_pack_kernel", ms_pack, b_pack), ("sign_vote_kernel<bf16>, 8 workers", ms_vote, b_vote)):
+        gbs = b / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "bytes": b, "GB/s": round(gbs, 1),
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBPS,
+                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBPS, 4)}}
+        log(f"[sign] {name}: {ms:.3f} ms, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBPS:.1f} % of HBM peak)")
+    cpu = None
+    if not args.no_cpu:
+        import oracle.signmuon as osm
+        m = 1 << 22
+        x = np.random.default_rng(0).standard_normal(m).astype(np.float32)
+        t0 = time.time()
+        packed = osm.pack(osm.sign(x))
+        t_pack = time.time() - t0
+        bufs = [packed] * workers
+        t0 = time.time()
+        osm.vote(bufs, m)
+        t_vote = time.time() - t0
+        cpu = {"kind": "oracle", "sample": f"{m} entries, 8 workers", "pack_seconds": round(t_pack, 4),
+               "vote_seconds": round(t_vote, 4),
+               "pack_GB/s": round((4 * m + m / 8) / t_pack / 1e9, 3),
+               "vote_GB/s": round((workers * m / 8 + 2 * m) / t_vote / 1e9, 3)}
+    print(json.dumps({"metric": "Sign-Muon local kernels: HBM GB/s", "data": "synthetic: N(0,1) direction, "
+                      "uniform random packed buffers; seeded", "config": {"workload": "16384x16384 direction, "
+                      "8 workers", "entries": n}, "results": res, "cpu_baseline": cpu}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +244,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--diagnostics", action="store_true",
                     help="run the matrix-function diagnostics sweep instead of the step benchmark")
+    ap.add_argument("--sign", action="store_true",
+                    help="time the Sign-Muon sign-pack and vote kernels instead of the step benchmark")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the HiMuon step is tile-local and this build runs on "
@@ -198,6 +260,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.diagnostics:
         run_diagnostics(args)
+        return
+    if args.sign:
+        run_sign(args)
         return
     dev = torch.device("cuda:0")
     shapes = synth.STACKS[args.workload]

@@ -170,6 +170,30 @@ HIMUON_API void himuon_plan_destroy(himuon_plan_t *p);
 /* Message of the last failure on this thread ("" if none). */
 HIMUON_API const char *himuon_last_error(void);
 
+/* ---- Sign-Muon, local pieces ----------------------------------------------------
+   "Sign-Muon: Communication-Efficient Distributed Muon Optimization" (Figures 1 and 6):
+   a worker forms the entrywise sign S in {-1, +1} of its Newton-Schulz direction, packs
+   it to one bit per entry for an all-gather, and takes the majority vote of the gathered
+   buffers locally.  The collective itself is not part of this library.                */
+
+/* Packs sign(o) of a rows x cols fp32 device matrix (row-major, leading dimension
+   ld >= cols) into `bits` (device, 8-byte aligned, ceil(rows * cols / 8) bytes, written
+   in full): entry k = i * cols + j is bit k % 8 (least significant first) of byte k / 8,
+   1 for o >= 0 (so sign(0) = +1), 0 otherwise (NaN included).  Enqueued on hip_stream.
+   EINVAL: NULL pointers with rows * cols > 0, negative sizes, ld < cols, misaligned bits.
+   EDEVICE: launch failure.                                                            */
+HIMUON_API himuon_status himuon_sign_pack(const float *o, int64_t rows, int64_t cols, int64_t ld,
+                                          uint8_t *bits, void *hip_stream);
+
+/* Majority vote over the packed sign buffers of `workers` workers (1..255), worker m's
+   buffer at bits + m * stride (device; bits and stride 4-byte aligned, stride >=
+   ceil(n / 8)): out[k] = +scale if at least half of the workers have bit k set, else
+   -scale, for k < n (a tie counts as +1).  out: device array of n elements of out_dtype
+   (HIMUON_F32 or HIMUON_BF16).  Enqueued on hip_stream.  EINVAL on bad arguments,
+   EDEVICE on launch failure.                                                          */
+HIMUON_API himuon_status himuon_sign_vote(const uint8_t *bits, int32_t workers, int64_t stride, int64_t n,
+                                          himuon_dtype out_dtype, void *out, float scale, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

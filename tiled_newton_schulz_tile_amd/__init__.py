@@ -34,7 +34,8 @@ STATUS = {0: "HIMUON_OK", -1: "HIMUON_EINVAL", -2: "HIMUON_EBUDGET", -3: "HIMUON
 
 # every entry point include/himuon.h declares
 EXPORTED = ("himuon_plan", "himuon_workspace_size", "himuon_step", "himuon_set_tile_schedule",
-            "himuon_plan_stats", "himuon_plan_tiles", "himuon_plan_destroy", "himuon_last_error")
+            "himuon_plan_stats", "himuon_plan_tiles", "himuon_plan_destroy", "himuon_last_error",
+            "himuon_sign_pack", "himuon_sign_vote")
 
 
 class HiMuonError(RuntimeError):
@@ -85,8 +86,12 @@ def _load() -> ctypes.CDLL:
     path = library_path()
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
-                          "`python -m tiled_newton_schulz_tile_amd.build` (hipcc, gfx950)")
+                          "`python tiled_newton_schulz_tile_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(path)
+    missing = [n for n in EXPORTED if not hasattr(lib, n)]
+    if missing:
+        raise ImportError(f"{path} is stale (no {', '.join(missing)}): rebuild it with "
+                          "`python tiled_newton_schulz_tile_amd/build.py`")
     P = ctypes.c_void_p
     lib.himuon_plan.argtypes = [ctypes.POINTER(himuon_layer), ctypes.c_int32,
                                 ctypes.POINTER(himuon_config), ctypes.POINTER(P)]
@@ -98,6 +103,9 @@ def _load() -> ctypes.CDLL:
                                       ctypes.POINTER(ctypes.c_int64)]
     lib.himuon_plan_destroy.argtypes = [P]
     lib.himuon_plan_destroy.restype = None
+    lib.himuon_sign_pack.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P]
+    lib.himuon_sign_vote.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                     P, ctypes.c_float, P]
     lib.himuon_last_error.argtypes = []
     lib.himuon_last_error.restype = ctypes.c_char_p
     for name in EXPORTED:
@@ -157,6 +165,16 @@ def himuon_plan_tiles(plan) -> list:
 
 def himuon_plan_destroy(plan) -> None:
     _lib.himuon_plan_destroy(plan)
+
+
+def himuon_sign_pack(o_ptr: int, rows: int, cols: int, ld: int, bits_ptr: int, stream_ptr: int) -> None:
+    _check(_lib.himuon_sign_pack(o_ptr or None, rows, cols, ld, bits_ptr or None, stream_ptr or None))
+
+
+def himuon_sign_vote(bits_ptr: int, workers: int, stride: int, n: int, out_dtype: int, out_ptr: int,
+                     scale: float, stream_ptr: int) -> None:
+    _check(_lib.himuon_sign_vote(bits_ptr or None, workers, stride, n, out_dtype, out_ptr or None, scale,
+                                 stream_ptr or None))
 
 
 # ------------------------------------------------------------------ torch wrapper

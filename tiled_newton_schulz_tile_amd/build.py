@@ -1,6 +1,8 @@
 """Builds libhimuon.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m tiled_newton_schulz_tile_amd.build
+    python tiled_newton_schulz_tile_amd/build.py
+
+(run as a script: importing the package loads the library this builds)
 """
 from __future__ import annotations
 

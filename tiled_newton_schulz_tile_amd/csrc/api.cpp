@@ -239,3 +239,30 @@ void himuon_plan_destroy(himuon_plan_t *p) {
 const char *himuon_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"
+
+extern "C" HIMUON_API himuon_status himuon_sign_pack(const float *o, int64_t rows, int64_t cols, int64_t ld,
+                                                     uint8_t *bits, void *hip_stream) {
+  if (rows < 0 || cols < 0 || ld < cols) return fail(HIMUON_EINVAL, "sizes must be >= 0 and ld >= cols");
+  if (rows == 0 || cols == 0) return HIMUON_OK;
+  if (rows > (INT64_MAX / 2) / cols) return fail(HIMUON_EINVAL, "rows * cols too large");
+  if (!o || !bits) return fail(HIMUON_EINVAL, "NULL pointer");
+  if (reinterpret_cast<uintptr_t>(bits) % 8) return fail(HIMUON_EINVAL, "bits must be 8-byte aligned");
+  hipError_t e = himuon::launch_sign_pack(o, rows, cols, ld, bits, reinterpret_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? HIMUON_OK : hip_fail(e, "sign pack launch");
+}
+
+extern "C" HIMUON_API himuon_status himuon_sign_vote(const uint8_t *bits, int32_t workers, int64_t stride, int64_t n,
+                                                     himuon_dtype out_dtype, void *out, float scale,
+                                                     void *hip_stream) {
+  if (n < 0) return fail(HIMUON_EINVAL, "n must be >= 0");
+  if (workers < 1 || workers > 255) return fail(HIMUON_EINVAL, "workers must be in [1, 255]");
+  if (out_dtype != HIMUON_F32 && out_dtype != HIMUON_BF16) return fail(HIMUON_EINVAL, "out_dtype");
+  if (!std::isfinite(scale)) return fail(HIMUON_EINVAL, "scale must be finite");
+  if (n == 0) return HIMUON_OK;
+  if (!bits || !out) return fail(HIMUON_EINVAL, "NULL pointer");
+  if (stride < (n + 7) / 8 || stride % 4 || reinterpret_cast<uintptr_t>(bits) % 4)
+    return fail(HIMUON_EINVAL, "stride must be >= ceil(n / 8), and bits and stride 4-byte aligned");
+  hipError_t e = himuon::launch_sign_vote(bits, workers, stride, n, out_dtype == HIMUON_BF16, out, scale,
+                                          reinterpret_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? HIMUON_OK : hip_fail(e, "sign vote launch");
+}

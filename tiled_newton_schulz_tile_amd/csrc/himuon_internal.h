@@ -94,4 +94,15 @@ hipError_t launch_gemm_chunk(int prec, int state_bf16, const LayerDesc *layers, 
                              const GemmChunkLaunch &c, char *workspace, const NSParams &p,
                              hipStream_t stream);
 
+// ---- Sign-Muon local kernels (sign.hip) -----------------------------------------
+// Sign of a rows x cols fp32 matrix (leading dimension ld) packed to one bit per entry
+// (row-major entry k at byte k / 8, bit k % 8; 1 = non-negative).  bits: 8-byte aligned,
+// ceil(rows * cols / 8) bytes.
+hipError_t launch_sign_pack(const float *o, int64_t rows, int64_t cols, int64_t ld, unsigned char *bits,
+                            hipStream_t stream);
+// Majority vote over `workers` packed buffers (worker m at bits + m * stride; bits and
+// stride 4-byte aligned): out[k] = +-scale, ties +scale; out fp32 or bf16.
+hipError_t launch_sign_vote(const unsigned char *bits, int workers, int64_t stride, int64_t n, bool out_bf16,
+                            void *out, float scale, hipStream_t stream);
+
 }  // namespace himuon
