@@ -62,9 +62,16 @@ typedef enum { HIMUON_F32 = 0, HIMUON_BF16 = 1 } himuon_dtype;
 typedef enum {
   HIMUON_PREC_F32 = 0,    /* fp32 operands (fp32 MFMA)                                  */
   HIMUON_PREC_BF16 = 1,   /* operands rounded once to bf16, one bf16 MFMA per product   */
-  HIMUON_PREC_BF16X3 = 2  /* operands split x = hi + lo (both bf16), three bf16 products
+  HIMUON_PREC_BF16X3 = 2, /* operands split x = hi + lo (both bf16), three bf16 products
                              hi*hi + hi*lo + lo*hi per product: fp32-class accuracy at
                              3x the bf16 MFMA work                                       */
+  HIMUON_PREC_BF16F8 = 3  /* the same split, with the two correction products hi*lo and
+                             lo*hi on e4m3 (fp8) MFMA at twice the bf16 rate: 2x the bf16
+                             MFMA time; each fp8 operand carries a power-of-two scale
+                             chosen at plan time from bounds on the iterates.  Fused tiles
+                             of edge 64 and 128 run it; smaller tiles and the large-tile
+                             path run HIMUON_PREC_BF16X3.  himuon_plan returns
+                             HIMUON_EINVAL if the coefficients' iterates are unbounded. */
 } himuon_precision;
 
 #define HIMUON_TILE_FULL 0            /* one tile per matrix: full-matrix Muon        */

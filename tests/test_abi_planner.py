@@ -98,6 +98,40 @@ def test_llama_stack_tile_count_and_work():
     assert st["issued_flops"] == 2.25 * st["ns_flops"]
 
 
+def test_bf16f8_issues_one_bf16_and_two_half_rate_products():
+    p = plan_for(synth.STACKS["llama3-8b-32L"], 128, precision=hm.PREC_BF16F8)
+    st = hm.himuon_plan_stats(p)
+    hm.himuon_plan_destroy(p)
+    assert st["ns_flops"] == 6 * 6979321856 * 128 * 5
+    # hi*hi in bf16 plus two e4m3 products at twice the rate: 2 bf16-product units per
+    # product, on 10 of 16 blocks for the symmetric ones: 2 * (2 * 10/16 + 1) / 3 = 1.5x
+    assert st["issued_flops"] == 1.5 * st["ns_flops"]
+    # edge-32 tiles run the bf16x3 products
+    p = plan_for([(256, 512)], 32, precision=hm.PREC_BF16F8)
+    st32 = hm.himuon_plan_stats(p)
+    hm.himuon_plan_destroy(p)
+    p = plan_for([(256, 512)], 32, precision=hm.PREC_BF16X3)
+    assert st32["issued_flops"] == hm.himuon_plan_stats(p)["issued_flops"]
+    hm.himuon_plan_destroy(p)
+
+
+@pytest.mark.parametrize("coeffs,K,ok", [
+    (hm.QUINTIC, 5, True), (hm.QUINTIC, 100, True), (hm.CUBIC, 8, True),
+    ((2.0, -1.5, 0.5), 6, True), ((10.0, 10.0, 10.0), 5, False), ((3.0, 0.0, 0.0), 200, False),
+])
+def test_bf16f8_needs_bounded_iterates(coeffs, K, ok):
+    # the e4m3 scales come from bounds on the iterates: 10 s + 10 s^3 + 10 s^5 and 3 s
+    # grow without bound, so the plan is refused; the shipped presets are bounded
+    if ok:
+        hm.himuon_plan_destroy(plan_for([(300, 170)], 128, steps=K, coeffs=coeffs, precision=hm.PREC_BF16F8))
+    else:
+        with pytest.raises(hm.HiMuonError) as e:
+            plan_for([(300, 170)], 128, steps=K, coeffs=coeffs, precision=hm.PREC_BF16F8)
+        assert e.value.status == -1 and "unbounded" in str(e.value)
+        # the other precisions do not depend on the bounds
+        hm.himuon_plan_destroy(plan_for([(300, 170)], 128, steps=K, coeffs=coeffs, precision=hm.PREC_BF16X3))
+
+
 def test_full_and_large_tiles_use_gemm_path_and_chunks():
     shapes = [(4096, 14336), (14336, 4096), (4096, 1024)]
     p = plan_for(shapes, 0, workspace_budget=10 ** 9)

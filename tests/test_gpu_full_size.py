@@ -56,7 +56,8 @@ def check_step(picks, W0, W1, M1, T, K, coeffs, tol=(2e-2, 1e-2)):
     return worst, (num / den) ** 0.5
 
 
-def test_llama3_8b_stack_t128_bench_configuration():
+@pytest.mark.parametrize("prec", [hm.PREC_BF16X3, hm.PREC_BF16F8])
+def test_llama3_8b_stack_t128_bench_configuration(prec):
     _need_gpu()
     shapes = synth.STACKS["llama3-8b-32L"]
     import bench
@@ -65,7 +66,7 @@ def test_llama3_8b_stack_t128_bench_configuration():
     picks = sample_tiles(shapes, 128, 1000, 7, whole=(4, 6))
     W0 = grab(layers, picks, 0)
     G = grab(layers, picks, 2)
-    opt = hm.HiMuon(layers, 128, 5, hm.QUINTIC, workspace_budget=4 * 10 ** 9, precision=hm.PREC_BF16X3)
+    opt = hm.HiMuon(layers, 128, 5, hm.QUINTIC, workspace_budget=4 * 10 ** 9, precision=prec)
     opt.step(LR)
     torch.cuda.synchronize()
     opt.close()
@@ -74,9 +75,9 @@ def test_llama3_8b_stack_t128_bench_configuration():
     for g, m in zip(G, M1):
         assert torch.equal(g, m)           # M0 = 0: the stored momentum is G exactly
     worst, rf = check_step(picks, W0, W1, M1, 128, 5, Q)
-    print(f"\n8B stack T=128: {len(picks)} tiles, worst max-abs {worst[0]:.2e}, "
+    print(f"\n8B stack T=128 precision {prec}: {len(picks)} tiles, worst max-abs {worst[0]:.2e}, "
           f"worst tile rel-F {worst[1]:.2e}, pooled rel-F {rf:.2e}")
-    assert worst[0] < 2e-3                 # bf16x3 is fp32-class
+    assert worst[0] < (2e-3 if prec == hm.PREC_BF16X3 else 5e-3)   # bf16x3 is fp32-class
 
 
 def test_gpt2_stack_every_tile():

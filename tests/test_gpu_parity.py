@@ -100,6 +100,34 @@ def test_gpt2_layer_bf16x3_quintic(T):
         assert_bar(U, O, hm.PREC_BF16X3, tight=2e-3)
 
 
+@pytest.mark.parametrize("T", [32, 64, 128])
+@pytest.mark.parametrize("coeffs", [Q, C])
+def test_gpt2_layer_bf16f8(T, coeffs):
+    # hi*hi in bf16 with the two correction products in e4m3: about 20x inside the bf16
+    # bar on these matrices (edge-32 tiles run the bf16x3 products)
+    mats = [power_law(h, w, 150 + i) for i, (h, w) in enumerate(GPT2_LAYER)]
+    (res,), _ = gpu_step(mats, T, coeffs=coeffs, prec=hm.PREC_BF16F8)
+    for (W, M, U), G in zip(res, mats):
+        assert torch.equal(M, G.to(torch.bfloat16))
+        O = oracle.tiled_ns(M.double().numpy(), T, 5, coeffs)
+        assert_bar(U, O, hm.PREC_BF16F8, tight=5e-3)
+
+
+@pytest.mark.parametrize("T", [64, 128])
+@pytest.mark.parametrize("coeffs,K", [(C, 20), ((2.0, -1.5, 0.5), 6), ((1.875, -1.25, 0.375), 8)])
+def test_bf16f8_long_runs_and_other_coefficients(T, coeffs, K):
+    # K = 20 runs past the 16-entry table of per-step scales (its last entry serves the
+    # later steps), with the cubic map, which contracts towards the polar factor (the
+    # quintic preset keeps the singular values oscillating and amplifies any rounding
+    # over many steps, in every arithmetic); the other coefficient sets exercise the
+    # bounds that pick the scales
+    mats = [power_law(h, w, 170 + i) for i, (h, w) in enumerate(GPT2_LAYER[:2])]
+    (res,), _ = gpu_step(mats, T, K=K, coeffs=coeffs, prec=hm.PREC_BF16F8)
+    for (W, M, U), G in zip(res, mats):
+        O = oracle.tiled_ns(M.double().numpy(), T, K, coeffs)
+        assert_bar(U, O, hm.PREC_BF16F8, tight=5e-3)
+
+
 @pytest.mark.parametrize("T", [64, 128])
 def test_gpt2_layer_bf16_plain_cubic(T):
     mats = [power_law(h, w, 200 + i) for i, (h, w) in enumerate(GPT2_LAYER[:2])]
@@ -114,7 +142,8 @@ RAGGED = [(300, 170), (100, 260), (37, 53), (129, 1), (1, 200), (65, 65), (33, 9
 
 
 @pytest.mark.parametrize("T", [1, 7, 32, 64, 100, 128])
-@pytest.mark.parametrize("prec,state", [(0, torch.float32), (2, torch.bfloat16)])
+@pytest.mark.parametrize("prec,state", [(0, torch.float32), (2, torch.bfloat16), (3, torch.bfloat16),
+                                        (3, torch.float32)])
 @pytest.mark.parametrize("coeffs,K", [(Q, 5), (Q, 8), (C, 5)])
 def test_ragged_shapes(T, prec, state, coeffs, K):
     mats = [power_law(h, w, 300 + i) for i, (h, w) in enumerate(RAGGED)]
@@ -149,7 +178,8 @@ IDENTITY_SHAPES = [(100, 113), (113, 100), (300, 170), (170, 300), (1, 257), (25
 
 
 @pytest.mark.parametrize("T", [1, 7, 32, 64, 100, 128, 200, 256, 0])
-@pytest.mark.parametrize("state,prec", [(torch.float32, 0), (torch.bfloat16, 2), (torch.bfloat16, 1)])
+@pytest.mark.parametrize("state,prec", [(torch.float32, 0), (torch.bfloat16, 2), (torch.bfloat16, 1),
+                                        (torch.bfloat16, 3)])
 def test_identity_map_bit_exact(T, state, prec):
     """HIMUON_FLAG_IDENTITY_MAP: gather (oriented on the short side) and scatter only, so
     O is the stored momentum bit for bit at every tile size, on both the fused path
@@ -305,7 +335,8 @@ LARGE = [(300, 170), (170, 300), (520, 260), (129, 700), (1000, 1000), (37, 53)]
 
 
 @pytest.mark.parametrize("T", [200, 256, 0])
-@pytest.mark.parametrize("prec,state", [(0, torch.float32), (2, torch.bfloat16), (1, torch.bfloat16)])
+@pytest.mark.parametrize("prec,state", [(0, torch.float32), (2, torch.bfloat16), (1, torch.bfloat16),
+                                        (3, torch.bfloat16)])
 @pytest.mark.parametrize("coeffs,K", [(Q, 5), (C, 5), (Q, 8)])
 def test_large_tiles_and_full(T, prec, state, coeffs, K):
     if prec == 1 and coeffs == Q:
@@ -314,7 +345,7 @@ def test_large_tiles_and_full(T, prec, state, coeffs, K):
     (res,), _ = gpu_step(mats, T, K=K, coeffs=coeffs, prec=prec, state=state)
     for (W, M, U), G in zip(res, mats):
         O = oracle.tiled_ns(M.double().numpy(), T, K, coeffs)
-        assert_bar(U, O, prec, tight=None if prec != 2 else 5e-3)
+        assert_bar(U, O, prec, tight=None if prec not in (2, 3) else 5e-3)
 
 
 def test_chunking_is_invisible():

@@ -49,11 +49,13 @@ CELLS = [(T, K, co) for T in (32, 64, 128, 256) for K in (5, 8) for co in ("quin
 def test_precision_cell(T, K, co):
     coeffs = Q if co == "quintic" else C
     row = {}
-    for name, prec in (("f32", hm.PREC_F32), ("bf16x3", hm.PREC_BF16X3), ("bf16", hm.PREC_BF16)):
+    for name, prec in (("f32", hm.PREC_F32), ("bf16x3", hm.PREC_BF16X3), ("bf16f8", hm.PREC_BF16F8),
+                       ("bf16", hm.PREC_BF16)):
         row[name] = run(T, K, coeffs, prec)
     print(f"\nPRECISION T={T} K={K} {co}: " +
           "  ".join(f"{n}: max-abs {v[0]:.2e} rel-F {v[1]:.2e}" for n, v in row.items()), flush=True)
     assert row["f32"][0] <= 1e-4
     assert row["bf16x3"][0] <= 2e-2 and row["bf16x3"][1] <= 1e-2
+    assert row["bf16f8"][0] <= 2e-2 and row["bf16f8"][1] <= 1e-2
     if co == "cubic":
         assert row["bf16"][0] <= 2e-2 and row["bf16"][1] <= 1e-2

@@ -18,14 +18,14 @@ __all__ = [
     "himuon_plan", "himuon_workspace_size", "himuon_step", "himuon_set_tile_schedule",
     "himuon_plan_stats", "himuon_plan_tiles", "himuon_plan_destroy", "himuon_last_error",
     "HiMuon", "CUBIC", "QUINTIC", "TILE_FULL", "F32", "BF16", "PREC_F32", "PREC_BF16",
-    "PREC_BF16X3", "FLAG_WRITE_UPDATE", "FLAG_IDENTITY_MAP", "library_path", "EXPORTED",
+    "PREC_BF16X3", "PREC_BF16F8", "FLAG_WRITE_UPDATE", "FLAG_IDENTITY_MAP", "library_path", "EXPORTED",
 ]
 
 CUBIC = (1.5, -0.5, 0.0)
 QUINTIC = (3.4445, -4.7750, 2.0315)
 TILE_FULL = 0
 F32, BF16 = 0, 1
-PREC_F32, PREC_BF16, PREC_BF16X3 = 0, 1, 2
+PREC_F32, PREC_BF16, PREC_BF16X3, PREC_BF16F8 = 0, 1, 2, 3
 FLAG_WRITE_UPDATE = 1
 FLAG_IDENTITY_MAP = 2
 

@@ -165,10 +165,14 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
   prm.identity = (c.flags & HIMUON_FLAG_IDENTITY_MAP) ? 1 : 0;
   prm.steps = prm.identity ? 0 : c.steps;
   prm.write_update = (c.flags & HIMUON_FLAG_WRITE_UPDATE) ? 1 : 0;
+  prm.f8 = pl.f8;
+  // the e4m3 correction products exist for fused tiles of edge 64 and 128 only
+  const int gemm_prec = c.precision == HIMUON_PREC_BF16F8 ? (int)HIMUON_PREC_BF16X3 : (int)c.precision;
   const auto *dl = reinterpret_cast<const himuon::LayerDesc *>(p->d_buf);
   const auto *dft = reinterpret_cast<const himuon::FusedTile *>(p->d_buf + p->off_ftiles);
   for (const himuon::FusedGroup &g : pl.fgroups) {
-    hipError_t e = himuon::launch_fused(g.ts, (int)c.precision, c.state_dtype == HIMUON_BF16,
+    const int fprec = c.precision == HIMUON_PREC_BF16F8 && g.ts < 64 ? (int)HIMUON_PREC_BF16X3 : (int)c.precision;
+    hipError_t e = himuon::launch_fused(g.ts, fprec, c.state_dtype == HIMUON_BF16,
                                         g.dense, dl, dft + g.first, g.n, prm, stream);
     if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
   }
@@ -190,7 +194,7 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
       cl.n_upd = ch.upd.n;
       cl.app = dw[4] + ch.app.first;
       cl.n_app = ch.app.n;
-      hipError_t e = himuon::launch_gemm_chunk((int)c.precision, c.state_dtype == HIMUON_BF16, dl, dgt, cl,
+      hipError_t e = himuon::launch_gemm_chunk(gemm_prec, c.state_dtype == HIMUON_BF16, dl, dgt, cl,
                                                reinterpret_cast<char *>(workspace), prm, stream);
       if (e != hipSuccess) return hip_fail(e, "large-tile kernel launch");
     }

@@ -73,6 +73,32 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
+// ---- fp8 (OCP e4m3: 3 mantissa bits, largest finite 448; larger values convert to NaN)
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// four floats divided by d (a power of two) and rounded to e4m3 (nearest even), a in
+// the lowest byte: two v_cvt_scalef32_pk_fp8_f32, which compute e4m3(x / d)
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pack_fp8x4(float a, float b, float c, float d, float div) {
+  s16x2 w = {0, 0};
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, div, false);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, div, true);
+  return __builtin_bit_cast(unsigned, w);
+}
+
+// 32x32x64 e4m3 MFMA with block scales, fp32 accumulation: c + 2^(sa-127) 2^(sb-127) A B.
+// Operand lane l holds 32 consecutive k (selected by l / 32) of row (column) l % 32 as
+// bytes; any k order works as long as both operands use the same one.  Output layout
+// as mma_bf16.
+__device__ __forceinline__ f32x16 mma_f8s(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// 2^e as a float, for -126 <= e <= 127
+__device__ __forceinline__ float pow2i(int e) { return __builtin_bit_cast(float, (unsigned)(127 + e) << 23); }
+
 // LDS-only workgroup barrier: this wave's LDS traffic is complete, then all waves
 // meet; global loads in flight are not waited for.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

@@ -57,7 +57,18 @@ struct GemmWork {
 // Elements per momentum block of the GEMM path.
 constexpr int kGemmMomentumBlock = 8192;
 
-enum Prec : int { PREC_F32 = 0, PREC_BF16 = 1, PREC_BF16X3 = 2 };
+enum Prec : int { PREC_F32 = 0, PREC_BF16 = 1, PREC_BF16X3 = 2, PREC_BF16F8 = 3 };
+
+// Power-of-two scales of the fp8 planes (PREC_BF16F8), per NS step k (the last entry
+// serves every later step): the e4m3 hi plane of a matrix holds x * 2^e, its lo plane
+// (x - bf16(x)) * 2^(e + 8).  e is chosen from a bound on the matrix's entries so that
+// no scaled value reaches the e4m3 range limit.
+constexpr int kF8Steps = 16;
+struct F8Exps {
+  int8_t x[kF8Steps];   // X_k (input of step k); x[k + 1] for the X stored by step k
+  int8_t a[kF8Steps];   // A_k = X_k X_k^T, stored as the operand of A^2 (c != 0)
+  int8_t b[kF8Steps];   // a I + b A_k + c A_k^2, the update's operand
+};
 
 struct NSParams {
   float a, b, c;
@@ -65,7 +76,12 @@ struct NSParams {
   int32_t steps;
   int32_t write_update;
   int32_t identity;  // gather -> scatter only: no normalisation (steps is 0 then)
+  F8Exps f8;
 };
+
+// Fills e with the fp8 plane exponents for coefficients (a, b, c) over `steps` steps;
+// returns false if some bound is not finite (the coefficients blow up).
+bool f8_exponents(double a, double b, double c, int steps, F8Exps &e);
 
 // ---- launchers (ns_fused.hip) --------------------------------------------------
 // Runs momentum, K NS steps and the weight update for every tile of `tiles`

@@ -17,7 +17,9 @@
 //   X  : the oriented tile (short side r = rows), row-major, TS x TS
 //   AB : A = X X^T, then B = b A + c A^2 (both symmetric), row-major, TS x TS
 // Element formats: PREC_F32 one fp32 array; PREC_BF16 one bf16 array;
-// PREC_BF16X3 two bf16 arrays (hi = bf16(x), lo = bf16(x - hi)).
+// PREC_BF16X3 two bf16 arrays (hi = bf16(x), lo = bf16(x - hi)); PREC_BF16F8 the bf16
+// hi array and two e4m3 arrays, h8 = e4m3(x 2^e) and l8 = e4m3((x - hi) 2^(e+8)), with
+// a power-of-two exponent e per matrix and step.
 // Each wave owns a 64 x 32 block (32 x 32 when TS = 32) of every product, so a 128 tile
 // has 8 waves and two waves share each SIMD: one wave's LDS and VALU work overlaps the
 // other's MFMAs.
@@ -69,8 +71,12 @@ struct Geo {
   static constexpr bool SWZ = TS == 128;
   static constexpr int PB = SWZ ? TS : TS + 8;        // bf16 row pitch (elements)
   static constexpr int PF = TS + 4;                   // fp32 row pitch (elements)
+  // e4m3 rows (PREC_BF16F8): 128 bytes for 128-tiles, their 16-byte chunks permuted
+  // (chunk c of row r at c ^ swz8(r)), else padded to a multiple of 16 bytes
+  static constexpr int P8 = SWZ ? TS : TS + 16;
   static constexpr int REGION = PREC == PREC_F32 ? TS * PF * 4
-                              : PREC == PREC_BF16 ? TS * PB * 2 : TS * PB * 4;
+                              : PREC == PREC_BF16 ? TS * PB * 2
+                              : PREC == PREC_BF16X3 ? TS * PB * 4 : TS * PB * 2 + 2 * TS * P8;
   static constexpr int TILE_LDS = 2 * REGION > TS * PF * 4 ? 2 * REGION : TS * PF * 4;
   // the chunk permutation of row r: the two 2-bit halves of r % 16 swapped
   static __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
@@ -84,6 +90,19 @@ struct Geo {
   }
   // element offset of (r, c) in a bf16 matrix
   static __device__ __forceinline__ int bidx(int r, int c) { return r * PB + bcol(r & 15, c); }
+  // The e4m3 rows' chunk permutation, a function of r % 16: sixteen consecutive rows
+  // reading one chunk, and the eight rows of a transposing read (two adjacent chunks
+  // each), then fall on distinct 16-byte bank groups of two 128-byte rows.
+  static __device__ __forceinline__ int swz8(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+  // byte column c of a row congruent to r16 modulo 16, as stored
+  static __device__ __forceinline__ int b8col(int r16, int c) {
+    if constexpr (SWZ) {
+      return c ^ (swz8(r16) << 4);
+    } else {
+      return c;
+    }
+  }
+  static __device__ __forceinline__ int b8idx(int r, int c) { return r * P8 + b8col(r & 15, c); }
   // workgroup barriers synchronise one tile: several tiles per workgroup only with
   // one wave per tile
   static_assert(WPT == 1 || TPB == 1, "tile groups must not share s_barrier");
@@ -104,6 +123,11 @@ template <>
 struct Mat<PREC_BF16X3> {
   __bf16 *hi, *lo;
 };
+template <>
+struct Mat<PREC_BF16F8> {
+  __bf16 *hi;
+  unsigned char *h8, *l8;
+};
 
 template <int TS, int PREC>
 __device__ __forceinline__ Mat<PREC> make_mat(char *base) {
@@ -112,6 +136,11 @@ __device__ __forceinline__ Mat<PREC> make_mat(char *base) {
     m.f = reinterpret_cast<float *>(base);
   } else if constexpr (PREC == PREC_BF16) {
     m.hi = reinterpret_cast<__bf16 *>(base);
+  } else if constexpr (PREC == PREC_BF16F8) {
+    using G = Geo<TS, PREC>;
+    m.hi = reinterpret_cast<__bf16 *>(base);
+    m.h8 = reinterpret_cast<unsigned char *>(base + TS * G::PB * 2);
+    m.l8 = reinterpret_cast<unsigned char *>(base + TS * G::PB * 2 + TS * G::P8);
   } else {
     m.hi = reinterpret_cast<__bf16 *>(base);
     m.lo = reinterpret_cast<__bf16 *>(base + TS * Geo<TS, PREC>::PB * 2);
@@ -149,6 +178,26 @@ __device__ __forceinline__ bf16x8 tr_frag_g(const __bf16 *buf, int k, int m, int
   const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4 *)(p1));
   const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// Transposing e4m3 operand read: lane l receives buf[kb + 32 (l / 32) + i][m + l % 32] as
+// byte i, i = 0..31.  ds_read_tr8_b64 works on groups of 16 lanes: lane i of a group
+// receives byte i % 8 of the 8-byte pieces read by lanes i / 8 + 2 j, j = 0..7.  So lane
+// t reads 8 consecutive columns (from 8 (t % 2)) of row t / 2 and receives column t of
+// eight consecutive rows; four such reads cover the 32 rows of the lane's k run.
+template <class G>
+__device__ __forceinline__ i32x8 tr8_frag_g(const unsigned char *buf, int kb, int m, int lane) {
+  const int t = lane & 15, g = lane >> 4;
+  const int col = m + 16 * (g & 1) + 8 * (t & 1);
+  const int r0 = kb + 32 * (g >> 1) + (t >> 1);
+  i32x8 out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2 *)(buf + G::b8idx(r0 + 8 * q, col)));
+    out[2 * q] = v[0];
+    out[2 * q + 1] = v[1];
+  }
+  return out;
 }
 
 // ------------------------------------------------------------------ wave GEMM
@@ -298,11 +347,156 @@ __device__ __forceinline__ void sched_chunks() {
   }
 }
 
-// Full K = TS contraction; ZERO: start from zero, else accumulate onto acc.  The
-// fragments of chunk c + 1 are read from LDS while the MFMAs of chunk c run.
-template <int TS, int PREC, bool TRANS_L, bool ZERO, int NB = Geo<TS, PREC>::NI, bool RALIAS = false>
-__device__ __forceinline__ void wave_gemm(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &Lm, int l0,
-                                          const Mat<PREC> &Rm, int r0, int lane) {
+// ---- PREC_BF16F8 products.  Per 64-k chunk, four stages of MFMAs: the correction
+// products h8_L l8_R and l8_L h8_R (one e4m3 MFMA, K = 64, per output block each), then
+// the main product hi_L hi_R in two 32-k halves (two bf16 MFMAs per block each), so that
+// every stage takes the same MFMA time.  The operands of stage i + 1 are read from LDS
+// while the MFMAs of stage i run, so a wave holds the operands of at most two stages.
+template <int TS>
+struct F8Half {   // one e4m3 plane of each side, one 64-k chunk
+  static constexpr int NI = Geo<TS, PREC_BF16F8>::NI, NJ = Geo<TS, PREC_BF16F8>::NJ;
+  i32x8 l[NI], r[NJ];
+};
+template <int TS>
+struct HiPiece {  // bf16 hi of each side, one 32-k half chunk (two 16-k pieces)
+  static constexpr int NI = Geo<TS, PREC_BF16F8>::NI, NJ = Geo<TS, PREC_BF16F8>::NJ;
+  bf16x8 l[2][NI], r[2][NJ];
+};
+
+// The e4m3 operands of one correction product: L from plane lp (rows, or columns when
+// TRANS_L), R from plane rp, k in [kb, kb + 64).  An aliased R block is read again here.
+template <int TS, bool TRANS_L, int NB>
+__device__ __forceinline__ void load_f8(F8Half<TS> &f, const unsigned char *lp, int l0, const unsigned char *rp,
+                                        int r0, int lane, int kb) {
+  using G = Geo<TS, PREC_BF16F8>;
+  const int li = lane & 31, half = lane >> 5;
+  // plain reads: 32 bytes of row r from byte kb + 32 (lane / 32); the rows are all
+  // congruent to lane % 16 modulo 16, so two column offsets serve every plain read
+  int ko0 = G::b8col(li & 15, kb + 32 * half), ko1 = G::b8col(li & 15, kb + 32 * half + 16);
+  if constexpr (G::SWZ) {
+    asm("" : "+v"(ko0));
+    asm("" : "+v"(ko1));
+  }
+  auto prow = [&](const unsigned char *plane, int r) -> i32x8 {
+    const i32x4 a = *reinterpret_cast<const i32x4 *>(plane + r * G::P8 + ko0);
+    const i32x4 b = *reinterpret_cast<const i32x4 *>(plane + r * G::P8 + ko1);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+#pragma unroll
+  for (int b = 0; b < G::NJ; ++b) f.r[b] = prow(rp, r0 + b * 32 + li);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if constexpr (TRANS_L) {
+      f.l[b] = tr8_frag_g<G>(lp, kb, l0 + b * 32, lane);
+    } else {
+      f.l[b] = prow(lp, l0 + b * 32 + li);
+    }
+  }
+}
+
+// bf16 hi operands of the 32-k half chunk at k0 (two 16-k pieces)
+template <int TS, bool TRANS_L, int NB, bool RALIAS>
+__device__ __forceinline__ void load_hi(HiPiece<TS> &h, const Mat<PREC_BF16F8> &Lm, int l0, const Mat<PREC_BF16F8> &Rm,
+                                        int r0, int lane, int k0) {
+  using G = Geo<TS, PREC_BF16F8>;
+  const int li = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int k = k0 + 16 * p + 8 * half;
+    int ko = G::bcol(li & 15, k);
+    if constexpr (G::SWZ) asm("" : "+v"(ko));
+    if constexpr (!RALIAS) {
+#pragma unroll
+      for (int b = 0; b < G::NJ; ++b)
+        h.r[p][b] = *reinterpret_cast<const bf16x8 *>(Rm.hi + (r0 + b * 32 + li) * G::PB + ko);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if constexpr (TRANS_L) {
+        h.l[p][b] = tr_frag_g<G>(Lm.hi, k, l0 + b * 32, lane);
+      } else {
+        h.l[p][b] = *reinterpret_cast<const bf16x8 *>(Lm.hi + (l0 + b * 32 + li) * G::PB + ko);
+      }
+    }
+    if constexpr (RALIAS) h.r[p][0] = h.l[p][0];
+  }
+}
+
+// Scheduler directives for the stage sequence: stage i's MFMAs, each followed by some
+// of stage i + 1's reads.  Stage kinds: 0, 1 the correction products, 2, 3 the halves.
+template <int ST, int NST, int NMF, int NRF, int NMH, int NRH>
+__device__ __forceinline__ void sched_f8() {
+  constexpr int kind = ST % 4, next = (ST + 1) % 4;
+  constexpr int NM = kind < 2 ? NMF : NMH;
+  if constexpr (ST + 1 < NST) {
+    constexpr int NR = next < 2 ? NRF : NRH;
+    sched_mfma_reads<NM, NR, (NR + NM - 1) / NM>();
+    sched_f8<ST + 1, NST, NMF, NRF, NMH, NRH>();
+  } else {
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+  }
+}
+
+// sc: the E8M0 scale byte of both correction products, 127 - (eL + eR + 8), which undoes
+// the operands' exponents
+template <int TS, bool TRANS_L, bool ZERO, int NB, bool RALIAS>
+__device__ __forceinline__ void wave_gemm_f8(Acc<Geo<TS, PREC_BF16F8>::NI, Geo<TS, PREC_BF16F8>::NJ> &acc,
+                                             const Mat<PREC_BF16F8> &Lm, int l0, const Mat<PREC_BF16F8> &Rm, int r0,
+                                             int lane, int sc) {
+  using G = Geo<TS, PREC_BF16F8>;
+  constexpr int NJ = G::NJ;
+  static_assert(TS % 64 == 0, "e4m3 products run on 64-k chunks");
+  constexpr int NC = TS / 64;
+  constexpr int NRF = NB * (TRANS_L ? 4 : 2) + 2 * NJ;            // reads of one correction stage
+  constexpr int NRH = 2 * (NB * (TRANS_L ? 2 : 1) + (RALIAS ? 0 : NJ));  // reads of one half
+  constexpr int NMF = NB * NJ, NMH = 2 * NB * NJ;
+  F8Half<TS> fa, fb;
+  HiPiece<TS> h[2];
+  load_f8<TS, TRANS_L, NB>(fa, Lm.h8, l0, Rm.l8, r0, lane, 0);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int kb = 64 * c;
+    // h8_L l8_R (small terms first)
+    load_f8<TS, TRANS_L, NB>(fb, Lm.l8, l0, Rm.h8, r0, lane, kb);
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NJ; ++bj)
+        acc.b[bi][bj] = mma_f8s(fa.l[bi], fa.r[bj], (ZERO && c == 0) ? f32x16{} : acc.b[bi][bj], sc, 127);
+    // l8_L h8_R
+    load_hi<TS, TRANS_L, NB, RALIAS>(h[0], Lm, l0, Rm, r0, lane, kb);
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_f8s(fb.l[bi], fb.r[bj], acc.b[bi][bj], sc, 127);
+    // hi_L hi_R in two halves
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      if (s2 == 0) {
+        load_hi<TS, TRANS_L, NB, RALIAS>(h[1], Lm, l0, Rm, r0, lane, kb + 32);
+      } else if (c + 1 < NC) {
+        load_f8<TS, TRANS_L, NB>(fa, Lm.h8, l0, Rm.l8, r0, lane, kb + 64);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < NJ; ++bj) acc.b[bi][bj] = mma_bf16(h[s2].l[p][bi], h[s2].r[p][bj], acc.b[bi][bj]);
+    }
+  }
+  if constexpr (SCHED_GEMM) {
+    __builtin_amdgcn_sched_group_barrier(0x100, NRF, 0);
+    sched_f8<0, 4 * NC, NMF, NRF, NMH, NRH>();
+  }
+}
+
+// Full K = TS contraction in the fp32, bf16 and bf16x3 formats; ZERO: start from zero,
+// else accumulate onto acc.  The fragments of chunk c + 1 are read from LDS while the
+// MFMAs of chunk c run.
+template <int TS, int PREC, bool TRANS_L, bool ZERO, int NB, bool RALIAS>
+__device__ __forceinline__ void wave_gemm_std(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &Lm,
+                                              int l0, const Mat<PREC> &Rm, int r0, int lane) {
   using G = Geo<TS, PREC>;
   static_assert(NB >= 1 && NB <= G::NI, "row blocks");
   constexpr int KC = PREC == PREC_F32 ? 8 : 16;
@@ -322,6 +516,18 @@ __device__ __forceinline__ void wave_gemm(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::
   if constexpr (SCHED_GEMM) {
     __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
     sched_chunks<NC, NM, NR>();
+  }
+}
+
+// Full K = TS contraction; ZERO: start from zero, else accumulate onto acc.
+// f8sc: the correction products' scale byte (PREC_BF16F8 only).
+template <int TS, int PREC, bool TRANS_L, bool ZERO, int NB = Geo<TS, PREC>::NI, bool RALIAS = false>
+__device__ __forceinline__ void wave_gemm(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &Lm, int l0,
+                                          const Mat<PREC> &Rm, int r0, int lane, int f8sc = 127) {
+  if constexpr (PREC == PREC_BF16F8) {
+    wave_gemm_f8<TS, TRANS_L, ZERO, NB, RALIAS>(acc, Lm, l0, Rm, r0, lane, f8sc);
+  } else {
+    wave_gemm_std<TS, PREC, TRANS_L, ZERO, NB, RALIAS>(acc, Lm, l0, Rm, r0, lane);
   }
 }
 
@@ -388,19 +594,85 @@ __device__ __forceinline__ void with_job(const SymJob &jb, F &&f) {
 // from position [col][row..row+3] of a row-major LDS matrix, i.e. they store the
 // transpose of the accumulator block.
 
+// The exponents of one kind of matrix over the NS steps, as packed bytes in scalar
+// registers: entry k of the table is the current one at step k, and the last entry
+// serves every later step.  (Indexing the kernel argument by the step would move it to
+// scratch memory.)
+struct ExpStream {
+  uint64_t lo = 0, hi = 0;
+  int n = 0;
+  __device__ __forceinline__ void init(const int8_t (&e)[kF8Steps]) {
+    static_assert(kF8Steps == 16, "two 64-bit words");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo |= (uint64_t)(uint8_t)e[i] << (8 * i);
+      hi |= (uint64_t)(uint8_t)e[8 + i] << (8 * i);
+    }
+  }
+  __device__ __forceinline__ int cur() const { return (int)(int8_t)(lo & 0xff); }
+  __device__ __forceinline__ int next() const { return n + 1 < kF8Steps ? (int)(int8_t)((lo >> 8) & 0xff) : cur(); }
+  __device__ __forceinline__ void advance() {
+    if (n + 1 < kF8Steps) {
+      lo = (lo >> 8) | (hi << 56);
+      hi >>= 8;
+      ++n;
+    }
+  }
+};
+
+// The three exponent streams of PREC_BF16F8 (X, A, B); empty for the other formats.
+template <bool ON>
+struct F8Steps {
+  __device__ __forceinline__ void init(const F8Exps &) {}
+  __device__ __forceinline__ int x() const { return 0; }
+  __device__ __forceinline__ int xn() const { return 0; }
+  __device__ __forceinline__ int a() const { return 0; }
+  __device__ __forceinline__ int b() const { return 0; }
+  __device__ __forceinline__ void advance() {}
+};
+template <>
+struct F8Steps<true> {
+  ExpStream sx, sa, sb;
+  __device__ __forceinline__ void init(const F8Exps &e) {
+    sx.init(e.x);
+    sa.init(e.a);
+    sb.init(e.b);
+  }
+  __device__ __forceinline__ int x() const { return sx.cur(); }
+  __device__ __forceinline__ int xn() const { return sx.next(); }
+  __device__ __forceinline__ int a() const { return sa.cur(); }
+  __device__ __forceinline__ int b() const { return sb.cur(); }
+  __device__ __forceinline__ void advance() {
+    sx.advance();
+    sa.advance();
+    sb.advance();
+  }
+};
+
+// Divisors of the e4m3 planes (PREC_BF16F8): the hi plane holds x / h = x 2^e, the lo
+// plane r / l = r 2^(e + 8).
+struct F8S {
+  float h = 1.f, l = 1.f / 256.f;
+};
+__device__ __forceinline__ F8S f8s_of(int e) { return F8S{pow2i(-e), pow2i(-e - 8)}; }
+
 // Store the transpose of the accumulators' first NB row blocks into a matrix in the
 // precision's format.  SCALE: the stored value is s_store * acc; BACK: afterwards acc <-
 // s_back * acc (one pass over the accumulators serves both).  MIRROR (symmetric
 // results): blocks off the diagonal are also stored untransposed, at [row][col].
-template <int TS, int PREC, bool SCALE = false, bool BACK = false, int NB = Geo<TS, PREC>::NI, bool MIRROR = false>
+// DIAG: diag is added to the stored diagonal elements.  f8: the e4m3 planes' multipliers.
+template <int TS, int PREC, bool SCALE = false, bool BACK = false, int NB = Geo<TS, PREC>::NI, bool MIRROR = false,
+          bool DIAG = false>
 __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &m, int p0, int q0,
-                                            int lane, float s_store = 1.f, float s_back = 1.f) {
+                                            int lane, float s_store = 1.f, float s_back = 1.f, F8S f8 = F8S{},
+                                            float diag = 0.f) {
   using G = Geo<TS, PREC>;
   const int li = lane & 31, half = lane >> 5;
 #pragma unroll
   for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
     for (int bj = 0; bj < G::NJ; ++bj) {
+      const bool on_diag = DIAG && p0 + bi * 32 == q0 + bj * 32;   // wave-uniform
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int row = p0 + bi * 32 + 8 * g + 4 * half;
@@ -410,9 +682,24 @@ __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>
         for (int e = 0; e < 4; ++e) {
           const float x = acc.b[bi][bj][4 * g + e];
           v[e] = SCALE ? x * s_store : x;
+          if constexpr (DIAG) {
+            if (on_diag && li == 8 * g + 4 * half + e) v[e] += diag;
+          }
           if constexpr (BACK) acc.b[bi][bj][4 * g + e] = x * s_back;
         }
-        if constexpr (PREC == PREC_F32) {
+        if constexpr (PREC == PREC_BF16F8) {
+          // hi (bf16) as below; h8 and l8 (e4m3) at [col][row .. row+3]: one 4-byte write each
+          const int o = col * G::PB + G::bcol(li & 15, row);
+          const u32x2 hi = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2 *>(m.hi + o) = hi;
+          const float r0 = v[0] - __builtin_bit_cast(float, hi[0] << 16);
+          const float r1 = v[1] - __builtin_bit_cast(float, hi[0] & 0xffff0000u);
+          const float r2 = v[2] - __builtin_bit_cast(float, hi[1] << 16);
+          const float r3 = v[3] - __builtin_bit_cast(float, hi[1] & 0xffff0000u);
+          const int o8 = col * G::P8 + G::b8col(li & 15, row);
+          *reinterpret_cast<unsigned *>(m.h8 + o8) = pack_fp8x4(v[0], v[1], v[2], v[3], f8.h);
+          *reinterpret_cast<unsigned *>(m.l8 + o8) = pack_fp8x4(r0, r1, r2, r3, f8.l);
+        } else if constexpr (PREC == PREC_F32) {
           *reinterpret_cast<f32x4 *>(m.f + col * G::PF + row) = v;
           if (MIRROR && p0 + bi * 32 != q0 + bj * 32) {   // off the diagonal (wave-uniform)
 #pragma unroll
@@ -459,6 +746,22 @@ __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>
           *reinterpret_cast<bf16x8 *>(m.lo + od) = vl;
         }
         *reinterpret_cast<bf16x8 *>(m.hi + od) = vh;
+      }
+      if constexpr (PREC == PREC_BF16F8) {
+        // e4m3 planes: lane t of a 16-lane group g reads 8 bytes of row q0 + 16 u + 8 (g / 2)
+        // + t / 2 of the transposed copy, and the transposing read hands lane t 8
+        // consecutive columns (q0 + 16 u + 8 (g / 2) ..) of row pb + 16 (g % 2) + t of the
+        // untransposed block, stored as one 8-byte piece.
+        const int pb = p0 + bi * 32, t = ln & 15, gg = ln >> 4;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int so = G::b8idx(q0 + 16 * u + 8 * (gg >> 1) + (t >> 1), pb + 16 * (gg & 1) + 8 * (t & 1));
+          const int dof = G::b8idx(pb + 16 * (gg & 1) + t, q0 + 16 * u + 8 * (gg >> 1));
+          const i32x2 a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2 *)(m.h8 + so));
+          const i32x2 b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2 *)(m.l8 + so));
+          *reinterpret_cast<i32x2 *>(m.h8 + dof) = a;
+          *reinterpret_cast<i32x2 *>(m.l8 + dof) = b;
+        }
       }
     }
   }
@@ -848,6 +1151,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
   const int p0 = (wv / (TS / G::WBN)) * G::WBM;          // wave block origin (rows)
   const int q0 = (wv % (TS / G::WBN)) * G::WBN;          //                   (columns)
   const float ca = prm.a, cb = prm.b, cc = prm.c;
+  const int fx0 = PREC == PREC_BF16F8 ? (int)prm.f8.x[0] : 0;   // exponent of X_0's e4m3 planes
 
   TileRegs<TS, NT, S> io;
   TileView t = view_of(tiles, tix);
@@ -927,6 +1231,24 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
           }
           *reinterpret_cast<f32x4 *>(X.f + r * PF + c) = a;
           *reinterpret_cast<f32x4 *>(X.f + r * PF + c + 4) = b;
+        } else if constexpr (PREC == PREC_BF16F8) {
+          const F8S f8 = f8s_of(fx0);
+          u32x4 hi;
+          float xv[8], rv[8];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            xv[e] = vd[i][e] * inv;
+            xv[e + 1] = vd[i][e + 1] * inv;
+            hi[e / 2] = pack_bf16x2(xv[e], xv[e + 1]);
+            rv[e] = __builtin_fmaf(vd[i][e], inv, -__builtin_bit_cast(float, hi[e / 2] << 16));
+            rv[e + 1] = __builtin_fmaf(vd[i][e + 1], inv, -__builtin_bit_cast(float, hi[e / 2] & 0xffff0000u));
+          }
+          *reinterpret_cast<u32x4 *>(X.hi + G::bidx(r, c)) = hi;
+          const int o8 = G::b8idx(r, c);
+          *reinterpret_cast<u32x2 *>(X.h8 + o8) = u32x2{pack_fp8x4(xv[0], xv[1], xv[2], xv[3], f8.h),
+                                                        pack_fp8x4(xv[4], xv[5], xv[6], xv[7], f8.h)};
+          *reinterpret_cast<u32x2 *>(X.l8 + o8) = u32x2{pack_fp8x4(rv[0], rv[1], rv[2], rv[3], f8.l),
+                                                        pack_fp8x4(rv[4], rv[5], rv[6], rv[7], f8.l)};
         } else {
           u32x4 hi, lo;
 #pragma unroll
@@ -945,7 +1267,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     } else {
       load_acc_t<TS, PREC>(xr, st, p0, q0, lane, inv);
       tile_sync<G::WPT>();
-      store_acc_t<TS, PREC>(xr, X, p0, q0, lane);
+      store_acc_t<TS, PREC>(xr, X, p0, q0, lane, 1.f, 1.f, f8s_of(fx0));
       tile_sync<G::WPT>();
     }
 
@@ -955,20 +1277,30 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     // X in fp32 registers and forms a X there, since its LDS copy is bf16-rounded.
     constexpr bool FOLD_A = PREC != PREC_BF16;
     // Dense tiles issue the loads of W before the last update product, so that their
-    // HBM latency passes while it runs (the other variants lack the registers).
-    constexpr bool EARLY_W = DENSE;
+    // HBM latency passes while it runs (the other variants, and PREC_BF16F8 with its
+    // larger operand fragments, lack the registers).
+    constexpr bool EARLY_W = DENSE && (PREC != PREC_BF16F8 || TS < 128);
     const SymJob jb = sym_job<TS>(wv);
+    // e4m3 plane exponents of the current step (PREC_BF16F8); a product's scale byte
+    // 127 - (eL + eR + 8) undoes its operands' exponents
+    constexpr bool F8 = PREC == PREC_BF16F8;
+    F8Steps<F8> fs;
+    if constexpr (F8) fs.init(prm.f8);
     // The symmetric part of a step, on the wave's job: B (with a on its diagonal when
     // folded) ends up in AB.
     auto sym_part = [&]() {
+      const int ex = fs.x(), ea = fs.a(), eb = fs.b();
       Acc<NI, NJ> acc;
       with_job<TS>(jb, [&](auto NBC, auto ALC) {
         constexpr int NB = decltype(NBC)::value;
         constexpr bool AL = decltype(ALC)::value;
-        wave_gemm<TS, PREC, false, true, NB, AL>(acc, X, jb.p0, X, jb.q0, lane);   // A = X X^T
+        wave_gemm<TS, PREC, false, true, NB, AL>(acc, X, jb.p0, X, jb.q0, lane, 127 - (2 * ex + 8));   // A = X X^T
         if (cc != 0.f) {
           // B = b A + c A^2 = c ((b/c) A + A A^T): accumulate A A^T onto (b/c) A
-          store_acc_t<TS, PREC, false, true, NB, true>(acc, AB, jb.p0, jb.q0, lane, 1.f, cb / cc);
+          store_acc_t<TS, PREC, false, true, NB, true>(acc, AB, jb.p0, jb.q0, lane, 1.f, cb / cc, f8s_of(ea));
+        } else if constexpr (F8) {
+          // B + a I = b A + a I
+          store_acc_t<TS, PREC, true, false, NB, true, true>(acc, AB, jb.p0, jb.q0, lane, cb, 1.f, f8s_of(eb), ca);
         } else {
           store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cb);   // B = b A
           if constexpr (FOLD_A) add_diag<TS, PREC, NB>(AB, jb.p0, jb.q0, lane, ca);       // B + a I
@@ -979,17 +1311,38 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
         with_job<TS>(jb, [&](auto NBC, auto ALC) {
           constexpr int NB = decltype(NBC)::value;
           constexpr bool AL = decltype(ALC)::value;
-          wave_gemm<TS, PREC, false, false, NB, AL>(acc, AB, jb.p0, AB, jb.q0, lane);
+          wave_gemm<TS, PREC, false, false, NB, AL>(acc, AB, jb.p0, AB, jb.q0, lane, 127 - (2 * ea + 8));
         });
         tile_sync<G::WPT>();                                             // A fully read
         with_job<TS>(jb, [&](auto NBC, auto) {
           constexpr int NB = decltype(NBC)::value;
-          store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cc);   // B
-          if constexpr (FOLD_A) add_diag<TS, PREC, NB>(AB, jb.p0, jb.q0, lane, ca);       // B + a I
+          if constexpr (F8) {
+            store_acc_t<TS, PREC, true, false, NB, true, true>(acc, AB, jb.p0, jb.q0, lane, cc, 1.f, f8s_of(eb), ca);
+          } else {
+            store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cc);   // B
+            if constexpr (FOLD_A) add_diag<TS, PREC, NB>(AB, jb.p0, jb.q0, lane, ca);       // B + a I
+          }
         });
       }
     };
-    if (prm.steps > 0) {
+    if constexpr (F8) {
+      for (int it = 0; it < prm.steps; ++it) {
+        sym_part();
+        const int sxb = 127 - (fs.x() + fs.b() + 8);
+        tile_sync<G::WPT>();
+        if (it + 1 == prm.steps) {
+          if constexpr (EARLY_W) io.template load_w<DENSE>(t, L, gt);
+          wave_gemm<TS, PREC, true, true>(xr, X, p0, AB, q0, lane, sxb);   // X^T <- X^T (aI + B)
+          tile_sync<G::WPT>();
+          break;
+        }
+        wave_gemm<TS, PREC, true, true>(xr, X, p0, AB, q0, lane, sxb);     // X^T <- X^T (aI + B)
+        tile_sync<G::WPT>();
+        store_acc_t<TS, PREC>(xr, X, p0, q0, lane, 1.f, 1.f, f8s_of(fs.xn()));
+        tile_sync<G::WPT>();
+        fs.advance();
+      }
+    } else if (prm.steps > 0) {
       for (int it = 0;; ++it) {
         sym_part();
         if constexpr (!FOLD_A) {
@@ -1082,6 +1435,12 @@ hipError_t launch_prec(int prec, int state_bf16, bool dense, const LayerDesc *la
     case PREC_F32: return launch_state<TS, PREC_F32>(state_bf16, dense, layers, tiles, n, p, stream);
     case PREC_BF16: return launch_state<TS, PREC_BF16>(state_bf16, dense, layers, tiles, n, p, stream);
     case PREC_BF16X3: return launch_state<TS, PREC_BF16X3>(state_bf16, dense, layers, tiles, n, p, stream);
+    case PREC_BF16F8:
+      if constexpr (TS >= 64) {
+        return launch_state<TS, PREC_BF16F8>(state_bf16, dense, layers, tiles, n, p, stream);
+      } else {
+        return hipErrorInvalidValue;   // the caller runs these tiles with PREC_BF16X3
+      }
     default: return hipErrorInvalidValue;
   }
 }
@@ -1105,6 +1464,9 @@ size_t fused_lds_bytes(int ts, int prec) {
     switch (prec) {
       case PREC_F32: return Geo<TS, PREC_F32>::TPB * Geo<TS, PREC_F32>::TILE_LDS;
       case PREC_BF16: return Geo<TS, PREC_BF16>::TPB * Geo<TS, PREC_BF16>::TILE_LDS;
+      case PREC_BF16F8:
+        if constexpr (TS >= 64) return Geo<TS, PREC_BF16F8>::TPB * Geo<TS, PREC_BF16F8>::TILE_LDS;
+        [[fallthrough]];
       default: return Geo<TS, PREC_BF16X3>::TPB * Geo<TS, PREC_BF16X3>::TILE_LDS;
     }
   };

@@ -91,8 +91,12 @@ himuon_status plan_init(Plan &p, const himuon_layer *layers, int32_t n, const hi
     return HIMUON_EINVAL;
   }
   if (c.precision != HIMUON_PREC_F32 && c.precision != HIMUON_PREC_BF16 &&
-      c.precision != HIMUON_PREC_BF16X3) {
-    err = "precision must be HIMUON_PREC_F32, HIMUON_PREC_BF16 or HIMUON_PREC_BF16X3";
+      c.precision != HIMUON_PREC_BF16X3 && c.precision != HIMUON_PREC_BF16F8) {
+    err = "precision must be HIMUON_PREC_F32, HIMUON_PREC_BF16, HIMUON_PREC_BF16X3 or HIMUON_PREC_BF16F8";
+    return HIMUON_EINVAL;
+  }
+  if (c.precision == HIMUON_PREC_BF16F8 && !f8_exponents(c.coeffs.a, c.coeffs.b, c.coeffs.c, c.steps, p.f8)) {
+    err = "HIMUON_PREC_BF16F8: the coefficients' iterates are unbounded; use HIMUON_PREC_BF16X3";
     return HIMUON_EINVAL;
   }
   if (c.flags & ~(HIMUON_FLAG_WRITE_UPDATE | HIMUON_FLAG_IDENTITY_MAP)) {
@@ -150,6 +154,68 @@ himuon_status plan_init(Plan &p, const himuon_layer *layers, int32_t n, const hi
   return HIMUON_OK;
 }
 
+// Bounds on the entries of the matrices of each NS step, from bounds on singular values
+// (an entry never exceeds the largest singular value): X_0 = Y / (|Y|_F + eps) has
+// sigma_max < 1; A = X X^T has sigma_max(X)^2; a I + b A + c A^2 has the largest |a + b l
+// + c l^2| over eigenvalues l in [0, sigma_max(X)^2]; and X' = p(X) has the largest
+// |a s + b s^3 + c s^5| over s in [0, sigma_max(X)].  The maxima of these polynomials on
+// an interval are taken at its ends or at a real critical point inside it.
+namespace {
+double max_abs_quad(double a, double b, double c, double L) {   // max |a + b l + c l^2|, l in [0, L]
+  auto f = [&](double l) { return std::fabs(a + b * l + c * l * l); };
+  double m = std::max(f(0.0), f(L));
+  if (c != 0.0) {
+    const double v = -b / (2.0 * c);
+    if (v > 0.0 && v < L) m = std::max(m, f(v));
+  }
+  return m;
+}
+double max_abs_odd5(double a, double b, double c, double S) {   // max |a s + b s^3 + c s^5|, s in [0, S]
+  auto g = [&](double x) { return std::fabs(x * (a + b * x * x + c * x * x * x * x)); };
+  double m = std::max(g(0.0), g(S));
+  // g'(s) = a + 3 b u + 5 c u^2 with u = s^2
+  double us[2];
+  int nu = 0;
+  if (c != 0.0) {
+    const double disc = 9.0 * b * b - 20.0 * a * c;
+    if (disc >= 0.0) {
+      const double r = std::sqrt(disc);
+      us[nu++] = (-3.0 * b + r) / (10.0 * c);
+      us[nu++] = (-3.0 * b - r) / (10.0 * c);
+    }
+  } else if (b != 0.0) {
+    us[nu++] = -a / (3.0 * b);
+  }
+  for (int i = 0; i < nu; ++i)
+    if (us[i] > 0.0 && us[i] < S * S) m = std::max(m, g(std::sqrt(us[i])));
+  return m;
+}
+// the largest e with bound * 2^e <= 224 (half the e4m3 limit), clamped to [-60, 59]
+int f8_exp_for(double bound) {
+  if (!(bound > 1e-30)) return 59;
+  const double e = std::floor(std::log2(224.0 / bound));
+  return (int)std::max(-60.0, std::min(59.0, e));
+}
+}  // namespace
+
+bool f8_exponents(double a, double b, double c, int steps, F8Exps &e) {
+  double xs = 1.0;   // bound on sigma_max(X_k)
+  for (int i = 0; i < kF8Steps; ++i) e.x[i] = e.a[i] = e.b[i] = 59;
+  const int n = std::max(steps, 1);
+  for (int k = 0; k <= n; ++k) {
+    if (!std::isfinite(xs) || xs > 1e30) return false;
+    const int i = std::min(k, kF8Steps - 1);
+    // the last slot serves every later step: keep the smallest exponent
+    e.x[i] = (int8_t)std::min<int>(e.x[i], f8_exp_for(xs));
+    if (k == n) break;
+    const double as = xs * xs;
+    e.a[i] = (int8_t)std::min<int>(e.a[i], f8_exp_for(as));
+    e.b[i] = (int8_t)std::min<int>(e.b[i], f8_exp_for(max_abs_quad(a, b, c, as)));
+    xs = max_abs_odd5(a, b, c, xs);
+  }
+  return true;
+}
+
 himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
   if (tile < 0) {
     err = "tile must be >= 1 or HIMUON_TILE_FULL (0)";
@@ -159,7 +225,10 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
   const int prec = (int)c.precision;
   const int64_t K = c.steps;
   const bool quintic = c.coeffs.c != 0.0;
-  const double split = prec == HIMUON_PREC_BF16X3 ? 3.0 : 1.0;
+  // MFMA work per product in units of one bf16 product: the split scheme issues three;
+  // BF16F8 one bf16 product and two e4m3 products at twice the rate (fused tiles of edge
+  // 64 and 128; smaller and larger tiles run the BF16X3 products)
+  const double split = prec == HIMUON_PREC_BF16X3 || prec == HIMUON_PREC_BF16F8 ? 3.0 : 1.0;
   const size_t esz = c.state_dtype == HIMUON_BF16 ? 2 : 4;
 
   std::vector<FusedTile> by_edge[3][2];   // [edge][dense]
@@ -188,7 +257,8 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
             // the symmetric products (X X^T, A^2) run on the (nb + 1) / (2 nb) share of
             // 32x32 blocks on and above the diagonal; the update on all blocks
             const double nb = e / 32.0, f = (nb + 1.0) / (2.0 * nb);
-            issued += (double)K * split * 2.0 * e * e * e * (1.0 + f * (quintic ? 2.0 : 1.0));
+            const double sp = prec == HIMUON_PREC_BF16F8 && e >= 64 ? 2.0 : split;
+            issued += (double)K * sp * 2.0 * e * e * e * (1.0 + f * (quintic ? 2.0 : 1.0));
           }
         } else {
           const GemmSizes z = gemm_sizes(h, w);

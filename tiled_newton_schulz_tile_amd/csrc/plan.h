@@ -36,6 +36,7 @@ struct Plan {
   std::vector<himuon_layer> layers;
   std::vector<LayerDesc> ldesc;
   himuon_config cfg{};
+  F8Exps f8{};                 // fp8 plane exponents (HIMUON_PREC_BF16F8)
   int32_t tile = 0;
   std::vector<FusedTile> ftiles;    // grouped by kernel edge, each group in table order
   std::vector<FusedGroup> fgroups;
