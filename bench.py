@@ -28,11 +28,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E
 METRIC = "HiMuon step ms & NS TFLOP/s (% MFMA peak) vs T, 8B-shaped stack"
 
-# HBM bytes of one launch of the T=128 fused kernel on this workload, from two
+# HBM bytes of one launch of the T=128 fused kernel (bf16f8) on this workload, from two
 # rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), scaled by the
 # readings of a 1 GiB elementwise copy (x2.0 read, x1.0 write).  Valid only for the
 # kernel source it was measured on (sha256 prefix of ns_fused.hip).
-TRAFFIC_T128 = {"source_sha256_16": "6f2c270c3c2a7de5", "fetch_kib": 27291182.1875,
+TRAFFIC_T128 = {"source_sha256_16": "d13dc34e000a2a84", "precision": "bf16f8", "fetch_kib": 27291172.3125,
                 "write_kib": 40894464.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
@@ -45,6 +45,16 @@ def measured_traffic():
     if sha != t["source_sha256_16"]:
         return None
     return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
+
+
+# name -> (library constant, dtype field, description)
+PRECISIONS = {
+    "bf16f8": ("PREC_BF16F8", "bf16+e4m3",
+               "bf16f8: operands split x = hi + lo; hi*hi on bf16 MFMA, hi*lo and lo*hi on "
+               "e4m3 MFMA with power-of-two block scales; fp32 accumulate"),
+    "bf16x3": ("PREC_BF16X3", "bf16",
+               "bf16x3: operands split hi+lo bf16, 3 MFMA products, fp32 accumulate"),
+}
 
 
 def log(*a):
@@ -242,6 +252,9 @@ def main():
     ap.add_argument("--workload", type=str, default="llama3-8b-32L")
     ap.add_argument("--inputs", choices=["power-law", "randn"], default="power-law")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--precision", choices=sorted(PRECISIONS), default="bf16f8",
+                    help="arithmetic of the NS products (bf16f8: bf16 main product, e4m3 "
+                         "correction products; bf16x3: three bf16 products)")
     ap.add_argument("--diagnostics", action="store_true",
                     help="run the matrix-function diagnostics sweep instead of the step benchmark")
     ap.add_argument("--sign", action="store_true",
@@ -268,8 +281,9 @@ def main():
     shapes = synth.STACKS[args.workload]
     K, coeffs = 5, hm.QUINTIC
     layers = build_inputs(shapes, dev, kind=args.inputs)
+    prec_const, prec_dtype, prec_text = PRECISIONS[args.precision]
     opt = hm.HiMuon(layers, args.tile, K, coeffs, beta=0.95, eps=1e-7,
-                    workspace_budget=4 * 10 ** 9, precision=hm.PREC_BF16X3)
+                    workspace_budget=4 * 10 ** 9, precision=getattr(hm, prec_const))
     st = opt.stats()
     log(f"[bench] plan: {st['tiles']} tiles, kernel tile {st['kernel_tile']}, "
         f"{st['ns_flops']:.4e} NS flops/step, workspace {st['workspace_bytes']} B")
@@ -321,8 +335,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "precision": "bf16x3: operands split hi+lo bf16, 3 MFMA products, fp32 accumulate",
+        "dtype": prec_dtype,
+        "precision": prec_text,
         "data": ("synthetic: G = U diag(1/i) V^T + 0.01 N(0,1) per matrix (Haar U, V shared per "
                  "shape), M0 = 0, W0 = 0.02 N(0,1); seeded") if args.inputs == "power-law" else
                 "synthetic: G = 0.01 N(0,1), M0 = 0, W0 = 0.02 N(0,1); seeded (counter run)",
@@ -337,9 +351,10 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic() if (args.tile == 128 and args.workload == "llama3-8b-32L")
+                     "traffic": measured_traffic() if (args.tile == 128 and args.workload == "llama3-8b-32L"
+                                                       and args.precision == TRAFFIC_T128["precision"])
                      else None,
-                     "kernel": "fused_step_kernel<128, bf16x3, bf16 state>",
+                     "kernel": f"fused_step_kernel<128, {args.precision}, bf16 state>",
                      "launches_per_step": 1, "algorithmic_flops_per_launch": st["ns_flops"],
                      "issued_flops_per_launch": st["issued_flops"],
                      "algorithmic_bytes_per_launch": st["step_bytes"]},
