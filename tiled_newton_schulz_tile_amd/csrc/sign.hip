@@ -7,8 +7,10 @@
 // the comparison x >= 0 is false for it).  Each wave takes 64 consecutive entries per
 // turn: one 4-byte load per lane, one ballot, one 8-byte store (partial at the end).
 // Vote: out[k] = scale * sign(sum_m (2 b_m[k] - 1)), a tie counting as +1.  A thread
-// takes 32 consecutive entries (one 32-bit word of every worker's buffer) and writes 32
-// outputs; the counts are kept bit-sliced (see sign_vote_kernel).  Both are HBM-bound streams.
+// takes 32 consecutive entries (one 32-bit word of every worker's buffer); the counts are
+// kept bit-sliced (see sign_vote_kernel), and a wave's 2048 results are redistributed
+// across its lanes so that every store instruction writes one contiguous run.  Both are
+// HBM-bound streams.
 
 #include <type_traits>
 
@@ -51,6 +53,64 @@ __global__ __launch_bounds__(SIGN_THREADS) void sign_pack_kernel(const float *__
         if (lane == 0) *gmem(reinterpret_cast<unsigned long long *>(bits + c * 8)) = m;
       } else if (lane < (rem + 7) / 8) {
         gmem(bits)[c * 8 + lane] = (unsigned char)(m >> (8 * lane));
+      }
+    }
+  }
+}
+
+// Bit i of an 8-bit value moved to bit 4 i of the result.
+__device__ __forceinline__ unsigned int spread4(unsigned int x) {
+  x &= 0xffu;
+  x = (x | (x << 12)) & 0x000f000fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  x = (x | (x << 3)) & 0x11111111u;
+  return x;
+}
+
+// Contiguous 16-byte aligned input: a wave takes 256 consecutive entries per turn, four
+// per lane in one 16-byte load.  Ballot e collects element e of every lane (bit l = entry
+// 4 l + e); output word k (entries 32 k .. 32 k + 31, lanes 8 k .. 8 k + 7) interleaves
+// byte k of the four ballots, and lanes 0..7 store the turn's eight words.
+__global__ __launch_bounds__(SIGN_THREADS) void sign_pack4_kernel(const float *__restrict__ o, int64_t n,
+                                                                  unsigned char *__restrict__ bits) {
+  const int lane = threadIdx.x & 63;
+  const int64_t turns = (n + 255) / 256;
+  const int64_t nbytes = (n + 7) / 8;
+  const int64_t waves = (int64_t)gridDim.x * (SIGN_THREADS / 64);
+  for (int64_t c0 = ((int64_t)blockIdx.x * (SIGN_THREADS / 64) + (threadIdx.x >> 6)) * PACK_UNROLL; c0 < turns;
+       c0 += waves * PACK_UNROLL) {
+    f32x4 v[PACK_UNROLL];
+#pragma unroll
+    for (int u = 0; u < PACK_UNROLL; ++u) {
+      const int64_t k = (c0 + u) * 256 + 4 * lane;
+      if (k + 4 <= n) {
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS f32x4 *>(gmem(o + k)));
+      } else {
+        v[u] = f32x4{-1.f, -1.f, -1.f, -1.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (k + e < n) v[u][e] = gmem(o)[k + e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PACK_UNROLL; ++u) {
+      const int64_t c = c0 + u;
+      if (c >= turns) break;   // wave-uniform
+      unsigned int word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned long long m = __ballot(v[u][e] >= 0.f);
+        word |= spread4((unsigned int)(m >> (8 * (lane & 7)))) << e;
+      }
+      const int64_t b0 = c * 32 + 4 * lane;   // first output byte of lane < 8
+      if (lane < 8) {
+        if (b0 + 4 <= nbytes) {
+          *gmem(reinterpret_cast<unsigned int *>(bits + b0)) = word;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (b0 + j < nbytes) gmem(bits)[b0 + j] = (unsigned char)(word >> (8 * j));
+        }
       }
     }
   }
@@ -110,6 +170,37 @@ __global__ __launch_bounds__(SIGN_THREADS) void sign_vote_kernel(const unsigned 
       }
     }
     const unsigned int ge = gt | eq;   // bit j: entry j wins +1
+    // Whole waves (64 full words, 2048 entries) store coalesced: store instruction q of
+    // lane l covers entries q * 64 * EPS + l * EPS .. + EPS - 1 of the wave (EPS = 16 /
+    // sizeof(OUT) per 16-byte store), whose bits sit in the word of lane (q * 64 * EPS +
+    // l * EPS) / 32, fetched with ds_bpermute.  The condition is wave-uniform.
+    const int64_t wave_w0 = w - (threadIdx.x & 63);
+    if ((wave_w0 + 64) * 32 <= n && ((reinterpret_cast<uintptr_t>(out) & 15) == 0)) {
+      constexpr int EPS = 16 / (int)sizeof(OUT);   // entries per 16-byte store: 8 or 4
+      constexpr int NQ = 2048 / (64 * EPS);        // stores per lane: 4 or 8
+      const int l = threadIdx.x & 63;
+      OUT *base = out + wave_w0 * 32;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int e0 = q * 64 * EPS + l * EPS;     // first entry (within the wave) of this store
+        const unsigned int word = (unsigned int)__builtin_amdgcn_ds_bpermute((e0 >> 5) * 4, (int)ge);
+        const unsigned int bits = word >> (e0 & 31);
+        if constexpr (sizeof(OUT) == 4) {
+          f32x4 v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = ((bits >> j) & 1u) ? scale : -scale;
+          *reinterpret_cast<GLOBAL_AS f32x4 *>(gmem(reinterpret_cast<float *>(base + e0))) = v;
+        } else {
+          float v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = ((bits >> j) & 1u) ? scale : -scale;
+          *reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(reinterpret_cast<__bf16 *>(base + e0))) =
+              u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7])};
+        }
+      }
+      continue;
+    }
     const int64_t k0 = w * 32;
     const int cnt_n = n - k0 < 32 ? (int)(n - k0) : 32;
     float v[32];
@@ -144,6 +235,11 @@ hipError_t launch_sign_pack(const float *o, int64_t rows, int64_t cols, int64_t 
                             hipStream_t stream) {
   const int64_t n = rows * cols;
   if (n == 0) return hipSuccess;
+  if (ld == cols && (reinterpret_cast<uintptr_t>(o) & 15) == 0) {
+    const int grid4 = grid_for((n + 255) / 256, (SIGN_THREADS / 64) * PACK_UNROLL);
+    hipLaunchKernelGGL(sign_pack4_kernel, dim3(grid4), dim3(SIGN_THREADS), 0, stream, o, n, bits);
+    return hipGetLastError();
+  }
   const int grid = grid_for((n + 63) / 64, (SIGN_THREADS / 64) * PACK_UNROLL);
   if (ld == cols) {
     hipLaunchKernelGGL(sign_pack_kernel<true>, dim3(grid), dim3(SIGN_THREADS), 0, stream, o, cols, ld, n, bits);
