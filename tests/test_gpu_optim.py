@@ -18,17 +18,18 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def test_optimizer_step_equals_library_step():
+@pytest.mark.parametrize("prec", [hm.PREC_BF16X3, hm.PREC_BF16F8])
+def test_optimizer_step_equals_library_step(prec):
     _need_gpu()
     shapes = [(300, 170), (128, 512), (64, 64)]
     P = [torch.nn.Parameter(synth.weights(h, w, 10 + i, "cuda")) for i, (h, w) in enumerate(shapes)]
     W_ref = [p.detach().clone() for p in P]
     grads = [synth.power_law_matrix(h, w, 20 + i, device="cuda", dtype=torch.float32)
              for i, (h, w) in enumerate(shapes)]
-    opt = HiMuonOptimizer(P, lr=0.02, tile=64)
+    opt = HiMuonOptimizer(P, lr=0.02, tile=64, precision=prec)
     M_ref = [torch.zeros(h, w, dtype=torch.bfloat16, device="cuda") for h, w in shapes]
     G_ref = [torch.zeros_like(m) for m in M_ref]
-    ref = hm.HiMuon(list(zip(W_ref, M_ref, G_ref)), 64, 5, hm.QUINTIC, precision=hm.PREC_BF16X3)
+    ref = hm.HiMuon(list(zip(W_ref, M_ref, G_ref)), 64, 5, hm.QUINTIC, precision=prec)
     for step in range(3):
         for p, g, gr in zip(P, grads, G_ref):
             p.grad = (1.0 + step) * g
