@@ -920,6 +920,10 @@ template <int TS, int NT, typename S>
 struct TileRegs {
   static constexpr int CPR = TS / 8, GM_IT = TS * CPR / NT;
   static constexpr int WPR = TS / 4, W_IT = TS * WPR / NT;
+  // a thread's chunks lie NT / CPR (resp. NT / WPR) rows apart in one column position,
+  // so dense tiles address them from one row pointer and a uniform row stride
+  static_assert(NT % CPR == 0 && NT % WPR == 0, "whole rows per pass");
+  static constexpr int GM_ROWS = NT / CPR, W_ROWS = NT / WPR;
   Chunk8<S> g[GM_IT], m[GM_IT];
   f32x4 w[W_IT];
 
@@ -931,13 +935,15 @@ struct TileRegs {
     const S *mb = reinterpret_cast<const S *>(L.m);
     const S *gb = reinterpret_cast<const S *>(L.g);
     if constexpr (DENSE) {
+      const int64_t r0 = t.row0 + gt / CPR;
+      const int c = (gt % CPR) * 8;
+      const S *gp = gb + r0 * L.ld_g + t.col0 + c;
+      const S *mp = mb + r0 * L.ld_m + t.col0 + c;
+      const int64_t sg = (int64_t)GM_ROWS * L.ld_g, sm = (int64_t)GM_ROWS * L.ld_m;
 #pragma unroll
       for (int i = 0; i < GM_IT; ++i) {
-        const int q = gt + i * NT;
-        const int r = q / CPR, c = (q % CPR) * 8;
-        const int64_t gr = (int64_t)(t.row0 + r);
-        g[i] = load_chunk_vec<S>(gb + gr * L.ld_g + t.col0 + c);
-        m[i] = load_chunk_vec<S>(mb + gr * L.ld_m + t.col0 + c);
+        g[i] = load_chunk_vec<S>(gp + i * sg);
+        m[i] = load_chunk_vec<S>(mp + i * sm);
       }
       return;
     }
@@ -956,13 +962,11 @@ struct TileRegs {
   template <bool DENSE>
   __device__ __forceinline__ void load_w(TileView t, const LayerView &L, int gt) {
     if constexpr (DENSE) {
+      const float *wp = L.w + (int64_t)(t.row0 + gt / WPR) * L.ld_w + t.col0 + (gt % WPR) * 4;
+      const int64_t sw = (int64_t)W_ROWS * L.ld_w;
 #pragma unroll
-      for (int i = 0; i < W_IT; ++i) {
-        const int q = gt + i * NT;
-        const int r = q / WPR, c = (q % WPR) * 4;
-        const float *src = L.w + (int64_t)(t.row0 + r) * L.ld_w + t.col0 + c;
-        w[i] = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4 *>(src)));
-      }
+      for (int i = 0; i < W_IT; ++i)
+        w[i] = __builtin_nontemporal_load(gmem(reinterpret_cast<const f32x4 *>(wp + i * sw)));
       return;
     }
     const bool vec = L.vec_w && (t.col0 % 4 == 0);
@@ -989,12 +993,12 @@ struct TileRegs {
   __device__ __forceinline__ float momentum_dense(TileView t, const LayerView &L, int gt, float beta,
                                                   float (&v)[GM_IT][8]) const {
     S *mb = reinterpret_cast<S *>(L.m);
+    S *mp = mb + (int64_t)(t.row0 + gt / CPR) * L.ld_m + t.col0 + (gt % CPR) * 8;
+    const int64_t sm = (int64_t)GM_ROWS * L.ld_m;
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < GM_IT; ++i) {
-      const int q = gt + i * NT;
-      const int r = q / CPR, c = (q % CPR) * 8;
-      S *dst = mb + (int64_t)(t.row0 + r) * L.ld_m + t.col0 + c;
+      S *dst = mp + i * sm;
       if constexpr (sizeof(S) == 2) {
         unsigned code[4];
 #pragma unroll
@@ -1099,7 +1103,11 @@ struct TileRegs {
       float nw[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) nw[e] = __builtin_fmaf(nlr, o[e], w[i][e]);
-      GLOBAL_AS float *dst = gmem(L.w + (int64_t)(t.row0 + r) * L.ld_w + t.col0 + c);
+      // (dense tiles: one row pointer and a uniform stride, as in load_w)
+      GLOBAL_AS float *dst =
+          DENSE ? gmem(L.w + (int64_t)(t.row0 + gt / WPR) * L.ld_w + t.col0 + (gt % WPR) * 4 +
+                       i * ((int64_t)W_ROWS * L.ld_w))
+                : gmem(L.w + (int64_t)(t.row0 + r) * L.ld_w + t.col0 + c);
       if (vec && n == 4) {
         *reinterpret_cast<GLOBAL_AS f32x4 *>(dst) = f32x4{nw[0], nw[1], nw[2], nw[3]};
       } else {
@@ -1108,7 +1116,10 @@ struct TileRegs {
           if (e < n) dst[e] = nw[e];
       }
       if (write_u) {
-        GLOBAL_AS float *ud = gmem(L.u + (int64_t)(t.row0 + r) * L.ld_u + t.col0 + c);
+        GLOBAL_AS float *ud =
+            DENSE ? gmem(L.u + (int64_t)(t.row0 + gt / WPR) * L.ld_u + t.col0 + (gt % WPR) * 4 +
+                         i * ((int64_t)W_ROWS * L.ld_u))
+                  : gmem(L.u + (int64_t)(t.row0 + r) * L.ld_u + t.col0 + c);
         if (vec && n == 4) {
           *reinterpret_cast<GLOBAL_AS f32x4 *>(ud) = f32x4{o[0], o[1], o[2], o[3]};
         } else {
