@@ -81,8 +81,11 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // four floats divided by d (a power of two) and rounded to e4m3 (nearest even), a in
 // the lowest byte: two v_cvt_scalef32_pk_fp8_f32, which compute e4m3(x / d)
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+// (the first conversion writes the low half and keeps the high one, which the second
+// overwrites, so the initial value is immaterial: a's bits, whose register is often
+// free by then, rather than a cleared register)
 __device__ __forceinline__ unsigned pack_fp8x4(float a, float b, float c, float d, float div) {
-  s16x2 w = {0, 0};
+  s16x2 w = __builtin_bit_cast(s16x2, a);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, a, b, div, false);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, c, d, div, true);
   return __builtin_bit_cast(unsigned, w);

@@ -365,7 +365,8 @@ struct HiPiece {  // bf16 hi of each side, one 32-k half chunk (two 16-k pieces)
 
 // The e4m3 operands of one correction product: L from plane lp (rows, or columns when
 // TRANS_L), R from plane rp, k in [kb, kb + 64).  An aliased R block is read again here.
-template <int TS, bool TRANS_L, int NB>
+// B0: the first L block is not read (the caller supplies it).
+template <int TS, bool TRANS_L, int NB, bool READ_R = true, int B0 = 0>
 __device__ __forceinline__ void load_f8(F8Half<TS> &f, const unsigned char *lp, int l0, const unsigned char *rp,
                                         int r0, int lane, int kb) {
   using G = Geo<TS, PREC_BF16F8>;
@@ -382,10 +383,12 @@ __device__ __forceinline__ void load_f8(F8Half<TS> &f, const unsigned char *lp, 
     const i32x4 b = *reinterpret_cast<const i32x4 *>(plane + r * G::P8 + ko1);
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   };
+  if constexpr (READ_R) {
 #pragma unroll
-  for (int b = 0; b < G::NJ; ++b) f.r[b] = prow(rp, r0 + b * 32 + li);
+    for (int b = 0; b < G::NJ; ++b) f.r[b] = prow(rp, r0 + b * 32 + li);
+  }
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
+  for (int b = B0; b < NB; ++b) {
     if constexpr (TRANS_L) {
       f.l[b] = tr8_frag_g<G>(lp, kb, l0 + b * 32, lane);
     } else {
@@ -424,14 +427,19 @@ __device__ __forceinline__ void load_hi(HiPiece<TS> &h, const Mat<PREC_BF16F8> &
 
 // Scheduler directives for the stage sequence: stage i's MFMAs, each followed by some
 // of stage i + 1's reads.  Stage kinds: 0, 1 the correction products, 2, 3 the halves.
-template <int ST, int NST, int NMF, int NRF, int NMH, int NRH>
+// NRF / NRB: reads of the first / second correction stage, NRH: of a half.
+template <int ST, int NST, int NMF, int NRF, int NRB, int NMH, int NRH>
 __device__ __forceinline__ void sched_f8() {
   constexpr int kind = ST % 4, next = (ST + 1) % 4;
   constexpr int NM = kind < 2 ? NMF : NMH;
   if constexpr (ST + 1 < NST) {
-    constexpr int NR = next < 2 ? NRF : NRH;
-    sched_mfma_reads<NM, NR, (NR + NM - 1) / NM>();
-    sched_f8<ST + 1, NST, NMF, NRF, NMH, NRH>();
+    constexpr int NR = next == 0 ? NRF : next == 1 ? NRB : NRH;
+    if constexpr (NR > 0) {
+      sched_mfma_reads<NM, NR, (NR + NM - 1) / NM>();
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    }
+    sched_f8<ST + 1, NST, NMF, NRF, NRB, NMH, NRH>();
   } else {
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
   }
@@ -447,7 +455,11 @@ __device__ __forceinline__ void wave_gemm_f8(Acc<Geo<TS, PREC_BF16F8>::NI, Geo<T
   constexpr int NJ = G::NJ;
   static_assert(TS % 64 == 0, "e4m3 products run on 64-k chunks");
   constexpr int NC = TS / 64;
+  // RALIAS: the R block is L's first block, so the second correction stage's operands
+  // l8_L[0] and h8_R are the first stage's l8_R and h8_L[0], kept in registers
+  static_assert(!RALIAS || !TRANS_L, "aliased operands are plain rows");
   constexpr int NRF = NB * (TRANS_L ? 4 : 2) + 2 * NJ;            // reads of one correction stage
+  constexpr int NRB = RALIAS ? 2 * (NB - 1) : NRF;                 // of the second one
   constexpr int NRH = 2 * (NB * (TRANS_L ? 2 : 1) + (RALIAS ? 0 : NJ));  // reads of one half
   constexpr int NMF = NB * NJ, NMH = 2 * NB * NJ;
   F8Half<TS> fa, fb;
@@ -457,7 +469,13 @@ __device__ __forceinline__ void wave_gemm_f8(Acc<Geo<TS, PREC_BF16F8>::NI, Geo<T
   for (int c = 0; c < NC; ++c) {
     const int kb = 64 * c;
     // h8_L l8_R (small terms first)
-    load_f8<TS, TRANS_L, NB>(fb, Lm.l8, l0, Rm.h8, r0, lane, kb);
+    if constexpr (RALIAS) {
+      load_f8<TS, TRANS_L, NB, false, 1>(fb, Lm.l8, l0, Rm.h8, r0, lane, kb);
+      fb.l[0] = fa.r[0];
+      fb.r[0] = fa.l[0];
+    } else {
+      load_f8<TS, TRANS_L, NB>(fb, Lm.l8, l0, Rm.h8, r0, lane, kb);
+    }
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
@@ -487,7 +505,7 @@ __device__ __forceinline__ void wave_gemm_f8(Acc<Geo<TS, PREC_BF16F8>::NI, Geo<T
   }
   if constexpr (SCHED_GEMM) {
     __builtin_amdgcn_sched_group_barrier(0x100, NRF, 0);
-    sched_f8<0, 4 * NC, NMF, NRF, NMH, NRH>();
+    sched_f8<0, 4 * NC, NMF, NRF, NRB, NMH, NRH>();
   }
 }
 
@@ -660,19 +678,43 @@ __device__ __forceinline__ F8S f8s_of(int e) { return F8S{pow2i(-e), pow2i(-e - 
 // precision's format.  SCALE: the stored value is s_store * acc; BACK: afterwards acc <-
 // s_back * acc (one pass over the accumulators serves both).  MIRROR (symmetric
 // results): blocks off the diagonal are also stored untransposed, at [row][col].
-// DIAG: diag is added to the stored diagonal elements.  f8: the e4m3 planes' multipliers.
+// DIAG: diag is added to the stored diagonal elements; the scaling and the addition are
+// then applied to acc in place (it is left holding the stored values, and BACK must be
+// off).  f8: the e4m3 planes' multipliers.
 template <int TS, int PREC, bool SCALE = false, bool BACK = false, int NB = Geo<TS, PREC>::NI, bool MIRROR = false,
           bool DIAG = false>
 __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &m, int p0, int q0,
                                             int lane, float s_store = 1.f, float s_back = 1.f, F8S f8 = F8S{},
                                             float diag = 0.f) {
   using G = Geo<TS, PREC>;
+  static_assert(!(DIAG && BACK), "DIAG rewrites the accumulators");
   const int li = lane & 31, half = lane >> 5;
+  if constexpr (DIAG) {
+    // Only blocks on the diagonal (a wave-uniform test, so a branch) pay for the lane
+    // test; element (g, e) of this lane sits on the diagonal iff li - 4 half == 8 g + e.
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < G::NJ; ++bj) {
+        if (p0 + bi * 32 == q0 + bj * 32) {
+          int dk = li - 4 * half;
+          asm volatile("" : "+v"(dk));   // formed here, not hoisted as sixteen lane masks
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const float x = acc.b[bi][bj][k];
+            acc.b[bi][bj][k] = __builtin_fmaf(SCALE ? s_store : 1.f, x, dk == 8 * (k / 4) + k % 4 ? diag : 0.f);
+          }
+        } else if constexpr (SCALE) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) acc.b[bi][bj][k] *= s_store;
+        }
+      }
+  }
+  constexpr bool SC = SCALE && !DIAG;   // scaling still to apply while storing
 #pragma unroll
   for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
     for (int bj = 0; bj < G::NJ; ++bj) {
-      const bool on_diag = DIAG && p0 + bi * 32 == q0 + bj * 32;   // wave-uniform
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int row = p0 + bi * 32 + 8 * g + 4 * half;
@@ -681,10 +723,7 @@ __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x = acc.b[bi][bj][4 * g + e];
-          v[e] = SCALE ? x * s_store : x;
-          if constexpr (DIAG) {
-            if (on_diag && li == 8 * g + 4 * half + e) v[e] += diag;
-          }
+          v[e] = SC ? x * s_store : x;
           if constexpr (BACK) acc.b[bi][bj][4 * g + e] = x * s_back;
         }
         if constexpr (PREC == PREC_BF16F8) {
