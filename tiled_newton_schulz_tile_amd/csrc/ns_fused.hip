@@ -1338,22 +1338,49 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     if constexpr (F8) fs.init(prm.f8);
     // The symmetric part of a step, on the wave's job: B (with a on its diagonal when
     // folded) ends up in AB.
-    auto sym_part = [&]() {
+    // On full TS x TS tiles PREC_BF16F8 runs the first steps partly in plain bf16 (hi
+    // operands only): the Gram product of step 0, and the square product of steps 0 and 1
+    // with A stored as its hi plane alone.  While the singular values of X are still
+    // small the A^2 term is small against a I + b A, and the rounding error of an r x r
+    // Gram matrix is spread over r directions, so these roundings cost no accuracy at
+    // r = 64 or 128; once the singular values saturate (from step 2 on), and on thin
+    // ragged tiles (few large singular values), every product takes the correction terms.
+    // (128-tiles keep the square product split: its plain variant costs registers that
+    // the 128-tile code does not have, and spilling them slows the whole tile loop)
+    constexpr int PLAIN_GRAM_STEPS = 1, PLAIN_SQUARE_STEPS = TS == 128 ? 0 : 2;
+    const bool full = DENSE || (t.h == TS && t.w == TS);         // wave-uniform
+    auto sym_part = [&](int it) {
       const int ex = fs.x(), ea = fs.a(), eb = fs.b();
+      const bool pg = F8 && full && it < PLAIN_GRAM_STEPS;      // wave-uniform
+      const bool pa = F8 && full && it < PLAIN_SQUARE_STEPS && cc != 0.f;
       Acc<NI, NJ> acc;
       with_job<TS>(jb, [&](auto NBC, auto ALC) {
         constexpr int NB = decltype(NBC)::value;
         constexpr bool AL = decltype(ALC)::value;
-        wave_gemm<TS, PREC, false, true, NB, AL>(acc, X, jb.p0, X, jb.q0, lane, 127 - (2 * ex + 8));   // A = X X^T
-        if (cc != 0.f) {
-          // B = b A + c A^2 = c ((b/c) A + A A^T): accumulate A A^T onto (b/c) A
-          store_acc_t<TS, PREC, false, true, NB, true>(acc, AB, jb.p0, jb.q0, lane, 1.f, cb / cc, f8s_of(ea));
-        } else if constexpr (F8) {
-          // B + a I = b A + a I
-          store_acc_t<TS, PREC, true, false, NB, true, true>(acc, AB, jb.p0, jb.q0, lane, cb, 1.f, f8s_of(eb), ca);
+        if constexpr (F8) {
+          const Mat<PREC_BF16> Xh{X.hi}, ABh{AB.hi};
+          if (pg) {
+            wave_gemm_std<TS, PREC_BF16, false, true, NB, AL>(acc, Xh, jb.p0, Xh, jb.q0, lane);   // A = X X^T
+          } else {
+            wave_gemm<TS, PREC, false, true, NB, AL>(acc, X, jb.p0, X, jb.q0, lane, 127 - (2 * ex + 8));
+          }
+          if (cc == 0.f) {
+            // B + a I = b A + a I
+            store_acc_t<TS, PREC, true, false, NB, true, true>(acc, AB, jb.p0, jb.q0, lane, cb, 1.f, f8s_of(eb), ca);
+          } else if (pa) {
+            store_acc_t<TS, PREC_BF16, false, true, NB, true>(acc, ABh, jb.p0, jb.q0, lane, 1.f, cb / cc);
+          } else {
+            store_acc_t<TS, PREC, false, true, NB, true>(acc, AB, jb.p0, jb.q0, lane, 1.f, cb / cc, f8s_of(ea));
+          }
         } else {
-          store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cb);   // B = b A
-          if constexpr (FOLD_A) add_diag<TS, PREC, NB>(AB, jb.p0, jb.q0, lane, ca);       // B + a I
+          wave_gemm<TS, PREC, false, true, NB, AL>(acc, X, jb.p0, X, jb.q0, lane);   // A = X X^T
+          if (cc != 0.f) {
+            // B = b A + c A^2 = c ((b/c) A + A A^T): accumulate A A^T onto (b/c) A
+            store_acc_t<TS, PREC, false, true, NB, true>(acc, AB, jb.p0, jb.q0, lane, 1.f, cb / cc);
+          } else {
+            store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cb);   // B = b A
+            if constexpr (FOLD_A) add_diag<TS, PREC, NB>(AB, jb.p0, jb.q0, lane, ca);       // B + a I
+          }
         }
       });
       if (cc != 0.f) {
@@ -1361,7 +1388,16 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
         with_job<TS>(jb, [&](auto NBC, auto ALC) {
           constexpr int NB = decltype(NBC)::value;
           constexpr bool AL = decltype(ALC)::value;
-          wave_gemm<TS, PREC, false, false, NB, AL>(acc, AB, jb.p0, AB, jb.q0, lane, 127 - (2 * ea + 8));
+          if constexpr (F8) {
+            const Mat<PREC_BF16> ABh{AB.hi};
+            if (pa) {
+              wave_gemm_std<TS, PREC_BF16, false, false, NB, AL>(acc, ABh, jb.p0, ABh, jb.q0, lane);
+            } else {
+              wave_gemm<TS, PREC, false, false, NB, AL>(acc, AB, jb.p0, AB, jb.q0, lane, 127 - (2 * ea + 8));
+            }
+          } else {
+            wave_gemm<TS, PREC, false, false, NB, AL>(acc, AB, jb.p0, AB, jb.q0, lane);
+          }
         });
         tile_sync<G::WPT>();                                             // A fully read
         with_job<TS>(jb, [&](auto NBC, auto) {
@@ -1377,7 +1413,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     };
     if constexpr (F8) {
       for (int it = 0; it < prm.steps; ++it) {
-        sym_part();
+        sym_part(it);
         const int sxb = 127 - (fs.x() + fs.b() + 8);
         tile_sync<G::WPT>();
         if (it + 1 == prm.steps) {
@@ -1394,7 +1430,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
       }
     } else if (prm.steps > 0) {
       for (int it = 0;; ++it) {
-        sym_part();
+        sym_part(it);
         if constexpr (!FOLD_A) {
 #pragma unroll
           for (int bi = 0; bi < NI; ++bi)
