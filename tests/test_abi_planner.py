@@ -104,8 +104,20 @@ def test_bf16f8_issues_one_bf16_and_two_half_rate_products():
     hm.himuon_plan_destroy(p)
     assert st["ns_flops"] == 6 * 6979321856 * 128 * 5
     # hi*hi in bf16 plus two e4m3 products at twice the rate: 2 bf16-product units per
-    # product, on 10 of 16 blocks for the symmetric ones: 2 * (2 * 10/16 + 1) / 3 = 1.5x
-    assert st["issued_flops"] == 1.5 * st["ns_flops"]
+    # product (units of 2 T^3 flops), on 10 of 16 blocks for the symmetric ones; on full
+    # 128-tiles the Gram product of step 0 is plain bf16 (1 unit):
+    #   step 0: 10/16 * 1 + 10/16 * 2 + 2 = 3.875, steps 1..4: 10/16 * 2 * 2 + 2 = 4.5
+    assert st["issued_flops"] == (3.875 + 4 * 4.5) * 2 * 128 ** 3 * 425984
+    # full 64-tiles: plain Gram in step 0 and plain square in steps 0 and 1 (3 of 4 blocks)
+    p = plan_for(synth.STACKS["llama3-8b-32L"], 64, precision=hm.PREC_BF16F8)
+    st64 = hm.himuon_plan_stats(p)
+    hm.himuon_plan_destroy(p)
+    assert st64["issued_flops"] == (3.5 + 4.25 + 3 * 5.0) * 2 * 64 ** 3 * (6979321856 // 64 ** 2)
+    # ragged tiles take every correction product: 2 units per product in every step
+    p = plan_for([(100, 200)], 128, precision=hm.PREC_BF16F8)
+    str_ = hm.himuon_plan_stats(p)
+    hm.himuon_plan_destroy(p)
+    assert str_["issued_flops"] == 2 * 5 * (2 * 10 / 16 * 2 + 2) * 2 * 128 ** 3
     # edge-32 tiles run the bf16x3 products
     p = plan_for([(256, 512)], 32, precision=hm.PREC_BF16F8)
     st32 = hm.himuon_plan_stats(p)

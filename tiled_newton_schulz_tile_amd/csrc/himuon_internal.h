@@ -70,6 +70,13 @@ struct F8Exps {
   int8_t b[kF8Steps];   // a I + b A_k + c A_k^2, the update's operand
 };
 
+// PREC_BF16F8 on full e x e tiles of the fused kernel: the Gram product of the first
+// kF8PlainGramSteps NS steps, and the square product of the first
+// f8_plain_square_steps(e) steps (with A stored as its bf16 plane alone), take the bf16
+// operands only.
+constexpr int kF8PlainGramSteps = 1;
+constexpr int f8_plain_square_steps(int edge) { return edge == 128 ? 0 : 2; }
+
 struct NSParams {
   float a, b, c;
   float beta, eps, lr;

@@ -1347,7 +1347,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     // ragged tiles (few large singular values), every product takes the correction terms.
     // (128-tiles keep the square product split: its plain variant costs registers that
     // the 128-tile code does not have, and spilling them slows the whole tile loop)
-    constexpr int PLAIN_GRAM_STEPS = 1, PLAIN_SQUARE_STEPS = TS == 128 ? 0 : 2;
+    constexpr int PLAIN_GRAM_STEPS = kF8PlainGramSteps, PLAIN_SQUARE_STEPS = f8_plain_square_steps(TS);
     const bool full = DENSE || (t.h == TS && t.w == TS);         // wave-uniform
     auto sym_part = [&](int it) {
       const int ex = fs.x(), ea = fs.a(), eb = fs.b();

@@ -255,10 +255,20 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
               FusedTile{(int32_t)li, (int32_t)r0, (int32_t)c0, (int16_t)h, (int16_t)w});
           {
             // the symmetric products (X X^T, A^2) run on the (nb + 1) / (2 nb) share of
-            // 32x32 blocks on and above the diagonal; the update on all blocks
+            // 32x32 blocks on and above the diagonal; the update on all blocks.  bf16f8
+            // issues two bf16-product units per product, one for the plain products of
+            // the first steps on full tiles.
             const double nb = e / 32.0, f = (nb + 1.0) / (2.0 * nb);
-            const double sp = prec == HIMUON_PREC_BF16F8 && e >= 64 ? 2.0 : split;
-            issued += (double)K * sp * 2.0 * e * e * e * (1.0 + f * (quintic ? 2.0 : 1.0));
+            if (prec == HIMUON_PREC_BF16F8 && e >= 64) {
+              const bool full = h == e && w == e;
+              const int pg = full ? kF8PlainGramSteps : 0, ps = full ? f8_plain_square_steps(e) : 0;
+              for (int k = 0; k < K; ++k) {
+                const double units = f * (k < pg ? 1.0 : 2.0) + (quintic ? f * (k < ps ? 1.0 : 2.0) : 0.0) + 2.0;
+                issued += 2.0 * e * e * e * units;
+              }
+            } else {
+              issued += (double)K * split * 2.0 * e * e * e * (1.0 + f * (quintic ? 2.0 : 1.0));
+            }
           }
         } else {
           const GemmSizes z = gemm_sizes(h, w);
