@@ -113,6 +113,52 @@ def test_gpt2_layer_bf16f8(T, coeffs):
         assert_bar(U, O, hm.PREC_BF16F8, tight=5e-3)
 
 
+def structured_tiles(T, seed):
+    """One T x 4T matrix of four full tiles with concentrated spectra: rank 1, rank 4
+    (singular values 1, 0.8, 0.6, 0.5), an orthogonal matrix, and singular values 1/i^2."""
+    g = torch.Generator().manual_seed(seed)
+
+    def haar(n, k):
+        q, r = torch.linalg.qr(torch.randn(n, k, dtype=torch.float64, generator=g))
+        return q * torch.sign(torch.diagonal(r))
+
+    U, V = haar(T, 4), haar(T, 4)
+    rank1 = U[:, :1] @ V[:, :1].T
+    rank4 = U @ torch.diag(torch.tensor([1.0, 0.8, 0.6, 0.5], dtype=torch.float64)) @ V.T
+    orth = haar(T, T)
+    decay = haar(T, T) @ torch.diag(1.0 / torch.arange(1, T + 1, dtype=torch.float64) ** 2) @ haar(T, T).T
+    return torch.cat([rank1, rank4, orth, decay], dim=1).float()
+
+
+@pytest.mark.parametrize("T", [64, 128])
+@pytest.mark.parametrize("coeffs", [Q, C])
+def test_structured_spectra(T, coeffs):
+    # Full tiles whose singular values are large from the start (rank 1, rank 4,
+    # orthogonal, 1/i^2).  The quintic map grows rounding noise in the empty directions
+    # of a low-rank tile by about a = 3.4 per step, so there the error is set by the
+    # precision of the update's X operand: bf16x3 (hi + lo bf16, about 2^-17) stays far
+    # inside the bar on every tile; bf16f8 (e4m3 corrections, about 2^-13) stays inside it
+    # on the orthogonal and 1/i^2 tiles and in max-abs everywhere, but its relative
+    # Frobenius error on the exactly low-rank tiles (rank 1, rank 4) is 1.5-1.8e-2 with
+    # quintic K = 5, outside the 1e-2 bar.  That is a property of the e4m3 corrections,
+    # not of the plain early steps (the same figures with and without them); bf16x3 is
+    # the scheme for such inputs.
+    G = structured_tiles(T, 500 + T)
+    for prec in (hm.PREC_BF16X3, hm.PREC_BF16F8):
+        (res,), _ = gpu_step([G], T, K=5, coeffs=coeffs, prec=prec)
+        W, M, U = res[0]
+        O = oracle.tiled_ns(M.double().numpy(), T, 5, coeffs)
+        for j in range(4):
+            Uj, Oj = U[:, j * T:(j + 1) * T], O[:, j * T:(j + 1) * T]
+            if prec == hm.PREC_BF16X3:
+                assert_bar(Uj, Oj, prec, tight=2e-3)
+            elif j >= 2 or coeffs == C:
+                assert_bar(Uj, Oj, prec, tight=5e-3)
+            else:
+                mx, rf = errs(Uj, Oj)
+                assert mx <= 2e-2 and rf <= 2.5e-2, (j, mx, rf)
+
+
 @pytest.mark.parametrize("T", [64, 128])
 @pytest.mark.parametrize("coeffs,K", [(C, 20), ((2.0, -1.5, 0.5), 6), ((1.875, -1.25, 0.375), 8)])
 def test_bf16f8_long_runs_and_other_coefficients(T, coeffs, K):
