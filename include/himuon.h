@@ -70,8 +70,14 @@ typedef enum {
                              MFMA time; each fp8 operand carries a power-of-two scale
                              chosen at plan time from bounds on the iterates.  Fused tiles
                              of edge 64 and 128 run it; smaller tiles and the large-tile
-                             path run HIMUON_PREC_BF16X3.  himuon_plan returns
-                             HIMUON_EINVAL if the coefficients' iterates are unbounded. */
+                             path run HIMUON_PREC_BF16X3.  On tiles that fill 64 x 64 or
+                             128 x 128, the Gram product of NS step 0 (and at edge 64 the
+                             square product of steps 0 and 1) uses the bf16 hi operands
+                             alone.  Its relative error on exactly low-rank tiles can
+                             exceed 1e-2 (the quintic map grows the e4m3 rounding noise in
+                             their empty directions); HIMUON_PREC_BF16X3 does not.
+                             himuon_plan returns HIMUON_EINVAL if the coefficients'
+                             iterates are unbounded.                                     */
 } himuon_precision;
 
 #define HIMUON_TILE_FULL 0            /* one tile per matrix: full-matrix Muon        */
