@@ -56,6 +56,11 @@ struct GemmWork {
 
 // Elements per momentum block of the GEMM path.
 constexpr int kGemmMomentumBlock = 8192;
+// GEMM products whose K (the padded short and long side of every tile in a chunk) is at
+// least this long stream K slices of 64 elements (whole 128-byte lines of bf16 rows)
+// through one LDS stage; shorter ones use slices of 32 through two stages, which hides
+// more latency when a block has only a few slices.
+constexpr int64_t kGemmLongK = 1024;
 
 enum Prec : int { PREC_F32 = 0, PREC_BF16 = 1, PREC_BF16X3 = 2, PREC_BF16F8 = 3 };
 
@@ -110,6 +115,7 @@ struct GemmChunkLaunch {
   const GemmWork *sym;  int64_t n_sym; // (tile, bi <= bj): 128-blocks of r x r
   const GemmWork *upd;  int64_t n_upd; // (tile, bi, bj): 128-blocks of r x s
   const GemmWork *app;  int64_t n_app; // (tile, bi, bj): 64-blocks of the h x w tile
+  int32_t long_k;                       // K slices of 64 (one LDS stage) instead of 32 (two)
 };
 // Runs one full step for the tiles of a chunk: momentum and partial norms, norm
 // reduction, staging of X0, K Newton-Schulz steps as grouped MFMA GEMMs, update.

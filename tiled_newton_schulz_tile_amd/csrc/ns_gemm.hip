@@ -14,8 +14,11 @@
 //                B = b A + c A A^T   (symmetric, epilogue adds b A; skipped when c = 0)
 //                X <- (a I + B) X    (a on B's diagonal; plain bf16 adds a X in fp32)
 //   apply        W <- W - lr O, O reoriented (LDS transpose for tall tiles)
-// GEMM blocks are 128 x 128 with K steps of 32 staged through LDS (register
-// double buffering); four waves each own a 64 x 64 block (2 x 2 MFMA 32x32 tiles).
+// GEMM blocks are 128 x 128; K slices of 32 (two LDS stages) or, when every K of a chunk
+// is long, of 64 (one stage) are staged through LDS from registers loaded one slice
+// ahead; four waves each own a 64 x 64 block (2 x 2 MFMA 32x32 tiles).
+#include <type_traits>
+
 #include "device_common.h"
 #include "himuon_internal.h"
 
@@ -24,7 +27,7 @@ namespace {
 
 using namespace dev;
 
-constexpr int BM = 128, BK = 32;
+constexpr int BM = 128;
 constexpr int THREADS = 256;
 
 enum Mode : int { MODE_GRAM = 0, MODE_SQUARE = 1, MODE_UPDATE = 2 };
@@ -388,7 +391,8 @@ __device__ __forceinline__ int xcd_work_index() {
 
 // LDS tile of one operand for one K step, per plane: [rows][BK + pad] (row operand) or
 // [BK][BM + pad] (column operand of the update, read with ds_read_tr).
-template <int PREC>
+// BK: the K slice (32: two LDS stages; 64: one stage).
+template <int PREC, int BK>
 struct GemmLds {
   static constexpr bool F32 = PREC == PREC_F32;
   static constexpr int NPL = PREC == PREC_BF16X3 ? 2 : 1;     // planes staged
@@ -399,119 +403,88 @@ struct GemmLds {
   static constexpr int COLT = BK * CP * ES;                   // one plane of a column tile
   static constexpr int STAGE = NPL * (ROWT + (ROWT > COLT ? ROWT : COLT));
   static constexpr int SP = BM + 4;                           // fp32 staging pitch
-  static constexpr int BYTES = 2 * STAGE > BM * SP * 4 ? 2 * STAGE : BM * SP * 4;
+  static constexpr int NSTAGE = BK == 32 ? 2 : 1;
+  static constexpr int BYTES = NSTAGE * STAGE > BM * SP * 4 ? NSTAGE * STAGE : BM * SP * 4;
+  static constexpr int CPR = BK * ES / 16;       // 16-byte chunks per row of a row tile
+  static constexpr int CPC = BM * ES / 16;       //                per k row of a column tile
+  static constexpr int NQ = BM * CPR / THREADS;  // chunks per thread, per plane and operand
+  static_assert(BM * CPR % THREADS == 0 && BK * CPC == BM * CPR, "whole chunks per thread");
 };
 
 // Per-thread registers of one K step's global loads (both operands, all planes).
-template <int PREC>
+template <int PREC, int BK>
 struct KRegs {
-  static constexpr int N = PREC == PREC_F32 ? 4 : (PREC == PREC_BF16X3 ? 4 : 2);
+  static constexpr int N = GemmLds<PREC, BK>::NPL * GemmLds<PREC, BK>::NQ;
   u32x4 l[N], r[N];
 };
 
-template <int PREC, int MODE>
-__device__ __forceinline__ void gemm_load(KRegs<PREC> &kr, const Planes<PREC> &Lp, int i0,
+template <int PREC, int MODE, int BK>
+__device__ __forceinline__ void gemm_load(KRegs<PREC, BK> &kr, const Planes<PREC> &Lp, int i0,
                                           const Planes<PREC> &Rp, int j0, int kb) {
+  using LD = GemmLds<PREC, BK>;
   const int tid = threadIdx.x;
-  if constexpr (PREC == PREC_F32) {
+  constexpr int EPC = 16 / LD::ES;   // elements per 16-byte chunk
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+  for (int pl = 0; pl < LD::NPL; ++pl) {
+    const char *lb = PREC == PREC_F32 ? reinterpret_cast<const char *>(Lp.f())
+                                      : reinterpret_cast<const char *>(pl ? Lp.lo() : Lp.hi());
+    const char *rb = PREC == PREC_F32 ? reinterpret_cast<const char *>(Rp.f())
+                                      : reinterpret_cast<const char *>(pl ? Rp.lo() : Rp.hi());
+#pragma unroll
+    for (int q = 0; q < LD::NQ; ++q) {
       const int idx = tid + q * THREADS;
-      const int row = idx >> 3, ch = idx & 7;       // 128 rows x 8 chunks of 4 floats
+      const int row = idx / LD::CPR, ch = idx % LD::CPR;   // BM rows x CPR chunks
       const int gi = i0 + row;
-      kr.l[q] = gi < Lp.rows ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
-                                   gmem(Lp.f() + (int64_t)gi * Lp.ld + kb + ch * 4)))
-                             : u32x4{0, 0, 0, 0};
+      kr.l[pl * LD::NQ + q] =
+          gi < Lp.rows ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
+                             gmem(lb + ((int64_t)gi * Lp.ld + kb + ch * EPC) * LD::ES)))
+                       : u32x4{0, 0, 0, 0};
       if constexpr (MODE == MODE_UPDATE) {
-        const int kr_ = idx >> 5, cc = idx & 31;    // 32 k-rows x 32 chunks of 4 floats
-        const int gk = kb + kr_, gj = j0 + cc * 4;
-        kr.r[q] = (gk < Rp.rows && gj < Rp.ld) ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
-                                                     gmem(Rp.f() + (int64_t)gk * Rp.ld + gj)))
-                                               : u32x4{0, 0, 0, 0};
+        const int kr_ = idx / LD::CPC, cc = idx % LD::CPC;   // BK k rows x CPC chunks
+        const int gk = kb + kr_, gj = j0 + cc * EPC;
+        kr.r[pl * LD::NQ + q] =
+            (gk < Rp.rows && gj < Rp.ld) ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
+                                               gmem(rb + ((int64_t)gk * Rp.ld + gj) * LD::ES)))
+                                         : u32x4{0, 0, 0, 0};
       } else {
         const int gj = j0 + row;
-        kr.r[q] = gj < Rp.rows ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
-                                     gmem(Rp.f() + (int64_t)gj * Rp.ld + kb + ch * 4)))
-                               : u32x4{0, 0, 0, 0};
-      }
-    }
-  } else {
-    constexpr int NPL = GemmLds<PREC>::NPL;
-#pragma unroll
-    for (int pl = 0; pl < NPL; ++pl) {
-      const __bf16 *lb = pl ? Lp.lo() : Lp.hi();
-      const __bf16 *rb = pl ? Rp.lo() : Rp.hi();
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int idx = tid + q * THREADS;
-        const int row = idx >> 2, ch = idx & 3;     // 128 rows x 4 chunks of 8 bf16
-        const int gi = i0 + row;
-        kr.l[pl * 2 + q] = gi < Lp.rows ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
-                                               gmem(lb + (int64_t)gi * Lp.ld + kb + ch * 8)))
-                                         : u32x4{0, 0, 0, 0};
-        if constexpr (MODE == MODE_UPDATE) {
-          const int kr_ = idx >> 4, cc = idx & 15;  // 32 k-rows x 16 chunks of 8 bf16
-          const int gk = kb + kr_, gj = j0 + cc * 8;
-          kr.r[pl * 2 + q] = (gk < Rp.rows && gj < Rp.ld)
-                                 ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
-                                       gmem(rb + (int64_t)gk * Rp.ld + gj)))
-                                 : u32x4{0, 0, 0, 0};
-        } else {
-          const int gj = j0 + row;
-          kr.r[pl * 2 + q] = gj < Rp.rows ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
-                                                gmem(rb + (int64_t)gj * Rp.ld + kb + ch * 8)))
-                                          : u32x4{0, 0, 0, 0};
-        }
+        kr.r[pl * LD::NQ + q] =
+            gj < Rp.rows ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
+                               gmem(rb + ((int64_t)gj * Rp.ld + kb + ch * EPC) * LD::ES)))
+                         : u32x4{0, 0, 0, 0};
       }
     }
   }
 }
 
-template <int PREC, int MODE>
-__device__ __forceinline__ void gemm_store_lds(const KRegs<PREC> &kr, char *stage) {
-  using LD = GemmLds<PREC>;
+template <int PREC, int MODE, int BK>
+__device__ __forceinline__ void gemm_store_lds(const KRegs<PREC, BK> &kr, char *stage) {
+  using LD = GemmLds<PREC, BK>;
   const int tid = threadIdx.x;
+  constexpr int EPC = 16 / LD::ES;
   char *lt = stage;                         // row tiles of L: NPL planes
   char *rt = stage + LD::NPL * LD::ROWT;    // then the R tiles
-  if constexpr (PREC == PREC_F32) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+  for (int pl = 0; pl < LD::NPL; ++pl) {
+#pragma unroll
+    for (int q = 0; q < LD::NQ; ++q) {
       const int idx = tid + q * THREADS;
-      const int row = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<u32x4 *>(reinterpret_cast<float *>(lt) + row * LD::RP + ch * 4) = kr.l[q];
+      const int row = idx / LD::CPR, ch = idx % LD::CPR;
+      *reinterpret_cast<u32x4 *>(lt + pl * LD::ROWT + (row * LD::RP + ch * EPC) * LD::ES) = kr.l[pl * LD::NQ + q];
       if constexpr (MODE == MODE_UPDATE) {
-        const int kr_ = idx >> 5, cc = idx & 31;
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<float *>(rt) + kr_ * LD::CP + cc * 4) = kr.r[q];
+        const int kr_ = idx / LD::CPC, cc = idx % LD::CPC;
+        *reinterpret_cast<u32x4 *>(rt + pl * LD::COLT + (kr_ * LD::CP + cc * EPC) * LD::ES) = kr.r[pl * LD::NQ + q];
       } else {
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<float *>(rt) + row * LD::RP + ch * 4) = kr.r[q];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int pl = 0; pl < LD::NPL; ++pl) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int idx = tid + q * THREADS;
-        const int row = idx >> 2, ch = idx & 3;
-        *reinterpret_cast<u32x4 *>(reinterpret_cast<__bf16 *>(lt + pl * LD::ROWT) + row * LD::RP + ch * 8) =
-            kr.l[pl * 2 + q];
-        if constexpr (MODE == MODE_UPDATE) {
-          const int kr_ = idx >> 4, cc = idx & 15;
-          *reinterpret_cast<u32x4 *>(reinterpret_cast<__bf16 *>(rt + pl * LD::COLT) + kr_ * LD::CP + cc * 8) =
-              kr.r[pl * 2 + q];
-        } else {
-          *reinterpret_cast<u32x4 *>(reinterpret_cast<__bf16 *>(rt + pl * LD::ROWT) + row * LD::RP + ch * 8) =
-              kr.r[pl * 2 + q];
-        }
+        *reinterpret_cast<u32x4 *>(rt + pl * LD::ROWT + (row * LD::RP + ch * EPC) * LD::ES) = kr.r[pl * LD::NQ + q];
       }
     }
   }
 }
 
 // MFMAs of one K step from an LDS stage; wave block rows wm*64.., columns wn*64...
-template <int PREC, int MODE>
+template <int PREC, int MODE, int BK>
 __device__ __forceinline__ void gemm_compute(f32x16 (&acc)[2][2], const char *stage, int wm, int wn, int lane) {
-  using LD = GemmLds<PREC>;
+  using LD = GemmLds<PREC, BK>;
   const int li = lane & 31, half = lane >> 5;
   const char *lt = stage;
   const char *rt = stage + LD::NPL * LD::ROWT;
@@ -587,11 +560,11 @@ __device__ __forceinline__ void gemm_compute(f32x16 (&acc)[2][2], const char *st
 //   GRAM    D = X X^T over the tile's X (upper blocks); writes A, or B = b A (+ a I) if c = 0
 //   SQUARE  D = A A^T; writes B = b A + c D (+ a I)
 //   UPDATE  D = B X;   writes X_next = D (+ a X for plain bf16)
-template <int PREC, int MODE>
+template <int PREC, int MODE, int BK>
 __global__ __launch_bounds__(THREADS) void gemm_ns_kernel(const GemmTile *__restrict__ tiles,
                                                           const GemmWork *__restrict__ work, char *ws,
                                                           GemmParams gp) {
-  using LD = GemmLds<PREC>;
+  using LD = GemmLds<PREC, BK>;
   __shared__ __attribute__((aligned(16))) char lds[LD::BYTES];
   const GemmWork wk = work[xcd_work_index()];
   const TileG t = tile_of(tiles, wk.tile);
@@ -613,18 +586,31 @@ __global__ __launch_bounds__(THREADS) void gemm_ns_kernel(const GemmTile *__rest
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = f32x16{};
 
-  KRegs<PREC> kr;
-  gemm_load<PREC, MODE>(kr, Lp, i0, Rp, j0, 0);
-  gemm_store_lds<PREC, MODE>(kr, lds);
+  // The next K slice's global loads are in flight in registers while the MFMAs read the
+  // current one from LDS.  Slices of 32 alternate between two LDS stages (one barrier
+  // per slice); slices of 64 (whole 128-byte lines of bf16 rows, for long K) use one
+  // stage, and two workgroups share a CU, so one's LDS stores overlap the other's
+  // products.
+  KRegs<PREC, BK> kr;
+  gemm_load<PREC, MODE, BK>(kr, Lp, i0, Rp, j0, 0);
+  gemm_store_lds<PREC, MODE, BK>(kr, lds);
   __syncthreads();
   int cur = 0;
   for (int kb = 0; kb < kdim; kb += BK) {
     const bool more = kb + BK < kdim;
-    if (more) gemm_load<PREC, MODE>(kr, Lp, i0, Rp, j0, kb + BK);
-    gemm_compute<PREC, MODE>(acc, lds + cur * LD::STAGE, wm, wn, lane);
-    if (more) gemm_store_lds<PREC, MODE>(kr, lds + (cur ^ 1) * LD::STAGE);
-    __syncthreads();
-    cur ^= 1;
+    if (more) gemm_load<PREC, MODE, BK>(kr, Lp, i0, Rp, j0, kb + BK);
+    gemm_compute<PREC, MODE, BK>(acc, lds + cur * LD::STAGE, wm, wn, lane);
+    if constexpr (LD::NSTAGE == 2) {
+      if (more) gemm_store_lds<PREC, MODE, BK>(kr, lds + (cur ^ 1) * LD::STAGE);
+      __syncthreads();
+      cur ^= 1;
+    } else {
+      __syncthreads();   // the stage fully read
+      if (more) {
+        gemm_store_lds<PREC, MODE, BK>(kr, lds);
+        __syncthreads();
+      }
+    }
   }
 
   // ---- epilogue: stage D^T in LDS (fp32), then write rows with 16-element stores
@@ -716,12 +702,20 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
   if (c.tile_n) hipLaunchKernelGGL(gemm_norm_kernel, grid(c.tile_n), dim3(THREADS), 0, stream, tiles, (int)c.tile_first, ws, p.eps, p.identity);
   if (c.n_stg) hipLaunchKernelGGL((gemm_stage_kernel<S, PREC>), grid(c.n_stg), dim3(THREADS), 0, stream, layers, tiles, c.stg, ws);
   GemmParams gp{p.a, p.b, p.c, 0, PREC != PREC_BF16};
-  for (int it = 0; it < p.steps; ++it) {
-    gp.xsel = it & 1;
-    hipLaunchKernelGGL((gemm_ns_kernel<PREC, MODE_GRAM>), grid(c.n_sym), dim3(THREADS), 0, stream, tiles, c.sym, ws, gp);
-    if (p.c != 0.f)
-      hipLaunchKernelGGL((gemm_ns_kernel<PREC, MODE_SQUARE>), grid(c.n_sym), dim3(THREADS), 0, stream, tiles, c.sym, ws, gp);
-    hipLaunchKernelGGL((gemm_ns_kernel<PREC, MODE_UPDATE>), grid(c.n_upd), dim3(THREADS), 0, stream, tiles, c.upd, ws, gp);
+  auto products = [&](auto bkc) {
+    constexpr int BK = decltype(bkc)::value;
+    for (int it = 0; it < p.steps; ++it) {
+      gp.xsel = it & 1;
+      hipLaunchKernelGGL((gemm_ns_kernel<PREC, MODE_GRAM, BK>), grid(c.n_sym), dim3(THREADS), 0, stream, tiles, c.sym, ws, gp);
+      if (p.c != 0.f)
+        hipLaunchKernelGGL((gemm_ns_kernel<PREC, MODE_SQUARE, BK>), grid(c.n_sym), dim3(THREADS), 0, stream, tiles, c.sym, ws, gp);
+      hipLaunchKernelGGL((gemm_ns_kernel<PREC, MODE_UPDATE, BK>), grid(c.n_upd), dim3(THREADS), 0, stream, tiles, c.upd, ws, gp);
+    }
+  };
+  if (c.long_k) {
+    products(std::integral_constant<int, 64>{});
+  } else {
+    products(std::integral_constant<int, 32>{});
   }
   if (c.n_app)
     hipLaunchKernelGGL((gemm_apply_kernel<PREC>), grid(c.n_app), dim3(THREADS), 0, stream, layers, tiles, c.app, ws,

@@ -46,8 +46,8 @@ GemmSizes gemm_sizes(int64_t h, int64_t w) {
   GemmSizes z;
   z.r = std::min(h, w);
   z.s = std::max(h, w);
-  z.ldx = roundup(z.s, 32);
-  z.lda = roundup(z.r, 32);
+  z.ldx = roundup(z.s, 64);   // whole K slices of the GEMM kernels
+  z.lda = roundup(z.r, 64);
   z.nred = cdiv(h * w, kGemmMomentumBlock);
   z.x = align256((size_t)z.r * z.ldx * 4);
   z.ab = align256((size_t)z.r * z.lda * 4);
@@ -288,7 +288,7 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
           max_ws = std::max(max_ws, gemm_tile_workspace(h, w));
           {
             // 128-blocks as launched: symmetric products on the upper blocks only, K
-            // padded to 32; the update over all blocks
+            // padded to 64; the update over all blocks
             const double nb = (double)cdiv(r, 128), nbs = (double)cdiv(z.ldx, 128);
             const double sym = nb * (nb + 1) / 2 * 2.0 * 128 * 128;
             issued += (double)K * split * (sym * z.ldx + (quintic ? sym * z.lda : 0.0) +
@@ -337,6 +337,9 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
         for (int32_t bi = 0; bi < (int32_t)cdiv(g.h, 64); ++bi)
           for (int32_t bj = 0; bj < (int32_t)cdiv(g.w, 64); ++bj) wapp.push_back(GemmWork{ti, bi, bj});
       }
+      ch.long_k = true;
+      for (int64_t i = first; i < end; ++i)
+        ch.long_k = ch.long_k && gt[(size_t)i].lda >= kGemmLongK && gt[(size_t)i].ldx >= kGemmLongK;
       ch.mom.n = (int64_t)wmom.size() - ch.mom.first;
       ch.stg.n = (int64_t)wstg.size() - ch.stg.first;
       ch.sym.n = (int64_t)wsym.size() - ch.sym.first;

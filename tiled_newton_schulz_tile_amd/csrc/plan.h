@@ -30,6 +30,7 @@ struct GemmChunk {
   int64_t first, n;   // range in Plan::gtiles
   size_t ws_bytes;    // workspace the chunk uses
   Range mom, stg, sym, upd, app;  // ranges in the work lists
+  bool long_k;        // every GEMM K of its tiles >= kGemmLongK: K slices of 64
 };
 
 struct Plan {
