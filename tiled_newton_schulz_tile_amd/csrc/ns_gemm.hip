@@ -244,123 +244,70 @@ __global__ __launch_bounds__(THREADS) void gemm_norm_kernel(const GemmTile *__re
 }
 
 // ------------------------------------------------------------------ stage / apply
-// 64 x 64 blocks through an LDS tile (pitch 65): thread t covers row t / 4, columns
-// 16 (t % 4) .. +15 of the block.
+// Tall tiles (transposed on their short side): 64 x 64 blocks through an LDS tile (pitch
+// 65); thread t covers row t / 4, columns 16 (t % 4) .. +15 of the block.  Wide and square
+// tiles need no transpose: strips of 16 rows x 256 columns, thread t covering row t / 16,
+// columns 16 (t % 16) .. +15, so that a wave reads and writes 1 KB runs of fp32 weights
+// (512 B of each bf16 plane) per row instead of 256 B.
 constexpr int SB = 64, SBP = 65;
+constexpr int STRIP_R = 16, STRIP_C = 256;
 
-// Work item (tile, bi, bj): oriented block rows [64 bi, +64), columns [64 bj, +64) of
-// X0 (r x ldx); zeros outside the r x s tile.
-template <typename S, int PREC>
-__global__ __launch_bounds__(THREADS) void gemm_stage_kernel(const LayerDesc *__restrict__ layers,
-                                                             const GemmTile *__restrict__ tiles,
-                                                             const GemmWork *__restrict__ work, char *ws) {
-  __shared__ float blk[SB * SBP];
-  const GemmWork wk = work[blockIdx.x];
-  const TileG t = tile_of(tiles, wk.tile);
-  const LayerDesc *L = layers + t.layer;
-  const float inv = gmem(reinterpret_cast<const float *>(ws + t.red))[t.nred];
-  const S *mb = reinterpret_cast<const S *>(L->m);
-  const int64_t ldm = L->ld_m;
-  const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 16;
-  // the global block this oriented block comes from
-  const int gr0 = t.tall ? wk.bj * SB : wk.bi * SB;
-  const int gc0 = t.tall ? wk.bi * SB : wk.bj * SB;
-  {
-    const int gi = gr0 + lr;
-    const int gj = gc0 + lc;
-    float v[16];
-    if (gi < t.h && gj + 16 <= t.w && L->vec_ok && ((t.col0 + gj) & 7) == 0) {
-      const int64_t o = (int64_t)(t.row0 + gi) * ldm + t.col0 + gj;
-      if constexpr (sizeof(S) == 2) {
-        const GLOBAL_AS u32x4 *p = reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(mb + o));
-        const u32x4 a = p[0], b = p[1];
+// 16 consecutive state values of tile row gi from tile column gj, zero outside the tile.
+template <typename S>
+__device__ __forceinline__ void load_state16(const LayerDesc *L, const S *mb, int64_t ldm, const TileG &t, int gi,
+                                             int gj, float (&v)[16]) {
+  if (gi < t.h && gj + 16 <= t.w && L->vec_ok && ((t.col0 + gj) & 7) == 0) {
+    const int64_t o = (int64_t)(t.row0 + gi) * ldm + t.col0 + gj;
+    if constexpr (sizeof(S) == 2) {
+      const GLOBAL_AS u32x4 *p = reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(mb + o));
+      const u32x4 a = p[0], b = p[1];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const unsigned wa = a[q >> 1], wb = b[q >> 1];
-          v[q] = __builtin_bit_cast(float, (q & 1) ? (wa & 0xffff0000u) : (wa << 16));
-          v[q + 8] = __builtin_bit_cast(float, (q & 1) ? (wb & 0xffff0000u) : (wb << 16));
-        }
-      } else {
-        const GLOBAL_AS f32x4 *p = reinterpret_cast<const GLOBAL_AS f32x4 *>(gmem(mb + o));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 x = p[q];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
-        }
+      for (int q = 0; q < 8; ++q) {
+        const unsigned wa = a[q >> 1], wb = b[q >> 1];
+        v[q] = __builtin_bit_cast(float, (q & 1) ? (wa & 0xffff0000u) : (wa << 16));
+        v[q + 8] = __builtin_bit_cast(float, (q & 1) ? (wb & 0xffff0000u) : (wb << 16));
       }
     } else {
+      const GLOBAL_AS f32x4 *p = reinterpret_cast<const GLOBAL_AS f32x4 *>(gmem(mb + o));
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        float x = 0.f;
-        if (gi < t.h && gj + q < t.w) {
-          const int64_t o = (int64_t)(t.row0 + gi) * ldm + t.col0 + gj + q;
-          if constexpr (sizeof(S) == 2)
-            x = bf16_bits_to_f32(gmem(reinterpret_cast<const unsigned short *>(mb))[o]);
-          else
-            x = gmem(mb)[o];
-        }
-        v[q] = x;
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 x = p[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
       }
     }
+  } else {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) blk[lr * SBP + lc + q] = v[q] * inv;
-  }
-  __syncthreads();
-  const int orow = wk.bi * SB + lr, ocol = wk.bj * SB + lc;
-  if (orow < t.r && ocol < t.ldx) {
-    float v[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = t.tall ? blk[(lc + q) * SBP + lr] : blk[lr * SBP + lc + q];
-    const Planes<PREC> X{ws + t.x0, t.r, t.ldx};
-    X.put16(orow, ocol, v);
+    for (int q = 0; q < 16; ++q) {
+      float x = 0.f;
+      if (gi < t.h && gj + q < t.w) {
+        const int64_t o = (int64_t)(t.row0 + gi) * ldm + t.col0 + gj + q;
+        if constexpr (sizeof(S) == 2)
+          x = bf16_bits_to_f32(gmem(reinterpret_cast<const unsigned short *>(mb))[o]);
+        else
+          x = gmem(mb)[o];
+      }
+      v[q] = x;
+    }
   }
 }
 
-// Work item (tile, bi, bj): global block rows [64 bi, +64), columns [64 bj, +64) of the
-// h x w tile.  O comes from the X buffer the last step wrote.
-template <int PREC>
-__global__ __launch_bounds__(THREADS) void gemm_apply_kernel(const LayerDesc *__restrict__ layers,
-                                                             const GemmTile *__restrict__ tiles,
-                                                             const GemmWork *__restrict__ work, char *ws,
-                                                             int xsel, float lr_, int write_u) {
-  __shared__ float blk[SB * SBP];
-  const GemmWork wk = work[blockIdx.x];
-  const TileG t = tile_of(tiles, wk.tile);
-  const LayerDesc *L = layers + t.layer;
-  const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 16;
-  const int or0 = t.tall ? wk.bj * SB : wk.bi * SB;   // oriented block holding this block
-  const int oc0 = t.tall ? wk.bi * SB : wk.bj * SB;
-  const Planes<PREC> X{ws + (xsel ? t.x1 : t.x0), t.r, t.ldx};
-  {
-    const int oi = or0 + lr, oj = oc0 + lc;
-    float v[16];
-    if (oi < t.r && oj < t.s) {
-      X.get16(oi, oj, v);   // oj + 16 <= ldx: ldx is a multiple of 32 and oj of 16
-    } else {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) v[q] = 0.f;
-    }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) blk[lr * SBP + lc + q] = oj + q < t.s ? v[q] : 0.f;
-  }
-  __syncthreads();
-  const int gi = wk.bi * SB + lr, gj = wk.bj * SB + lc;
-  if (gi >= t.h || gj >= t.w) return;
-  float o[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) o[q] = t.tall ? blk[(lc + q) * SBP + lr] : blk[lr * SBP + lc + q];
+// W <- W - lr o (and U <- o) for the n <= 16 weights of tile row gi from column gj.
+__device__ __forceinline__ void apply16(const LayerDesc *L, const TileG &t, int gi, int gj, const float (&o)[16],
+                                        float lr_, int write_u) {
   const int n = t.w - gj < 16 ? t.w - gj : 16;
   float *wrow = L->w + (int64_t)(t.row0 + gi) * L->ld_w + t.col0 + gj;
   const float nlr = -lr_;
   if (n == 16 && L->vec_w && ((t.col0 + gj) & 3) == 0) {
     GLOBAL_AS f32x4 *p = reinterpret_cast<GLOBAL_AS f32x4 *>(gmem(wrow));
+    f32x4 x[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = p[q];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      f32x4 x = p[q];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(nlr, o[4 * q + e], x[e]);
-      p[q] = x;
+      for (int e = 0; e < 4; ++e) x[q][e] = __builtin_fmaf(nlr, o[4 * q + e], x[q][e]);
+      p[q] = x[q];
     }
     if (write_u) {
       GLOBAL_AS f32x4 *u = reinterpret_cast<GLOBAL_AS f32x4 *>(
@@ -376,6 +323,98 @@ __global__ __launch_bounds__(THREADS) void gemm_apply_kernel(const LayerDesc *__
       for (int q = 0; q < n; ++q) u[q] = o[q];
     }
   }
+}
+
+// Work item (tile, bi, bj): tall tiles, oriented block rows [64 bi, +64), columns
+// [64 bj, +64) of X0 (r x ldx); other tiles, rows [16 bi, +16), columns [256 bj, +256).
+// Zeros outside the r x s tile.
+template <typename S, int PREC>
+__global__ __launch_bounds__(THREADS) void gemm_stage_kernel(const LayerDesc *__restrict__ layers,
+                                                             const GemmTile *__restrict__ tiles,
+                                                             const GemmWork *__restrict__ work, char *ws) {
+  __shared__ float blk[SB * SBP];
+  const GemmWork wk = work[blockIdx.x];
+  const TileG t = tile_of(tiles, wk.tile);
+  const LayerDesc *L = layers + t.layer;
+  const float inv = gmem(reinterpret_cast<const float *>(ws + t.red))[t.nred];
+  const S *mb = reinterpret_cast<const S *>(L->m);
+  const int64_t ldm = L->ld_m;
+  const Planes<PREC> X{ws + t.x0, t.r, t.ldx};
+  if (!t.tall) {   // uniform over the workgroup: no transpose, straight from registers
+    const int gi = wk.bi * STRIP_R + (int)(threadIdx.x >> 4);
+    const int gj = wk.bj * STRIP_C + (int)(threadIdx.x & 15) * 16;
+    if (gi >= t.r || gj >= t.ldx) return;
+    float v[16];
+    load_state16<S>(L, mb, ldm, t, gi, gj, v);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] *= inv;
+    X.put16(gi, gj, v);
+    return;
+  }
+  const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 16;
+  // the global block this oriented block comes from
+  {
+    const int gi = wk.bj * SB + lr;
+    const int gj = wk.bi * SB + lc;
+    float v[16];
+    load_state16<S>(L, mb, ldm, t, gi, gj, v);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) blk[lr * SBP + lc + q] = v[q] * inv;
+  }
+  __syncthreads();
+  const int orow = wk.bi * SB + lr, ocol = wk.bj * SB + lc;
+  if (orow < t.r && ocol < t.ldx) {
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = blk[(lc + q) * SBP + lr];
+    X.put16(orow, ocol, v);
+  }
+}
+
+// Work item (tile, bi, bj): tall tiles, global block rows [64 bi, +64), columns
+// [64 bj, +64) of the h x w tile; other tiles, rows [16 bi, +16), columns [256 bj, +256).
+// O comes from the X buffer the last step wrote.
+template <int PREC>
+__global__ __launch_bounds__(THREADS) void gemm_apply_kernel(const LayerDesc *__restrict__ layers,
+                                                             const GemmTile *__restrict__ tiles,
+                                                             const GemmWork *__restrict__ work, char *ws,
+                                                             int xsel, float lr_, int write_u) {
+  __shared__ float blk[SB * SBP];
+  const GemmWork wk = work[blockIdx.x];
+  const TileG t = tile_of(tiles, wk.tile);
+  const LayerDesc *L = layers + t.layer;
+  const Planes<PREC> X{ws + (xsel ? t.x1 : t.x0), t.r, t.ldx};
+  if (!t.tall) {   // uniform over the workgroup: O row gi is X row gi
+    const int gi = wk.bi * STRIP_R + (int)(threadIdx.x >> 4);
+    const int gj = wk.bj * STRIP_C + (int)(threadIdx.x & 15) * 16;
+    if (gi >= t.h || gj >= t.w) return;
+    float o[16];
+    X.get16(gi, gj, o);   // gj + 16 <= ldx: ldx is a multiple of 64 and gj of 16
+    apply16(L, t, gi, gj, o, lr_, write_u);
+    return;
+  }
+  const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 16;
+  const int or0 = wk.bj * SB;   // oriented block holding this block
+  const int oc0 = wk.bi * SB;
+  {
+    const int oi = or0 + lr, oj = oc0 + lc;
+    float v[16];
+    if (oi < t.r && oj < t.s) {
+      X.get16(oi, oj, v);   // oj + 16 <= ldx: ldx is a multiple of 64 and oj of 16
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) blk[lr * SBP + lc + q] = oj + q < t.s ? v[q] : 0.f;
+  }
+  __syncthreads();
+  const int gi = wk.bi * SB + lr, gj = wk.bj * SB + lc;
+  if (gi >= t.h || gj >= t.w) return;
+  float o[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) o[q] = blk[(lc + q) * SBP + lr];
+  apply16(L, t, gi, gj, o, lr_, write_u);
 }
 
 // ------------------------------------------------------------------ grouped GEMMs

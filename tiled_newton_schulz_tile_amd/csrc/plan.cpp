@@ -327,15 +327,18 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
         const GemmTile &g = gt[(size_t)i];
         const int32_t ti = (int32_t)i;
         for (int32_t b = 0; b < g.nred; ++b) wmom.push_back(GemmWork{ti, b, 0});
-        for (int32_t bi = 0; bi < (int32_t)cdiv(g.r, 64); ++bi)
-          for (int32_t bj = 0; bj < (int32_t)cdiv(g.ldx, 64); ++bj) wstg.push_back(GemmWork{ti, bi, bj});
+        // stage / apply: 64 x 64 blocks for tall tiles (LDS transpose), else strips of
+        // 16 rows x 256 columns (straight from registers)
+        const int64_t sr = g.tall ? 64 : 16, sc = g.tall ? 64 : 256;
+        for (int32_t bi = 0; bi < (int32_t)cdiv(g.r, sr); ++bi)
+          for (int32_t bj = 0; bj < (int32_t)cdiv(g.ldx, sc); ++bj) wstg.push_back(GemmWork{ti, bi, bj});
         const int32_t nb = (int32_t)cdiv(g.r, 128);
         for (int32_t bi = 0; bi < nb; ++bi)
           for (int32_t bj = bi; bj < nb; ++bj) wsym.push_back(GemmWork{ti, bi, bj});
         for (int32_t bi = 0; bi < nb; ++bi)
           for (int32_t bj = 0; bj < (int32_t)cdiv(g.ldx, 128); ++bj) wupd.push_back(GemmWork{ti, bi, bj});
-        for (int32_t bi = 0; bi < (int32_t)cdiv(g.h, 64); ++bi)
-          for (int32_t bj = 0; bj < (int32_t)cdiv(g.w, 64); ++bj) wapp.push_back(GemmWork{ti, bi, bj});
+        for (int32_t bi = 0; bi < (int32_t)cdiv(g.h, sr); ++bi)
+          for (int32_t bj = 0; bj < (int32_t)cdiv(g.w, sc); ++bj) wapp.push_back(GemmWork{ti, bi, bj});
       }
       ch.long_k = true;
       for (int64_t i = first; i < end; ++i)
