@@ -364,8 +364,9 @@ struct HiPiece {  // bf16 hi of each side, one 32-k half chunk (two 16-k pieces)
 };
 
 // The e4m3 operands of one correction product: L from plane lp (rows, or columns when
-// TRANS_L), R from plane rp, k in [kb, kb + 64).  An aliased R block is read again here.
-// B0: the first L block is not read (the caller supplies it).
+// TRANS_L), R from plane rp, k in [kb, kb + 64).  READ_R false: R is not read; B0 = 1: the
+// first L block is not read (the caller supplies both, from the other correction stage,
+// when R is L's first block).
 template <int TS, bool TRANS_L, int NB, bool READ_R = true, int B0 = 0>
 __device__ __forceinline__ void load_f8(F8Half<TS> &f, const unsigned char *lp, int l0, const unsigned char *rp,
                                         int r0, int lane, int kb) {
