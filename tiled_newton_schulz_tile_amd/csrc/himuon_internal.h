@@ -61,6 +61,8 @@ constexpr int kGemmMomentumBlock = 8192;
 // through one LDS stage; shorter ones use slices of 32 through two stages, which hides
 // more latency when a block has only a few slices.
 constexpr int64_t kGemmLongK = 1024;
+// Block rows per group in the work order of long-K products.
+constexpr int kGemmGroupRows = 8;
 
 enum Prec : int { PREC_F32 = 0, PREC_BF16 = 1, PREC_BF16X3 = 2, PREC_BF16F8 = 3 };
 

@@ -323,6 +323,14 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
       ch.sym.first = (int64_t)wsym.size();
       ch.upd.first = (int64_t)wupd.size();
       ch.app.first = (int64_t)wapp.size();
+      ch.long_k = true;
+      for (int64_t i = first; i < end; ++i)
+        ch.long_k = ch.long_k && gt[(size_t)i].lda >= kGemmLongK && gt[(size_t)i].ldx >= kGemmLongK;
+      // Products of long-K chunks list their 128-blocks in groups of kGemmGroupRows block
+      // rows, column by column inside a group, so that the workgroups in flight on one
+      // XCD (a contiguous run of the list) share the K slices of a few row and column
+      // panels in that XCD's L2.  Short-K chunks keep the row-major order.
+      const int32_t grp = ch.long_k ? kGemmGroupRows : 0;
       for (int64_t i = first; i < end; ++i) {
         const GemmTile &g = gt[(size_t)i];
         const int32_t ti = (int32_t)i;
@@ -332,17 +340,24 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
         const int64_t sr = g.tall ? 64 : 16, sc = g.tall ? 64 : 256;
         for (int32_t bi = 0; bi < (int32_t)cdiv(g.r, sr); ++bi)
           for (int32_t bj = 0; bj < (int32_t)cdiv(g.ldx, sc); ++bj) wstg.push_back(GemmWork{ti, bi, bj});
-        const int32_t nb = (int32_t)cdiv(g.r, 128);
-        for (int32_t bi = 0; bi < nb; ++bi)
-          for (int32_t bj = bi; bj < nb; ++bj) wsym.push_back(GemmWork{ti, bi, bj});
-        for (int32_t bi = 0; bi < nb; ++bi)
-          for (int32_t bj = 0; bj < (int32_t)cdiv(g.ldx, 128); ++bj) wupd.push_back(GemmWork{ti, bi, bj});
+        const int32_t nb = (int32_t)cdiv(g.r, 128), nbj = (int32_t)cdiv(g.ldx, 128);
+        if (grp > 0) {
+          for (int32_t b0 = 0; b0 < nb; b0 += grp) {
+            const int32_t b1 = std::min(nb, b0 + grp);
+            for (int32_t bj = b0; bj < nb; ++bj)
+              for (int32_t bi = b0; bi < b1 && bi <= bj; ++bi) wsym.push_back(GemmWork{ti, bi, bj});
+            for (int32_t bj = 0; bj < nbj; ++bj)
+              for (int32_t bi = b0; bi < b1; ++bi) wupd.push_back(GemmWork{ti, bi, bj});
+          }
+        } else {
+          for (int32_t bi = 0; bi < nb; ++bi)
+            for (int32_t bj = bi; bj < nb; ++bj) wsym.push_back(GemmWork{ti, bi, bj});
+          for (int32_t bi = 0; bi < nb; ++bi)
+            for (int32_t bj = 0; bj < nbj; ++bj) wupd.push_back(GemmWork{ti, bi, bj});
+        }
         for (int32_t bi = 0; bi < (int32_t)cdiv(g.h, sr); ++bi)
           for (int32_t bj = 0; bj < (int32_t)cdiv(g.w, sc); ++bj) wapp.push_back(GemmWork{ti, bi, bj});
       }
-      ch.long_k = true;
-      for (int64_t i = first; i < end; ++i)
-        ch.long_k = ch.long_k && gt[(size_t)i].lda >= kGemmLongK && gt[(size_t)i].ldx >= kGemmLongK;
       ch.mom.n = (int64_t)wmom.size() - ch.mom.first;
       ch.stg.n = (int64_t)wstg.size() - ch.stg.first;
       ch.sym.n = (int64_t)wsym.size() - ch.sym.first;
