@@ -32,7 +32,7 @@ METRIC = "HiMuon step ms & NS TFLOP/s (% MFMA peak) vs T, 8B-shaped stack"
 # rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), scaled by the
 # readings of a 1 GiB elementwise copy (x2.0 read, x1.0 write).  Valid only for the
 # kernel source it was measured on (sha256 prefix of ns_fused.hip).
-TRAFFIC_T128 = {"source_sha256_16": "cfdd5f462e27cf02", "precision": "bf16f8", "fetch_kib": 27291183.5,
+TRAFFIC_T128 = {"source_sha256_16": "aa6cbb4a4531b882", "precision": "bf16f8", "fetch_kib": 27291179.125,
                 "write_kib": 40894464.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
