@@ -133,10 +133,10 @@ def cpu_baseline(K, coeffs, tile, shapes):
     fl = oracle.ns_flops(layer, tile, K, coeffs)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"one decoder layer of the stack ({len(layer)} matrices, "
-                      f"{sum(h * w for h, w in layer)} params; T={tile}, K={K}, quintic, fp64 numpy), "
-                      f"{dt:.1f} s for {fl:.3e} NS flops; whole-step time at this rate scales "
-                      f"by the flop ratio",
-            "seconds": dt}
+                      f"{sum(h * w for h, w in layer)} params; T={tile}, K={K}, quintic, fp64 numpy "
+                      f"{np.__version__}), {dt:.1f} s for {fl:.3e} NS flops; whole-step time at this "
+                      f"rate scales by the flop ratio",
+            "seconds": dt, "host_cpus": os.cpu_count()}
 
 
 def run_diagnostics(args):
