@@ -261,9 +261,9 @@ def main():
                     help="time the Sign-Muon sign-pack and vote kernels instead of the step benchmark")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the HiMuon step is tile-local and this build runs on "
-              "one MI355X; multi-GPU sharding is a design note only. Run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the HiMuon step is tile-local and the library runs "
+              "it on one MI355X; sharding its tiles across GPUs is designed, not built. "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -52,7 +52,7 @@ typedef enum {
   HIMUON_EBUDGET = -2,      /* workspace budget below what one tile needs          */
   HIMUON_ENOMEM = -3,       /* host or device allocation failed                    */
   HIMUON_EDEVICE = -4,      /* HIP runtime error (launch, copy, no device)         */
-  HIMUON_EUNSUPPORTED = -5  /* valid request this build does not implement         */
+  HIMUON_EUNSUPPORTED = -5  /* valid request the library does not implement        */
 } himuon_status;
 
 /* storage dtype of momentum and gradient */

@@ -2,7 +2,7 @@
 
     python tiled_newton_schulz_tile_amd/build.py
 
-(run as a script: importing the package loads the library this builds)
+(run as a script: importing the package loads the library it writes)
 """
 from __future__ import annotations
 
