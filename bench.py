@@ -47,6 +47,9 @@ def measured_traffic():
     return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
 
 
+STACK_TEXT = {"llama3-8b-32L": "Llama-3-8B-shaped stack", "decoder-1b-16L": "1B-class decoder stack",
+              "gpt2-small-12L": "GPT-2-small-shaped stack", "single-256x512": "single 256x512 matrix"}
+
 # name -> (library constant, dtype field, description)
 PRECISIONS = {
     "bf16f8": ("PREC_BF16F8", "bf16+e4m3",
@@ -324,6 +327,32 @@ def main():
             f"({cpu['seconds']:.1f}s)")
         cpu.pop("seconds", None)
 
+    n_params = sum(h * w for h, w in shapes)
+    kt = st["kernel_tile"]
+    if kt > 0 and st["gemm_tiles"] == 0:
+        # one launch of the fused kernel per step: the step time is its duration
+        kprec = args.precision if (args.precision != "bf16f8" or kt >= 64) else "bf16x3"
+        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic() if (kt == 128 and args.tile == 128
+                                                      and args.workload == "llama3-8b-32L"
+                                                      and args.precision == TRAFFIC_T128["precision"])
+                    else None,
+                    "kernel": f"fused_step_kernel<{kt}, {kprec}, bf16 state>",
+                    "launches_per_step": 1, "algorithmic_flops_per_launch": st["ns_flops"],
+                    "issued_flops_per_launch": st["issued_flops"],
+                    "algorithmic_bytes_per_launch": st["step_bytes"]}
+    else:
+        # the large-tile path: per chunk, momentum, norm, stage and apply launches plus the
+        # products of every NS step (Gram, square, update; bf16x3 arithmetic); rates are
+        # over the whole step, not one kernel
+        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": "large-tile path (gemm_ns_kernel products, bf16x3; whole step)",
+                    "launches_per_step": int(st["chunks"]) * (4 + 3 * K),
+                    "algorithmic_flops_per_step": st["ns_flops"], "issued_flops_per_step": st["issued_flops"],
+                    "algorithmic_bytes_per_step": st["step_bytes"]}
+
     out = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -340,24 +369,15 @@ def main():
         "data": ("synthetic: G = U diag(1/i) V^T + 0.01 N(0,1) per matrix (Haar U, V shared per "
                  "shape), M0 = 0, W0 = 0.02 N(0,1); seeded") if args.inputs == "power-law" else
                 "synthetic: G = 0.01 N(0,1), M0 = 0, W0 = 0.02 N(0,1); seeded (counter run)",
-        "config": {"workload": f"{args.workload} HiMuon step (Llama-3-8B-shaped stack, 224 "
-                               f"matrices, 6.98e9 params), T={args.tile}, K={K}, quintic",
+        "config": {"workload": f"{args.workload} HiMuon step ({STACK_TEXT.get(args.workload, args.workload)}, "
+                               f"{len(shapes)} matrices, {n_params:.3g} params), T={args.tile}, K={K}, quintic",
                    "tile": args.tile, "ns_steps": K, "coeffs": "quintic", "state_dtype": "bf16",
                    "weight_dtype": "f32", "workspace_budget": 4 * 10 ** 9,
-                   "tiles": st["tiles"], "params": sum(h * w for h, w in shapes)},
+                   "tiles": st["tiles"], "params": n_params},
         "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         "issued_mfma_tflops": round(issued, 2),
         "hbm_gbps": round(gbps, 1),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic() if (args.tile == 128 and args.workload == "llama3-8b-32L"
-                                                       and args.precision == TRAFFIC_T128["precision"])
-                     else None,
-                     "kernel": f"fused_step_kernel<128, {args.precision}, bf16 state>",
-                     "launches_per_step": 1, "algorithmic_flops_per_launch": st["ns_flops"],
-                     "issued_flops_per_launch": st["issued_flops"],
-                     "algorithmic_bytes_per_launch": st["step_bytes"]},
+        "roofline": roofline,
         "sweep": sweep,
         "cpu_baseline": cpu,
     }
