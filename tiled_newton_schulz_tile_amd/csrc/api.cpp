@@ -195,6 +195,7 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
       cl.app = dw[4] + ch.app.first;
       cl.n_app = ch.app.n;
       cl.long_k = ch.long_k ? 1 : 0;
+      cl.t256 = ch.t256 ? 1 : 0;
       hipError_t e = himuon::launch_gemm_chunk(gemm_prec, c.state_dtype == HIMUON_BF16, dl, dgt, cl,
                                                reinterpret_cast<char *>(workspace), prm, stream);
       if (e != hipSuccess) return hip_fail(e, "large-tile kernel launch");

@@ -118,6 +118,8 @@ struct GemmChunkLaunch {
   const GemmWork *upd;  int64_t n_upd; // (tile, bi, bj): 128-blocks of r x s
   const GemmWork *app;  int64_t n_app; // (tile, bi, bj): 64-blocks of the h x w tile
   int32_t long_k;                       // K slices of 64 (one LDS stage) instead of 32 (two)
+  int32_t t256;                         // every tile 256 x 256 (bf16 planes): one workgroup
+                                        // per tile and product; sym / upd lists unused
 };
 // Runs one full step for the tiles of a chunk: momentum and partial norms, norm
 // reduction, staging of X0, K Newton-Schulz steps as grouped MFMA GEMMs, update.

@@ -16,7 +16,10 @@
 //   apply        W <- W - lr O, O reoriented (LDS transpose for tall tiles)
 // GEMM blocks are 128 x 128; K slices of 32 (two LDS stages) or, when every K of a chunk
 // is long, of 64 (one stage) are staged through LDS from registers loaded one slice
-// ahead; four waves each own a 64 x 64 block (2 x 2 MFMA 32x32 tiles).
+// ahead; four waves each own a 64 x 64 block (2 x 2 MFMA 32x32 tiles).  Chunks of
+// 256 x 256 tiles run each product as one workgroup per tile (gemm_t256_kernel).
+// Operands are read with plain (not non-temporal) loads: a K slice of 32 bf16 is half
+// of a 128-byte line, and the other half is read by the next slice, from L2.
 #include <type_traits>
 
 #include "device_common.h"
@@ -475,20 +478,20 @@ __device__ __forceinline__ void gemm_load(KRegs<PREC, BK> &kr, const Planes<PREC
       const int row = idx / LD::CPR, ch = idx % LD::CPR;   // BM rows x CPR chunks
       const int gi = i0 + row;
       kr.l[pl * LD::NQ + q] =
-          gi < Lp.rows ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
+          gi < Lp.rows ? *(reinterpret_cast<const GLOBAL_AS u32x4 *>(
                              gmem(lb + ((int64_t)gi * Lp.ld + kb + ch * EPC) * LD::ES)))
                        : u32x4{0, 0, 0, 0};
       if constexpr (MODE == MODE_UPDATE) {
         const int kr_ = idx / LD::CPC, cc = idx % LD::CPC;   // BK k rows x CPC chunks
         const int gk = kb + kr_, gj = j0 + cc * EPC;
         kr.r[pl * LD::NQ + q] =
-            (gk < Rp.rows && gj < Rp.ld) ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
+            (gk < Rp.rows && gj < Rp.ld) ? *(reinterpret_cast<const GLOBAL_AS u32x4 *>(
                                                gmem(rb + ((int64_t)gk * Rp.ld + gj) * LD::ES)))
                                          : u32x4{0, 0, 0, 0};
       } else {
         const int gj = j0 + row;
         kr.r[pl * LD::NQ + q] =
-            gj < Rp.rows ? __builtin_nontemporal_load(reinterpret_cast<const GLOBAL_AS u32x4 *>(
+            gj < Rp.rows ? *(reinterpret_cast<const GLOBAL_AS u32x4 *>(
                                gmem(rb + ((int64_t)gj * Rp.ld + kb + ch * EPC) * LD::ES)))
                          : u32x4{0, 0, 0, 0};
       }
@@ -730,13 +733,207 @@ __global__ __launch_bounds__(THREADS) void gemm_ns_kernel(const GemmTile *__rest
   }
 }
 
+// ------------------------------------------------------------------ 256-tiles
+// Chunks whose tiles are all 256 x 256 (T = 256 on sides that are multiples of 256) run
+// each product of a tile in one workgroup: eight waves of 64 x 128 cover the whole
+// 256 x 256 output, so the tile's operands are streamed once per product instead of
+// once per 128-block (three or four times).  The symmetric products compute every block
+// (no mirror); K = 256 in slices of 32 through two LDS stages.  bf16 and bf16x3 planes.
+constexpr int T2 = 256, T2_THREADS = 512, T2_BK = 32;
+
+template <int PREC, int MODE>
+struct T2Lds {
+  static constexpr int NPL = PREC == PREC_BF16X3 ? 2 : 1;   // planes staged
+  static constexpr int RP = T2_BK + 8;                      // row panel pitch (elements)
+  static constexpr int CP = T2 + 8;                         // column panel pitch (update)
+  static constexpr int ROWT = T2 * RP * 2;                  // one plane of the row panel
+  static constexpr int COLT = T2_BK * CP * 2;               // one plane of the column panel
+  static constexpr int STAGE = NPL * (ROWT + (MODE == MODE_UPDATE ? COLT : 0));
+  static constexpr int SP = T2 + 4;                         // fp32 staging pitch
+  static constexpr int STG = (T2 / 2) * SP * 4;             // D^T of one column half
+  static constexpr int BYTES = 2 * STAGE > STG ? 2 * STAGE : STG;
+  static constexpr int NQ = T2 * (T2_BK / 8) / T2_THREADS;  // 16-byte chunks per thread, plane, operand
+  static_assert(T2 * (T2_BK / 8) % T2_THREADS == 0 && T2_BK * (T2 / 8) == T2 * (T2_BK / 8), "whole chunks");
+  static_assert(BYTES <= 160 * 1024, "LDS");
+};
+
+template <int PREC, int MODE>
+__global__ __launch_bounds__(T2_THREADS) void gemm_t256_kernel(const GemmTile *__restrict__ tiles, int first,
+                                                               char *ws, GemmParams gp) {
+  static_assert(PREC == PREC_BF16 || PREC == PREC_BF16X3, "bf16 planes");
+  using LD = T2Lds<PREC, MODE>;
+  __shared__ __attribute__((aligned(16))) char lds[LD::BYTES];
+  // every tile of the chunk is 256 x 256 with ldx = lda = 256 (the planner's chunk kind)
+  const TileG t = tile_of(tiles, first + (int)blockIdx.x);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;   // rows 64 wm.., columns 128 wn..
+  const int li = lane & 31, half = lane >> 5;
+
+  const Planes<PREC> Xc{ws + (gp.xsel ? t.x1 : t.x0), T2, T2};
+  const Planes<PREC> Xn{ws + (gp.xsel ? t.x0 : t.x1), T2, T2};
+  const Planes<PREC> A{ws + t.a, T2, T2};
+  const Planes<PREC> B{ws + t.b, T2, T2};
+  // row operand: X (Gram), A (square), B (update); the symmetric products' column
+  // operand is the same panel, the update's is X read along its columns
+  const Planes<PREC> Lp = MODE == MODE_GRAM ? Xc : (MODE == MODE_SQUARE ? A : B);
+
+  u32x4 rl_[LD::NPL * LD::NQ], rr_[LD::NPL * LD::NQ];
+  auto load = [&](int kb) {
+#pragma unroll
+    for (int pl = 0; pl < LD::NPL; ++pl) {
+      const __bf16 *lb = pl ? Lp.lo() : Lp.hi();
+      const __bf16 *xb = pl ? Xc.lo() : Xc.hi();
+#pragma unroll
+      for (int q = 0; q < LD::NQ; ++q) {
+        const int idx = tid + q * T2_THREADS;
+        const int row = idx / (T2_BK / 8), ch = idx % (T2_BK / 8);
+        rl_[pl * LD::NQ + q] = *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(lb + (int64_t)row * T2 + kb + ch * 8));
+        if constexpr (MODE == MODE_UPDATE) {
+          const int kr = idx / (T2 / 8), cc = idx % (T2 / 8);
+          rr_[pl * LD::NQ + q] = *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(xb + (int64_t)(kb + kr) * T2 + cc * 8));
+        }
+      }
+    }
+  };
+  auto store = [&](char *stage) {
+#pragma unroll
+    for (int pl = 0; pl < LD::NPL; ++pl) {
+#pragma unroll
+      for (int q = 0; q < LD::NQ; ++q) {
+        const int idx = tid + q * T2_THREADS;
+        const int row = idx / (T2_BK / 8), ch = idx % (T2_BK / 8);
+        *reinterpret_cast<u32x4 *>(stage + pl * LD::ROWT + (row * LD::RP + ch * 8) * 2) = rl_[pl * LD::NQ + q];
+        if constexpr (MODE == MODE_UPDATE) {
+          const int kr = idx / (T2 / 8), cc = idx % (T2 / 8);
+          *reinterpret_cast<u32x4 *>(stage + LD::NPL * LD::ROWT + pl * LD::COLT + (kr * LD::CP + cc * 8) * 2) =
+              rr_[pl * LD::NQ + q];
+        }
+      }
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = f32x16{};
+  auto compute = [&](const char *stage) {
+    const __bf16 *L0 = reinterpret_cast<const __bf16 *>(stage);
+    const __bf16 *L1 = reinterpret_cast<const __bf16 *>(stage + LD::ROWT);
+    const __bf16 *C0 = reinterpret_cast<const __bf16 *>(stage + LD::NPL * LD::ROWT);
+    const __bf16 *C1 = reinterpret_cast<const __bf16 *>(stage + LD::NPL * LD::ROWT + LD::COLT);
+#pragma unroll
+    for (int kc = 0; kc < T2_BK; kc += 16) {
+      const int k = kc + 8 * half;
+      bf16x8 lh[2], ll[2], rh[4], rl[4];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        lh[b] = *reinterpret_cast<const bf16x8 *>(L0 + (wm * 64 + b * 32 + li) * LD::RP + k);
+        if constexpr (PREC == PREC_BF16X3)
+          ll[b] = *reinterpret_cast<const bf16x8 *>(L1 + (wm * 64 + b * 32 + li) * LD::RP + k);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if constexpr (MODE == MODE_UPDATE) {
+          rh[b] = tr_frag(C0, LD::CP, k, wn * 128 + b * 32, lane);
+          if constexpr (PREC == PREC_BF16X3) rl[b] = tr_frag(C1, LD::CP, k, wn * 128 + b * 32, lane);
+        } else {
+          rh[b] = *reinterpret_cast<const bf16x8 *>(L0 + (wn * 128 + b * 32 + li) * LD::RP + k);
+          if constexpr (PREC == PREC_BF16X3)
+            rl[b] = *reinterpret_cast<const bf16x8 *>(L1 + (wn * 128 + b * 32 + li) * LD::RP + k);
+        }
+      }
+      if constexpr (PREC == PREC_BF16X3) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = mma_bf16(ll[bi], rh[bj], acc[bi][bj]);
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = mma_bf16(lh[bi], rl[bj], acc[bi][bj]);
+      }
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = mma_bf16(lh[bi], rh[bj], acc[bi][bj]);
+    }
+  };
+
+  // the next slice's loads are in flight while the MFMAs read the current stage
+  load(0);
+  store(lds);
+  __syncthreads();
+  int cur = 0;
+  for (int kb = 0; kb < T2; kb += T2_BK) {
+    const bool more = kb + T2_BK < T2;
+    if (more) load(kb + T2_BK);
+    compute(lds + cur * LD::STAGE);
+    if (more) store(lds + (cur ^ 1) * LD::STAGE);
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  // ---- epilogue, one column half at a time: D^T of the half staged in LDS (fp32), then
+  // rows written with 16-element stores
+  float *st = reinterpret_cast<float *>(lds);
+  const float a = gp.a, b = gp.b, c = gp.c;
+  const bool fold = gp.fold != 0;
+  const Planes<PREC> O = MODE == MODE_GRAM ? (c != 0.f ? A : B) : (MODE == MODE_SQUARE ? B : Xn);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (wn == h) {
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int il = wm * 64 + bi * 32 + 8 * g + 4 * half;
+            const int jl = bj * 32 + li;
+            *reinterpret_cast<f32x4 *>(st + jl * LD::SP + il) =
+                f32x4{acc[bi][bj][4 * g], acc[bi][bj][4 * g + 1], acc[bi][bj][4 * g + 2], acc[bi][bj][4 * g + 3]};
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q4 = 0; q4 < T2 * (T2 / 2 / 16) / T2_THREADS; ++q4) {
+      const int u = tid + q4 * T2_THREADS;
+      const int i = u >> 3, jl = (u & 7) * 16;   // row i, columns 128 h + jl .. +15
+      const int j = h * (T2 / 2) + jl;
+      float e[16];
+      if constexpr (MODE == MODE_SQUARE) {
+        A.get16(i, j, e);
+      } else if constexpr (MODE == MODE_UPDATE) {
+        if (!fold) Xc.get16(i, j, e);
+      }
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const float d = st[(jl + q) * LD::SP + i];
+        const bool dg = fold && i == j + q;
+        if constexpr (MODE == MODE_GRAM) {
+          v[q] = c != 0.f ? d : b * d + (dg ? a : 0.f);
+        } else if constexpr (MODE == MODE_SQUARE) {
+          v[q] = __builtin_fmaf(c, d, b * e[q]) + (dg ? a : 0.f);
+        } else {
+          v[q] = fold ? d : __builtin_fmaf(a, e[q], d);
+        }
+      }
+      O.put16(i, j, v);
+    }
+    __syncthreads();   // the staging read before the next half lands
+  }
+}
+
 template <typename S, int PREC>
 hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmChunkLaunch &c, char *ws,
                      const NSParams &p, hipStream_t stream) {
   auto grid = [](int64_t n) { return dim3((unsigned)n); };
   if (c.n_mom > 0x7fffffff || c.n_stg > 0x7fffffff || c.n_sym > 0x7fffffff || c.n_upd > 0x7fffffff ||
-      c.n_app > 0x7fffffff)
+      c.n_app > 0x7fffffff || c.tile_first + c.tile_n > 0x7fffffff)
     return hipErrorInvalidValue;
+  if (c.t256 && PREC != PREC_BF16 && PREC != PREC_BF16X3) return hipErrorInvalidValue;
   if (c.n_mom) hipLaunchKernelGGL(gemm_momentum_kernel<S>, grid(c.n_mom), dim3(THREADS), 0, stream, layers, tiles, c.mom, ws, p.beta);
   if (c.tile_n) hipLaunchKernelGGL(gemm_norm_kernel, grid(c.tile_n), dim3(THREADS), 0, stream, tiles, (int)c.tile_first, ws, p.eps, p.identity);
   if (c.n_stg) hipLaunchKernelGGL((gemm_stage_kernel<S, PREC>), grid(c.n_stg), dim3(THREADS), 0, stream, layers, tiles, c.stg, ws);
@@ -751,7 +948,21 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
       hipLaunchKernelGGL((gemm_ns_kernel<PREC, MODE_UPDATE, BK>), grid(c.n_upd), dim3(THREADS), 0, stream, tiles, c.upd, ws, gp);
     }
   };
-  if (c.long_k) {
+  if constexpr (PREC == PREC_BF16 || PREC == PREC_BF16X3) {
+    if (c.t256) {
+      for (int it = 0; it < p.steps; ++it) {
+        gp.xsel = it & 1;
+        const dim3 g((unsigned)c.tile_n), bl(T2_THREADS);
+        const int f = (int)c.tile_first;
+        hipLaunchKernelGGL((gemm_t256_kernel<PREC, MODE_GRAM>), g, bl, 0, stream, tiles, f, ws, gp);
+        if (p.c != 0.f) hipLaunchKernelGGL((gemm_t256_kernel<PREC, MODE_SQUARE>), g, bl, 0, stream, tiles, f, ws, gp);
+        hipLaunchKernelGGL((gemm_t256_kernel<PREC, MODE_UPDATE>), g, bl, 0, stream, tiles, f, ws, gp);
+      }
+    }
+  }
+  if (c.t256) {
+    // products launched above (bf16 planes only: the planner marks no fp32 chunk)
+  } else if (c.long_k) {
     products(std::integral_constant<int, 64>{});
   } else {
     products(std::integral_constant<int, 32>{});

@@ -54,6 +54,12 @@ GemmSizes gemm_sizes(int64_t h, int64_t w) {
   z.red = align256((size_t)(z.nred + 1) * 4);
   return z;
 }
+
+// Tiles of the large-tile path that the 256-tile product kernel runs: exactly 256 x 256
+// (so ldx = lda = 256), with bf16 planes (every precision except fp32).
+bool t256_kind(const GemmTile &g, int prec) {
+  return g.r == 256 && g.s == 256 && prec != HIMUON_PREC_F32;
+}
 }  // namespace
 
 size_t gemm_tile_workspace(int64_t h, int64_t w) {
@@ -286,7 +292,11 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
           g.nred = (int32_t)z.nred;
           gt.push_back(g);
           max_ws = std::max(max_ws, gemm_tile_workspace(h, w));
-          {
+          if (t256_kind(g, prec)) {
+            // one workgroup per tile and product, every 256 x 256 block computed
+            const double e3 = 2.0 * 256.0 * 256.0 * 256.0;
+            issued += (double)K * split * (e3 + (quintic ? e3 : 0.0) + e3);
+          } else {
             // 128-blocks as launched: symmetric products on the upper blocks only, K
             // padded to 64; the update over all blocks
             const double nb = (double)cdiv(r, 128), nbs = (double)cdiv(z.ldx, 128);
@@ -326,6 +336,8 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
       ch.long_k = true;
       for (int64_t i = first; i < end; ++i)
         ch.long_k = ch.long_k && gt[(size_t)i].lda >= kGemmLongK && gt[(size_t)i].ldx >= kGemmLongK;
+      // chunks are cut where the kind changes, so the first tile's kind is the chunk's
+      ch.t256 = end > first && t256_kind(gt[(size_t)first], prec);
       // Products of long-K chunks list their 128-blocks in groups of kGemmGroupRows block
       // rows, column by column inside a group, so that the workgroups in flight on one
       // XCD (a contiguous run of the list) share the K slices of a few row and column
@@ -341,7 +353,9 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
         for (int32_t bi = 0; bi < (int32_t)cdiv(g.r, sr); ++bi)
           for (int32_t bj = 0; bj < (int32_t)cdiv(g.ldx, sc); ++bj) wstg.push_back(GemmWork{ti, bi, bj});
         const int32_t nb = (int32_t)cdiv(g.r, 128), nbj = (int32_t)cdiv(g.ldx, 128);
-        if (grp > 0) {
+        if (ch.t256) {
+          // products address their tiles directly: no block lists
+        } else if (grp > 0) {
           for (int32_t b0 = 0; b0 < nb; b0 += grp) {
             const int32_t b1 = std::min(nb, b0 + grp);
             for (int32_t bj = b0; bj < nb; ++bj)
@@ -368,7 +382,8 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
     };
     for (size_t i = 0; i < gt.size(); ++i) {
       const size_t need = gemm_tile_workspace(gt[i].h, gt[i].w);
-      if (cur + need > c.workspace_budget && i > (size_t)first) {
+      const bool kind_change = i > (size_t)first && t256_kind(gt[i], prec) != t256_kind(gt[(size_t)first], prec);
+      if ((cur + need > c.workspace_budget || kind_change) && i > (size_t)first) {
         close_chunk((int64_t)i);
         first = (int64_t)i;
         cur = 0;

@@ -31,6 +31,7 @@ struct GemmChunk {
   size_t ws_bytes;    // workspace the chunk uses
   Range mom, stg, sym, upd, app;  // ranges in the work lists
   bool long_k;        // every GEMM K of its tiles >= kGemmLongK: K slices of 64
+  bool t256;          // every tile 256 x 256 and bf16 planes: one workgroup per tile product
 };
 
 struct Plan {
