@@ -749,8 +749,10 @@ struct T2Lds {
   static constexpr int ROWT = T2 * RP * 2;                  // one plane of the row panel
   static constexpr int COLT = T2_BK * CP * 2;               // one plane of the column panel
   static constexpr int STAGE = NPL * (ROWT + (MODE == MODE_UPDATE ? COLT : 0));
-  static constexpr int SP = T2 + 4;                         // fp32 staging pitch
-  static constexpr int STG = (T2 / 2) * SP * 4;             // D^T of one column half
+  // fp32 staging of one column half of D, row-major: rows 4 apart (the two lane halves
+  // of an accumulator) fall 32 banks apart, and a row's 16-column pieces are 16-byte reads
+  static constexpr int SP = T2 / 2 + 8;
+  static constexpr int STG = T2 * SP * 4;
   static constexpr int BYTES = 2 * STAGE > STG ? 2 * STAGE : STG;
   static constexpr int NQ = T2 * (T2_BK / 8) / T2_THREADS;  // 16-byte chunks per thread, plane, operand
   static_assert(T2 * (T2_BK / 8) % T2_THREADS == 0 && T2_BK * (T2 / 8) == T2 * (T2_BK / 8), "whole chunks");
@@ -874,8 +876,8 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_t256_kernel(const GemmTile *_
     cur ^= 1;
   }
 
-  // ---- epilogue, one column half at a time: D^T of the half staged in LDS (fp32), then
-  // rows written with 16-element stores
+  // ---- epilogue, one column half at a time: the half staged in LDS (fp32), then rows
+  // written with 16-element stores
   float *st = reinterpret_cast<float *>(lds);
   const float a = gp.a, b = gp.b, c = gp.c;
   const bool fold = gp.fold != 0;
@@ -891,8 +893,8 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_t256_kernel(const GemmTile *_
           for (int g = 0; g < 4; ++g) {
             const int il = wm * 64 + bi * 32 + 8 * g + 4 * half;
             const int jl = bj * 32 + li;
-            *reinterpret_cast<f32x4 *>(st + jl * LD::SP + il) =
-                f32x4{acc[bi][bj][4 * g], acc[bi][bj][4 * g + 1], acc[bi][bj][4 * g + 2], acc[bi][bj][4 * g + 3]};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[(il + e) * LD::SP + jl] = acc[bi][bj][4 * g + e];
           }
     }
     __syncthreads();
@@ -907,10 +909,17 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_t256_kernel(const GemmTile *_
       } else if constexpr (MODE == MODE_UPDATE) {
         if (!fold) Xc.get16(i, j, e);
       }
+      float dv[16];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(st + i * LD::SP + jl + 4 * m);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) dv[4 * m + e2] = x[e2];
+      }
       float v[16];
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const float d = st[(jl + q) * LD::SP + i];
+        const float d = dv[q];
         const bool dg = fold && i == j + q;
         if constexpr (MODE == MODE_GRAM) {
           v[q] = c != 0.f ? d : b * d + (dg ? a : 0.f);
