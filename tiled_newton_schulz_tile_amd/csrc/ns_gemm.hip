@@ -738,24 +738,27 @@ __global__ __launch_bounds__(THREADS) void gemm_ns_kernel(const GemmTile *__rest
 // each product of a tile in one workgroup: eight waves of 64 x 128 cover the whole
 // 256 x 256 output, so the tile's operands are streamed once per product instead of
 // once per 128-block (three or four times).  The symmetric products compute every block
-// (no mirror); K = 256 in slices of 32 through two LDS stages.  bf16 and bf16x3 planes.
-constexpr int T2 = 256, T2_THREADS = 512, T2_BK = 32;
+// (no mirror); K = 256 through two LDS stages, in slices of 64 (whole 128-byte lines,
+// twice the bytes in flight) for the symmetric products and of 32 for the update, whose
+// two operand panels leave no registers for more.  bf16 and bf16x3 planes.
+constexpr int T2 = 256, T2_THREADS = 512;
 
 template <int PREC, int MODE>
 struct T2Lds {
+  static constexpr int BK = MODE == MODE_UPDATE ? 32 : 64;  // K slice
   static constexpr int NPL = PREC == PREC_BF16X3 ? 2 : 1;   // planes staged
-  static constexpr int RP = T2_BK + 8;                      // row panel pitch (elements)
+  static constexpr int RP = BK + 8;                         // row panel pitch (elements)
   static constexpr int CP = T2 + 8;                         // column panel pitch (update)
   static constexpr int ROWT = T2 * RP * 2;                  // one plane of the row panel
-  static constexpr int COLT = T2_BK * CP * 2;               // one plane of the column panel
+  static constexpr int COLT = BK * CP * 2;                  // one plane of the column panel
   static constexpr int STAGE = NPL * (ROWT + (MODE == MODE_UPDATE ? COLT : 0));
   // fp32 staging of one column half of D, row-major: rows 4 apart (the two lane halves
   // of an accumulator) fall 32 banks apart, and a row's 16-column pieces are 16-byte reads
   static constexpr int SP = T2 / 2 + 8;
   static constexpr int STG = T2 * SP * 4;
   static constexpr int BYTES = 2 * STAGE > STG ? 2 * STAGE : STG;
-  static constexpr int NQ = T2 * (T2_BK / 8) / T2_THREADS;  // 16-byte chunks per thread, plane, operand
-  static_assert(T2 * (T2_BK / 8) % T2_THREADS == 0 && T2_BK * (T2 / 8) == T2 * (T2_BK / 8), "whole chunks");
+  static constexpr int NQ = T2 * (BK / 8) / T2_THREADS;     // 16-byte chunks per thread, plane, operand
+  static_assert(T2 * (BK / 8) % T2_THREADS == 0 && BK * (T2 / 8) == T2 * (BK / 8), "whole chunks");
   static_assert(BYTES <= 160 * 1024, "LDS");
 };
 
@@ -788,7 +791,7 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_t256_kernel(const GemmTile *_
 #pragma unroll
       for (int q = 0; q < LD::NQ; ++q) {
         const int idx = tid + q * T2_THREADS;
-        const int row = idx / (T2_BK / 8), ch = idx % (T2_BK / 8);
+        const int row = idx / (LD::BK / 8), ch = idx % (LD::BK / 8);
         rl_[pl * LD::NQ + q] = *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(lb + (int64_t)row * T2 + kb + ch * 8));
         if constexpr (MODE == MODE_UPDATE) {
           const int kr = idx / (T2 / 8), cc = idx % (T2 / 8);
@@ -803,7 +806,7 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_t256_kernel(const GemmTile *_
 #pragma unroll
       for (int q = 0; q < LD::NQ; ++q) {
         const int idx = tid + q * T2_THREADS;
-        const int row = idx / (T2_BK / 8), ch = idx % (T2_BK / 8);
+        const int row = idx / (LD::BK / 8), ch = idx % (LD::BK / 8);
         *reinterpret_cast<u32x4 *>(stage + pl * LD::ROWT + (row * LD::RP + ch * 8) * 2) = rl_[pl * LD::NQ + q];
         if constexpr (MODE == MODE_UPDATE) {
           const int kr = idx / (T2 / 8), cc = idx % (T2 / 8);
@@ -825,7 +828,7 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_t256_kernel(const GemmTile *_
     const __bf16 *C0 = reinterpret_cast<const __bf16 *>(stage + LD::NPL * LD::ROWT);
     const __bf16 *C1 = reinterpret_cast<const __bf16 *>(stage + LD::NPL * LD::ROWT + LD::COLT);
 #pragma unroll
-    for (int kc = 0; kc < T2_BK; kc += 16) {
+    for (int kc = 0; kc < LD::BK; kc += 16) {
       const int k = kc + 8 * half;
       bf16x8 lh[2], ll[2], rh[4], rl[4];
 #pragma unroll
@@ -867,9 +870,9 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_t256_kernel(const GemmTile *_
   store(lds);
   __syncthreads();
   int cur = 0;
-  for (int kb = 0; kb < T2; kb += T2_BK) {
-    const bool more = kb + T2_BK < T2;
-    if (more) load(kb + T2_BK);
+  for (int kb = 0; kb < T2; kb += LD::BK) {
+    const bool more = kb + LD::BK < T2;
+    if (more) load(kb + LD::BK);
     compute(lds + cur * LD::STAGE);
     if (more) store(lds + (cur ^ 1) * LD::STAGE);
     __syncthreads();
