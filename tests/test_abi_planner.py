@@ -127,6 +127,33 @@ def test_bf16f8_issues_one_bf16_and_two_half_rate_products():
     hm.himuon_plan_destroy(p)
 
 
+def test_256_tile_chunks_and_work():
+    # Tiles of exactly 256 x 256 with bf16 planes run each product as one workgroup per
+    # tile over the whole 256 x 256 output, so the symmetric products issue all four
+    # 128-blocks: three bf16 products (bf16x3) of 2 * 256^3 per product, Gram + square +
+    # update = 3x the algorithmic work of the quintic step
+    p = plan_for(synth.STACKS["llama3-8b-32L"], 256, precision=hm.PREC_BF16X3)
+    st = hm.himuon_plan_stats(p)
+    hm.himuon_plan_destroy(p)
+    assert st["tiles"] == st["gemm_tiles"] == 6979321856 // 256 ** 2
+    assert st["ns_flops"] == 6 * 6979321856 * 256 * 5
+    assert st["issued_flops"] == 3 * st["ns_flops"]
+    # fp32 keeps the 128-block kernel: upper blocks of the symmetric products (3 of 4)
+    p = plan_for(synth.STACKS["llama3-8b-32L"], 256, precision=hm.PREC_F32)
+    st = hm.himuon_plan_stats(p)
+    hm.himuon_plan_destroy(p)
+    assert st["issued_flops"] == 5 * (0.75 * 2 + 0.75 * 2 + 2) * 256 ** 3 * (6979321856 // 256 ** 2)
+    # chunks are cut where the kind changes: 512x512 and the two full tiles of 300x600
+    # (6 tiles of 256), then its three ragged tiles of the large-tile path (256x88 and
+    # two 44x256; its 44x88 tile goes to the fused kernel), then 256x256 again
+    shapes = [(512, 512), (300, 600), (256, 256)]
+    for prec, chunks in ((hm.PREC_BF16X3, 3), (hm.PREC_BF16, 3), (hm.PREC_BF16F8, 3), (hm.PREC_F32, 1)):
+        p = plan_for(shapes, 256, precision=prec)
+        st = hm.himuon_plan_stats(p)
+        hm.himuon_plan_destroy(p)
+        assert (st["tiles"], st["gemm_tiles"], st["chunks"]) == (11, 10, chunks), prec
+
+
 @pytest.mark.parametrize("coeffs,K,ok", [
     (hm.QUINTIC, 5, True), (hm.QUINTIC, 100, True), (hm.CUBIC, 8, True),
     ((2.0, -1.5, 0.5), 6, True), ((10.0, 10.0, 10.0), 5, False), ((3.0, 0.0, 0.0), 200, False),
