@@ -397,6 +397,25 @@ def test_large_tiles_and_full(T, prec, state, coeffs, K):
         assert_bar(U, O, prec, tight=None if prec not in (2, 3) else 5e-3)
 
 
+# Sides that are multiples of 256 take the 256-block product kernel (at FULL and for
+# tiles larger than 256), exactly 256 x 256 tiles the one-workgroup-per-tile kernel; the
+# stack mixes both kinds with 128-block matrices, so chunks are cut between them.
+MULT256 = [(512, 768), (768, 512), (512, 512), (256, 1024), (300, 600), (256, 256)]
+
+
+@pytest.mark.parametrize("T", [0, 512])
+@pytest.mark.parametrize("prec,state", [(2, torch.bfloat16), (1, torch.bfloat16), (3, torch.bfloat16)])
+@pytest.mark.parametrize("coeffs,K", [(Q, 5), (C, 5), (Q, 8)])
+def test_256_block_products(T, prec, state, coeffs, K):
+    if prec == 1 and coeffs == Q:
+        pytest.skip("plain bf16 operands with quintic coefficients are outside the bf16 bar")
+    mats = [power_law(h, w, 1300 + i) for i, (h, w) in enumerate(MULT256)]
+    (res,), _ = gpu_step(mats, T, K=K, coeffs=coeffs, prec=prec, state=state)
+    for (W, M, U), G in zip(res, mats):
+        O = oracle.tiled_ns(M.double().numpy(), T, K, coeffs)
+        assert_bar(U, O, prec, tight=None if prec not in (2, 3) else 5e-3)
+
+
 def test_chunking_is_invisible():
     # a budget that fits one tile at a time gives bit-identical results to one chunk
     _need_gpu()

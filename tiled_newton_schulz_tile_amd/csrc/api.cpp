@@ -196,6 +196,7 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
       cl.n_app = ch.app.n;
       cl.long_k = ch.long_k ? 1 : 0;
       cl.t256 = ch.t256 ? 1 : 0;
+      cl.b256 = ch.b256 ? 1 : 0;
       hipError_t e = himuon::launch_gemm_chunk(gemm_prec, c.state_dtype == HIMUON_BF16, dl, dgt, cl,
                                                reinterpret_cast<char *>(workspace), prm, stream);
       if (e != hipSuccess) return hip_fail(e, "large-tile kernel launch");

@@ -120,6 +120,8 @@ struct GemmChunkLaunch {
   int32_t long_k;                       // K slices of 64 (one LDS stage) instead of 32 (two)
   int32_t t256;                         // every tile 256 x 256 (bf16 planes): one workgroup
                                         // per tile and product; sym / upd lists unused
+  int32_t b256;                         // every side a multiple of 256 (bf16 planes): sym /
+                                        // upd lists hold 256-blocks
 };
 // Runs one full step for the tiles of a chunk: momentum and partial norms, norm
 // reduction, staging of X0, K Newton-Schulz steps as grouped MFMA GEMMs, update.

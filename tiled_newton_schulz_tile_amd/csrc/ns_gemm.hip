@@ -938,6 +938,263 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_t256_kernel(const GemmTile *_
   }
 }
 
+// ------------------------------------------------------------------ 256-blocks
+// Chunks of matrices (or tiles) whose two sides are multiples of 256, other than single
+// 256 x 256 tiles, run each product in 256 x 256 output blocks: eight waves of 64 x 128,
+// K in slices of 32 through two LDS stages, half the operand-panel traffic per output
+// element of the 128-blocks.  The symmetric products compute the blocks with bi <= bj
+// and write the off-diagonal ones to both positions; a diagonal block's two operand
+// panels are the same rows, loaded and staged once (SAME).
+template <int PREC, int MODE>
+struct B2Lds {
+  static constexpr int BK = 32;
+  static constexpr int NPL = PREC == PREC_BF16X3 ? 2 : 1;
+  static constexpr int RP = BK + 8, CP = T2 + 8;
+  static constexpr int ROWT = T2 * RP * 2;                      // one plane of a row panel
+  static constexpr int COLT = BK * CP * 2;                      // one plane of the column panel
+  static constexpr int RT = MODE == MODE_UPDATE ? COLT : ROWT;  // one plane of the column operand
+  static constexpr int STAGE = NPL * (ROWT + RT);
+  static constexpr int SP = T2 / 2 + 8;                         // D of a column half, row-major
+  static constexpr int SPT = T2 + 4;                            // its transpose (mirror pass)
+  static constexpr int STG = T2 * SP * 4 > (T2 / 2) * SPT * 4 ? T2 * SP * 4 : (T2 / 2) * SPT * 4;
+  static constexpr int BYTES = 2 * STAGE > STG ? 2 * STAGE : STG;
+  static constexpr int NQ = T2 * (BK / 8) / T2_THREADS;
+  static_assert(T2 * (BK / 8) % T2_THREADS == 0 && BK * (T2 / 8) == T2 * (BK / 8), "whole chunks");
+  static_assert(BYTES <= 160 * 1024, "LDS");
+};
+
+template <int PREC, int MODE, bool SAME>
+__device__ __forceinline__ void b256_block(const TileG &t, int i0, int j0, char *ws, const GemmParams &gp,
+                                           char *lds) {
+  using LD = B2Lds<PREC, MODE>;
+  constexpr int BK = LD::BK;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;   // rows 64 wm.., columns 128 wn.. of the block
+  const int li = lane & 31, half = lane >> 5;
+
+  const Planes<PREC> Xc{ws + (gp.xsel ? t.x1 : t.x0), t.r, t.ldx};
+  const Planes<PREC> Xn{ws + (gp.xsel ? t.x0 : t.x1), t.r, t.ldx};
+  const Planes<PREC> A{ws + t.a, t.r, t.lda};
+  const Planes<PREC> B{ws + t.b, t.r, t.lda};
+  const Planes<PREC> Lp = MODE == MODE_GRAM ? Xc : (MODE == MODE_SQUARE ? A : B);
+  const int kdim = MODE == MODE_GRAM ? t.ldx : t.lda;
+
+  u32x4 rl_[LD::NPL * LD::NQ], rr_[LD::NPL * LD::NQ];
+  auto load = [&](int kb) {
+#pragma unroll
+    for (int pl = 0; pl < LD::NPL; ++pl) {
+      const __bf16 *lb = pl ? Lp.lo() : Lp.hi();
+      const __bf16 *xb = pl ? Xc.lo() : Xc.hi();
+#pragma unroll
+      for (int q = 0; q < LD::NQ; ++q) {
+        const int idx = tid + q * T2_THREADS;
+        const int row = idx / (BK / 8), ch = idx % (BK / 8);
+        rl_[pl * LD::NQ + q] =
+            *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(lb + (int64_t)(i0 + row) * Lp.ld + kb + ch * 8));
+        if constexpr (MODE == MODE_UPDATE) {
+          const int kr = idx / (T2 / 8), cc = idx % (T2 / 8);
+          rr_[pl * LD::NQ + q] =
+              *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(xb + (int64_t)(kb + kr) * Xc.ld + j0 + cc * 8));
+        } else if constexpr (!SAME) {
+          rr_[pl * LD::NQ + q] =
+              *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(lb + (int64_t)(j0 + row) * Lp.ld + kb + ch * 8));
+        }
+      }
+    }
+  };
+  auto store = [&](char *stage) {
+#pragma unroll
+    for (int pl = 0; pl < LD::NPL; ++pl) {
+#pragma unroll
+      for (int q = 0; q < LD::NQ; ++q) {
+        const int idx = tid + q * T2_THREADS;
+        const int row = idx / (BK / 8), ch = idx % (BK / 8);
+        *reinterpret_cast<u32x4 *>(stage + pl * LD::ROWT + (row * LD::RP + ch * 8) * 2) = rl_[pl * LD::NQ + q];
+        char *rt = stage + LD::NPL * LD::ROWT + pl * LD::RT;
+        if constexpr (MODE == MODE_UPDATE) {
+          const int kr = idx / (T2 / 8), cc = idx % (T2 / 8);
+          *reinterpret_cast<u32x4 *>(rt + (kr * LD::CP + cc * 8) * 2) = rr_[pl * LD::NQ + q];
+        } else if constexpr (!SAME) {
+          *reinterpret_cast<u32x4 *>(rt + (row * LD::RP + ch * 8) * 2) = rr_[pl * LD::NQ + q];
+        }
+      }
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = f32x16{};
+  auto compute = [&](const char *stage) {
+    const __bf16 *L0 = reinterpret_cast<const __bf16 *>(stage);
+    const __bf16 *L1 = reinterpret_cast<const __bf16 *>(stage + LD::ROWT);
+    const char *rs = SAME ? stage : stage + LD::NPL * LD::ROWT;
+    const __bf16 *R0 = reinterpret_cast<const __bf16 *>(rs);
+    const __bf16 *R1 = reinterpret_cast<const __bf16 *>(rs + (SAME ? LD::ROWT : LD::RT));
+#pragma unroll
+    for (int kc = 0; kc < BK; kc += 16) {
+      const int k = kc + 8 * half;
+      bf16x8 lh[2], ll[2], rh[4], rl[4];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        lh[b] = *reinterpret_cast<const bf16x8 *>(L0 + (wm * 64 + b * 32 + li) * LD::RP + k);
+        if constexpr (PREC == PREC_BF16X3)
+          ll[b] = *reinterpret_cast<const bf16x8 *>(L1 + (wm * 64 + b * 32 + li) * LD::RP + k);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if constexpr (MODE == MODE_UPDATE) {
+          rh[b] = tr_frag(R0, LD::CP, k, wn * 128 + b * 32, lane);
+          if constexpr (PREC == PREC_BF16X3) rl[b] = tr_frag(R1, LD::CP, k, wn * 128 + b * 32, lane);
+        } else {
+          rh[b] = *reinterpret_cast<const bf16x8 *>(R0 + (wn * 128 + b * 32 + li) * LD::RP + k);
+          if constexpr (PREC == PREC_BF16X3)
+            rl[b] = *reinterpret_cast<const bf16x8 *>(R1 + (wn * 128 + b * 32 + li) * LD::RP + k);
+        }
+      }
+      if constexpr (PREC == PREC_BF16X3) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = mma_bf16(ll[bi], rh[bj], acc[bi][bj]);
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = mma_bf16(lh[bi], rl[bj], acc[bi][bj]);
+      }
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = mma_bf16(lh[bi], rh[bj], acc[bi][bj]);
+    }
+  };
+
+  load(0);
+  store(lds);
+  __syncthreads();
+  int cur = 0;
+  for (int kb = 0; kb < kdim; kb += BK) {
+    const bool more = kb + BK < kdim;
+    if (more) load(kb + BK);
+    compute(lds + cur * LD::STAGE);
+    if (more) store(lds + (cur ^ 1) * LD::STAGE);
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  // ---- epilogue, one column half at a time: the half staged row-major for the block's
+  // own rows, then (off-diagonal symmetric blocks) transposed for the mirrored rows
+  float *st = reinterpret_cast<float *>(lds);
+  const float a = gp.a, b = gp.b, c = gp.c;
+  const bool fold = gp.fold != 0;
+  const Planes<PREC> O = MODE == MODE_GRAM ? (c != 0.f ? A : B) : (MODE == MODE_SQUARE ? B : Xn);
+  // value stored at output (i, j) from the product d; e: element (i, j) of the addend
+  auto finish = [&](float d, float e, int i, int j) -> float {
+    const bool dg = fold && i == j;
+    if constexpr (MODE == MODE_GRAM) {
+      return c != 0.f ? d : b * d + (dg ? a : 0.f);
+    } else if constexpr (MODE == MODE_SQUARE) {
+      return __builtin_fmaf(c, d, b * e) + (dg ? a : 0.f);
+    } else {
+      return fold ? d : __builtin_fmaf(a, e, d);
+    }
+  };
+  auto addend16 = [&](int i, int j, float (&e)[16]) {
+    if constexpr (MODE == MODE_SQUARE) {
+      A.get16(i, j, e);
+    } else if constexpr (MODE == MODE_UPDATE) {
+      if (!fold) Xc.get16(i, j, e);
+    }
+  };
+  constexpr bool MIRROR = MODE != MODE_UPDATE && !SAME;
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    if (wn == h) {
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int il = wm * 64 + bi * 32 + 8 * g + 4 * half, jl = bj * 32 + li;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[(il + e) * LD::SP + jl] = acc[bi][bj][4 * g + e];
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q4 = 0; q4 < T2 * (T2 / 2 / 16) / T2_THREADS; ++q4) {
+      const int u = tid + q4 * T2_THREADS;
+      const int il = u >> 3, jl = (u & 7) * 16;   // block row il, columns 128 h + jl .. +15
+      const int gi = i0 + il, gj = j0 + h * (T2 / 2) + jl;
+      float e[16], dv[16], v[16];
+      addend16(gi, gj, e);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(st + il * LD::SP + jl + 4 * m);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) dv[4 * m + e2] = x[e2];
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = finish(dv[q], e[q], gi, gj + q);
+      O.put16(gi, gj, v);
+    }
+    __syncthreads();
+    if constexpr (MIRROR) {
+      // D^T of the half: row jl (column 128 h + jl of the block) holds the mirrored row
+      if (wn == h) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int il = wm * 64 + bi * 32 + 8 * g + 4 * half, jl = bj * 32 + li;
+              *reinterpret_cast<f32x4 *>(st + jl * LD::SPT + il) =
+                  f32x4{acc[bi][bj][4 * g], acc[bi][bj][4 * g + 1], acc[bi][bj][4 * g + 2], acc[bi][bj][4 * g + 3]};
+            }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q4 = 0; q4 < (T2 / 2) * (T2 / 16) / T2_THREADS; ++q4) {
+        const int u = tid + q4 * T2_THREADS;
+        const int jl = u >> 4, il = (u & 15) * 16;   // mirrored row 128 h + jl, columns il .. +15
+        const int gi = j0 + h * (T2 / 2) + jl, gj = i0 + il;
+        float e[16], dv[16], v[16];
+        addend16(gi, gj, e);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f32x4 x = *reinterpret_cast<const f32x4 *>(st + jl * LD::SPT + il + 4 * m);
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) dv[4 * m + e2] = x[e2];
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = finish(dv[q], e[q], gi, gj + q);
+        O.put16(gi, gj, v);
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <int PREC, int MODE>
+__global__ __launch_bounds__(T2_THREADS) void gemm_b256_kernel(const GemmTile *__restrict__ tiles,
+                                                               const GemmWork *__restrict__ work, char *ws,
+                                                               GemmParams gp) {
+  static_assert(PREC == PREC_BF16 || PREC == PREC_BF16X3, "bf16 planes");
+  __shared__ __attribute__((aligned(16))) char lds[B2Lds<PREC, MODE>::BYTES];
+  const GemmWork wk = work[xcd_work_index()];
+  const TileG t = tile_of(tiles, wk.tile);
+  // sides of every tile of the chunk are multiples of 256 (the planner's chunk kind), so
+  // ldx = s, lda = r and no block reaches past them
+  if (MODE != MODE_UPDATE && wk.bi == wk.bj) {   // uniform over the workgroup
+    b256_block<PREC, MODE, true>(t, wk.bi * T2, wk.bj * T2, ws, gp, lds);
+  } else {
+    b256_block<PREC, MODE, false>(t, wk.bi * T2, wk.bj * T2, ws, gp, lds);
+  }
+}
+
 template <typename S, int PREC>
 hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmChunkLaunch &c, char *ws,
                      const NSParams &p, hipStream_t stream) {
@@ -945,7 +1202,7 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
   if (c.n_mom > 0x7fffffff || c.n_stg > 0x7fffffff || c.n_sym > 0x7fffffff || c.n_upd > 0x7fffffff ||
       c.n_app > 0x7fffffff || c.tile_first + c.tile_n > 0x7fffffff)
     return hipErrorInvalidValue;
-  if (c.t256 && PREC != PREC_BF16 && PREC != PREC_BF16X3) return hipErrorInvalidValue;
+  if ((c.t256 || c.b256) && PREC != PREC_BF16 && PREC != PREC_BF16X3) return hipErrorInvalidValue;
   if (c.n_mom) hipLaunchKernelGGL(gemm_momentum_kernel<S>, grid(c.n_mom), dim3(THREADS), 0, stream, layers, tiles, c.mom, ws, p.beta);
   if (c.tile_n) hipLaunchKernelGGL(gemm_norm_kernel, grid(c.tile_n), dim3(THREADS), 0, stream, tiles, (int)c.tile_first, ws, p.eps, p.identity);
   if (c.n_stg) hipLaunchKernelGGL((gemm_stage_kernel<S, PREC>), grid(c.n_stg), dim3(THREADS), 0, stream, layers, tiles, c.stg, ws);
@@ -972,7 +1229,19 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
       }
     }
   }
-  if (c.t256) {
+  if constexpr (PREC == PREC_BF16 || PREC == PREC_BF16X3) {
+    if (c.b256) {
+      for (int it = 0; it < p.steps; ++it) {
+        gp.xsel = it & 1;
+        const dim3 bl(T2_THREADS);
+        hipLaunchKernelGGL((gemm_b256_kernel<PREC, MODE_GRAM>), grid(c.n_sym), bl, 0, stream, tiles, c.sym, ws, gp);
+        if (p.c != 0.f)
+          hipLaunchKernelGGL((gemm_b256_kernel<PREC, MODE_SQUARE>), grid(c.n_sym), bl, 0, stream, tiles, c.sym, ws, gp);
+        hipLaunchKernelGGL((gemm_b256_kernel<PREC, MODE_UPDATE>), grid(c.n_upd), bl, 0, stream, tiles, c.upd, ws, gp);
+      }
+    }
+  }
+  if (c.t256 || c.b256) {
     // products launched above (bf16 planes only: the planner marks no fp32 chunk)
   } else if (c.long_k) {
     products(std::integral_constant<int, 64>{});

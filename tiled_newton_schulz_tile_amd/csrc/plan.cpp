@@ -55,10 +55,13 @@ GemmSizes gemm_sizes(int64_t h, int64_t w) {
   return z;
 }
 
-// Tiles of the large-tile path that the 256-tile product kernel runs: exactly 256 x 256
-// (so ldx = lda = 256), with bf16 planes (every precision except fp32).
-bool t256_kind(const GemmTile &g, int prec) {
-  return g.r == 256 && g.s == 256 && prec != HIMUON_PREC_F32;
+// Product kernel of a large-path tile (bf16 planes, every precision except fp32):
+// 1: exactly 256 x 256, one workgroup per tile and product; 2: both sides multiples of
+// 256 (so ldx = s and lda = r), 256-blocks; 0: 128-blocks.  Chunks hold one kind.
+int gemm_kind(const GemmTile &g, int prec) {
+  if (prec == HIMUON_PREC_F32) return 0;
+  if (g.r == 256 && g.s == 256) return 1;
+  return g.r % 256 == 0 && g.s % 256 == 0 ? 2 : 0;
 }
 }  // namespace
 
@@ -292,10 +295,17 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
           g.nred = (int32_t)z.nred;
           gt.push_back(g);
           max_ws = std::max(max_ws, gemm_tile_workspace(h, w));
-          if (t256_kind(g, prec)) {
+          const int kind = gemm_kind(g, prec);
+          if (kind == 1) {
             // one workgroup per tile and product, every 256 x 256 block computed
             const double e3 = 2.0 * 256.0 * 256.0 * 256.0;
             issued += (double)K * split * (e3 + (quintic ? e3 : 0.0) + e3);
+          } else if (kind == 2) {
+            // 256-blocks: symmetric products on the upper blocks only; the update over all
+            const double nb = (double)(r / 256), nbs = (double)(s / 256);
+            const double sym = nb * (nb + 1) / 2 * 2.0 * 256 * 256;
+            issued += (double)K * split * (sym * z.ldx + (quintic ? sym * z.lda : 0.0) +
+                                           2.0 * 256 * 256 * nb * nbs * z.lda);
           } else {
             // 128-blocks as launched: symmetric products on the upper blocks only, K
             // padded to 64; the update over all blocks
@@ -337,12 +347,14 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
       for (int64_t i = first; i < end; ++i)
         ch.long_k = ch.long_k && gt[(size_t)i].lda >= kGemmLongK && gt[(size_t)i].ldx >= kGemmLongK;
       // chunks are cut where the kind changes, so the first tile's kind is the chunk's
-      ch.t256 = end > first && t256_kind(gt[(size_t)first], prec);
-      // Products of long-K chunks list their 128-blocks in groups of kGemmGroupRows block
-      // rows, column by column inside a group, so that the workgroups in flight on one
-      // XCD (a contiguous run of the list) share the K slices of a few row and column
-      // panels in that XCD's L2.  Short-K chunks keep the row-major order.
-      const int32_t grp = ch.long_k ? kGemmGroupRows : 0;
+      const int kind = end > first ? gemm_kind(gt[(size_t)first], prec) : 0;
+      ch.t256 = kind == 1;
+      ch.b256 = kind == 2;
+      // Products of long-K chunks list their blocks in groups of block rows (kGemmGroupRows
+      // of 128, half as many of 256), column by column inside a group, so that the
+      // workgroups in flight on one XCD (a contiguous run of the list) share the K slices
+      // of a few row and column panels in that XCD's L2.  Short-K chunks keep the
+      // row-major order.
       for (int64_t i = first; i < end; ++i) {
         const GemmTile &g = gt[(size_t)i];
         const int32_t ti = (int32_t)i;
@@ -352,7 +364,10 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
         const int64_t sr = g.tall ? 64 : 16, sc = g.tall ? 64 : 256;
         for (int32_t bi = 0; bi < (int32_t)cdiv(g.r, sr); ++bi)
           for (int32_t bj = 0; bj < (int32_t)cdiv(g.ldx, sc); ++bj) wstg.push_back(GemmWork{ti, bi, bj});
-        const int32_t nb = (int32_t)cdiv(g.r, 128), nbj = (int32_t)cdiv(g.ldx, 128);
+        // product blocks: 256 x 256 in 256-block chunks, else 128 x 128
+        const int64_t pb = ch.b256 ? 256 : 128;
+        const int32_t nb = (int32_t)cdiv(g.r, pb), nbj = (int32_t)cdiv(g.ldx, pb);
+        const int32_t grp = ch.long_k ? (ch.b256 ? kGemmGroupRows / 2 : kGemmGroupRows) : 0;
         if (ch.t256) {
           // products address their tiles directly: no block lists
         } else if (grp > 0) {
@@ -382,7 +397,7 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
     };
     for (size_t i = 0; i < gt.size(); ++i) {
       const size_t need = gemm_tile_workspace(gt[i].h, gt[i].w);
-      const bool kind_change = i > (size_t)first && t256_kind(gt[i], prec) != t256_kind(gt[(size_t)first], prec);
+      const bool kind_change = i > (size_t)first && gemm_kind(gt[i], prec) != gemm_kind(gt[(size_t)first], prec);
       if ((cur + need > c.workspace_budget || kind_change) && i > (size_t)first) {
         close_chunk((int64_t)i);
         first = (int64_t)i;

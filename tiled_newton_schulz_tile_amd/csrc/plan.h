@@ -32,6 +32,7 @@ struct GemmChunk {
   Range mom, stg, sym, upd, app;  // ranges in the work lists
   bool long_k;        // every GEMM K of its tiles >= kGemmLongK: K slices of 64
   bool t256;          // every tile 256 x 256 and bf16 planes: one workgroup per tile product
+  bool b256;          // otherwise every side a multiple of 256, bf16 planes: 256-blocks
 };
 
 struct Plan {
