@@ -348,9 +348,9 @@ def main():
         # over the whole step, not one kernel
         roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                    "kernel": ("large-tile path (gemm_t256_kernel products, bf16x3; whole step)"
-                               if args.tile == 256 else
-                               "large-tile path (gemm_ns_kernel products, bf16x3; whole step)"),
+                    "kernel": "large-tile path (GEMM products in bf16x3: gemm_t256_kernel for 256x256 "
+                              "tiles, gemm_b256_kernel for sides that are multiples of 256, else "
+                              "gemm_ns_kernel; whole step)",
                     "launches_per_step": int(st["chunks"]) * (4 + 3 * K),
                     "algorithmic_flops_per_step": st["ns_flops"], "issued_flops_per_step": st["issued_flops"],
                     "algorithmic_bytes_per_step": st["step_bytes"]}

@@ -16,8 +16,9 @@
 //   apply        W <- W - lr O, O reoriented (LDS transpose for tall tiles)
 // GEMM blocks are 128 x 128; K slices of 32 (two LDS stages) or, when every K of a chunk
 // is long, of 64 (one stage) are staged through LDS from registers loaded one slice
-// ahead; four waves each own a 64 x 64 block (2 x 2 MFMA 32x32 tiles).  Chunks of
-// 256 x 256 tiles run each product as one workgroup per tile (gemm_t256_kernel).
+// ahead; four waves each own a 64 x 64 block (2 x 2 MFMA 32x32 tiles).  Chunks whose
+// sides are multiples of 256 use 256 x 256 blocks of eight waves (gemm_b256_kernel), and
+// chunks of 256 x 256 tiles one workgroup per tile and product (gemm_t256_kernel).
 // Operands are read with plain (not non-temporal) loads: a K slice of 32 bf16 is half
 // of a 128-byte line, and the other half is read by the next slice, from L2.
 #include <type_traits>
