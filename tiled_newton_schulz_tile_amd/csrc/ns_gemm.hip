@@ -100,6 +100,50 @@ struct Planes {
       }
     }
   }
+  // fp32 values of 8 consecutive elements of row i from column j (j multiple of 8,
+  // j + 8 <= ld): one 16-byte load per bf16 plane
+  __device__ __forceinline__ void get8(int i, int j, float (&v)[8]) const {
+    const int64_t o = (int64_t)i * ld + j;
+    if constexpr (PREC == PREC_F32) {
+      const GLOBAL_AS f32x4 *s = reinterpret_cast<const GLOBAL_AS f32x4 *>(gmem(f() + o));
+      const f32x4 x0 = s[0], x1 = s[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = x0[e];
+        v[e + 4] = x1[e];
+      }
+    } else {
+      const u32x4 h = *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(hi() + o));
+      const u32x4 l = *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(lo() + o));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __builtin_bit_cast(float, h[e] << 16) + __builtin_bit_cast(float, l[e] << 16);
+        v[2 * e + 1] = __builtin_bit_cast(float, h[e] & 0xffff0000u) + __builtin_bit_cast(float, l[e] & 0xffff0000u);
+      }
+    }
+  }
+  // store 8 consecutive values of row i starting at column j (j multiple of 8, j + 8 <= ld)
+  __device__ __forceinline__ void put8(int i, int j, const float (&v)[8]) const {
+    const int64_t o = (int64_t)i * ld + j;
+    if constexpr (PREC == PREC_F32) {
+      GLOBAL_AS f32x4 *d = reinterpret_cast<GLOBAL_AS f32x4 *>(gmem(f() + o));
+      d[0] = f32x4{v[0], v[1], v[2], v[3]};
+      d[1] = f32x4{v[4], v[5], v[6], v[7]};
+    } else {
+      unsigned short hb[8], lb[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        hb[q] = to_bf16_bits(v[q]);
+        lb[q] = to_bf16_bits(v[q] - bf16_bits_to_f32(hb[q]));
+      }
+      *reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(hi() + o)) =
+          u32x4{hb[0] | (unsigned)hb[1] << 16, hb[2] | (unsigned)hb[3] << 16, hb[4] | (unsigned)hb[5] << 16,
+                hb[6] | (unsigned)hb[7] << 16};
+      *reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(lo() + o)) =
+          u32x4{lb[0] | (unsigned)lb[1] << 16, lb[2] | (unsigned)lb[3] << 16, lb[4] | (unsigned)lb[5] << 16,
+                lb[6] | (unsigned)lb[7] << 16};
+    }
+  }
   // store 16 consecutive values of row i starting at column j (j multiple of 16,
   // j + 16 <= ld)
   __device__ __forceinline__ void put16(int i, int j, const float (&v)[16]) const {
@@ -251,8 +295,9 @@ __global__ __launch_bounds__(THREADS) void gemm_norm_kernel(const GemmTile *__re
 // Tall tiles (transposed on their short side): 64 x 64 blocks through an LDS tile (pitch
 // 65); thread t covers row t / 4, columns 16 (t % 4) .. +15 of the block.  Wide and square
 // tiles need no transpose: strips of 16 rows x 256 columns, thread t covering row t / 16,
-// columns 16 (t % 16) .. +15, so that a wave reads and writes 1 KB runs of fp32 weights
-// (512 B of each bf16 plane) per row instead of 256 B.
+// columns 8 (t % 16) .. +7 and 128 + 8 (t % 16) .. +7, so that every load and store
+// instruction of a wave covers contiguous runs of a row (512 B of fp32 weights, 256 B of
+// each bf16 plane).
 constexpr int SB = 64, SBP = 65;
 constexpr int STRIP_R = 16, STRIP_C = 256;
 
@@ -283,6 +328,42 @@ __device__ __forceinline__ void load_state16(const LayerDesc *L, const S *mb, in
   } else {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
+      float x = 0.f;
+      if (gi < t.h && gj + q < t.w) {
+        const int64_t o = (int64_t)(t.row0 + gi) * ldm + t.col0 + gj + q;
+        if constexpr (sizeof(S) == 2)
+          x = bf16_bits_to_f32(gmem(reinterpret_cast<const unsigned short *>(mb))[o]);
+        else
+          x = gmem(mb)[o];
+      }
+      v[q] = x;
+    }
+  }
+}
+
+// 8 consecutive state values of tile row gi from tile column gj, zero outside the tile.
+template <typename S>
+__device__ __forceinline__ void load_state8(const LayerDesc *L, const S *mb, int64_t ldm, const TileG &t, int gi,
+                                            int gj, float (&v)[8]) {
+  if (gi < t.h && gj + 8 <= t.w && L->vec_ok && ((t.col0 + gj) & 7) == 0) {
+    const int64_t o = (int64_t)(t.row0 + gi) * ldm + t.col0 + gj;
+    if constexpr (sizeof(S) == 2) {
+      const u32x4 a = *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(mb + o));
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        v[q] = __builtin_bit_cast(float, (q & 1) ? (a[q >> 1] & 0xffff0000u) : (a[q >> 1] << 16));
+    } else {
+      const GLOBAL_AS f32x4 *p = reinterpret_cast<const GLOBAL_AS f32x4 *>(gmem(mb + o));
+      const f32x4 x0 = p[0], x1 = p[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = x0[e];
+        v[e + 4] = x1[e];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
       float x = 0.f;
       if (gi < t.h && gj + q < t.w) {
         const int64_t o = (int64_t)(t.row0 + gi) * ldm + t.col0 + gj + q;
@@ -345,14 +426,22 @@ __global__ __launch_bounds__(THREADS) void gemm_stage_kernel(const LayerDesc *__
   const int64_t ldm = L->ld_m;
   const Planes<PREC> X{ws + t.x0, t.r, t.ldx};
   if (!t.tall) {   // uniform over the workgroup: no transpose, straight from registers
+    // two pieces of 8 columns, 128 apart: each load and store instruction of a wave then
+    // covers contiguous 256-byte runs of a row
     const int gi = wk.bi * STRIP_R + (int)(threadIdx.x >> 4);
-    const int gj = wk.bj * STRIP_C + (int)(threadIdx.x & 15) * 16;
-    if (gi >= t.r || gj >= t.ldx) return;
-    float v[16];
-    load_state16<S>(L, mb, ldm, t, gi, gj, v);
+    const int gj = wk.bj * STRIP_C + (int)(threadIdx.x & 15) * 8;
+    if (gi >= t.r) return;
+    float v[2][8];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] *= inv;
-    X.put16(gi, gj, v);
+    for (int p = 0; p < 2; ++p)
+      if (gj + 128 * p < t.ldx) load_state8<S>(L, mb, ldm, t, gi, gj + 128 * p, v[p]);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (gj + 128 * p >= t.ldx) break;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[p][q] *= inv;
+      X.put8(gi, gj + 128 * p, v[p]);   // ldx is a multiple of 64 and gj of 8
+    }
     return;
   }
   const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 16;
@@ -389,12 +478,55 @@ __global__ __launch_bounds__(THREADS) void gemm_apply_kernel(const LayerDesc *__
   const LayerDesc *L = layers + t.layer;
   const Planes<PREC> X{ws + (xsel ? t.x1 : t.x0), t.r, t.ldx};
   if (!t.tall) {   // uniform over the workgroup: O row gi is X row gi
+    // two pieces of 8 columns, 128 apart (contiguous 512-byte runs of W per instruction)
     const int gi = wk.bi * STRIP_R + (int)(threadIdx.x >> 4);
-    const int gj = wk.bj * STRIP_C + (int)(threadIdx.x & 15) * 16;
-    if (gi >= t.h || gj >= t.w) return;
-    float o[16];
-    X.get16(gi, gj, o);   // gj + 16 <= ldx: ldx is a multiple of 64 and gj of 16
-    apply16(L, t, gi, gj, o, lr_, write_u);
+    const int gj = wk.bj * STRIP_C + (int)(threadIdx.x & 15) * 8;
+    if (gi >= t.h) return;
+    float o[2][8];
+    f32x4 w[2][2];
+    bool vec[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int j = gj + 128 * p;
+      vec[p] = j < t.w && t.w - j >= 8 && L->vec_w && ((t.col0 + j) & 3) == 0;
+      if (j < t.w) X.get8(gi, j, o[p]);   // j + 8 <= ldx: ldx is a multiple of 64 and j of 8
+      if (vec[p]) {
+        const GLOBAL_AS f32x4 *pw = reinterpret_cast<const GLOBAL_AS f32x4 *>(
+            gmem(L->w + (int64_t)(t.row0 + gi) * L->ld_w + t.col0 + j));
+        w[p][0] = pw[0];
+        w[p][1] = pw[1];
+      }
+    }
+    const float nlr = -lr_;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int j = gj + 128 * p;
+      if (j >= t.w) break;
+      float *wrow = L->w + (int64_t)(t.row0 + gi) * L->ld_w + t.col0 + j;
+      float *urow = write_u ? L->u + (int64_t)(t.row0 + gi) * L->ld_u + t.col0 + j : nullptr;
+      if (vec[p]) {
+        GLOBAL_AS f32x4 *pw = reinterpret_cast<GLOBAL_AS f32x4 *>(gmem(wrow));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[p][h][e] = __builtin_fmaf(nlr, o[p][4 * h + e], w[p][h][e]);
+          pw[h] = w[p][h];
+        }
+        if (write_u) {
+          GLOBAL_AS f32x4 *pu = reinterpret_cast<GLOBAL_AS f32x4 *>(gmem(urow));
+          pu[0] = f32x4{o[p][0], o[p][1], o[p][2], o[p][3]};
+          pu[1] = f32x4{o[p][4], o[p][5], o[p][6], o[p][7]};
+        }
+      } else {
+        const int nn = t.w - j < 8 ? t.w - j : 8;
+        GLOBAL_AS float *pw = gmem(wrow);
+        for (int q = 0; q < nn; ++q) pw[q] = __builtin_fmaf(nlr, o[p][q], pw[q]);
+        if (write_u) {
+          GLOBAL_AS float *pu = gmem(urow);
+          for (int q = 0; q < nn; ++q) pu[q] = o[p][q];
+        }
+      }
+    }
     return;
   }
   const int lr = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 16;
