@@ -154,6 +154,34 @@ def test_256_tile_chunks_and_work():
         assert (st["tiles"], st["gemm_tiles"], st["chunks"]) == (11, 10, chunks), prec
 
 
+def test_256_block_issued_work_at_full():
+    # every side of the 8B stack is a multiple of 256: the products run in 256-blocks,
+    # the symmetric ones (Gram over K = s, square over K = r) on the nb (nb + 1) / 2 upper
+    # blocks, the update (K = r) on all nb x (s / 256) blocks; bf16x3 issues 3 products
+    shapes = synth.STACKS["llama3-8b-32L"]
+    want = 0.0
+    for H, W in shapes:
+        r, s_ = min(H, W), max(H, W)
+        nb, nbs = r // 256, s_ // 256
+        sym = nb * (nb + 1) / 2 * 2.0 * 256 * 256
+        want += 5 * 3 * (sym * s_ + sym * r + 2.0 * 256 * 256 * nb * nbs * r)
+    p = plan_for(shapes, 0, precision=hm.PREC_BF16X3)
+    st = hm.himuon_plan_stats(p)
+    hm.himuon_plan_destroy(p)
+    assert st["gemm_tiles"] == len(shapes)
+    assert st["issued_flops"] == pytest.approx(want, rel=1e-12)
+    # a side that is not a multiple of 256 keeps the 128-blocks
+    p = plan_for([(4096, 4000)], 0, precision=hm.PREC_BF16X3)
+    st = hm.himuon_plan_stats(p)
+    hm.himuon_plan_destroy(p)
+    # short side r = 4000: 32 block rows, K of the square and the update padded to 4032;
+    # long side 4096: 32 block columns, K of the Gram 4096
+    nb, nbs = -(-4000 // 128), 4096 // 128
+    sym = nb * (nb + 1) / 2 * 2.0 * 128 * 128
+    assert st["issued_flops"] == pytest.approx(5 * 3 * (sym * 4096 + sym * 4032 + 2.0 * 128 * 128 * nb * nbs * 4032),
+                                               rel=1e-12)
+
+
 @pytest.mark.parametrize("coeffs,K,ok", [
     (hm.QUINTIC, 5, True), (hm.QUINTIC, 100, True), (hm.CUBIC, 8, True),
     ((2.0, -1.5, 0.5), 6, True), ((10.0, 10.0, 10.0), 5, False), ((3.0, 0.0, 0.0), 200, False),
