@@ -107,7 +107,8 @@ typedef struct {
   int32_t steps;                 /* K >= 0                                             */
   himuon_coeffs coeffs;          /* (a, b, c)                                          */
   float beta;                    /* momentum factor, e.g. 0.95                         */
-  float eps;                     /* normaliser guard, e.g. 1e-7                        */
+  float eps;                     /* normaliser guard, e.g. 1e-7 (>= 0); a zero tile maps
+                                    to zero for every eps, 0 included                  */
   size_t workspace_budget;       /* bytes of caller workspace the plan may use         */
   himuon_dtype state_dtype;      /* dtype of momentum and grad, same for all layers    */
   himuon_precision precision;    /* arithmetic of the NS products                      */

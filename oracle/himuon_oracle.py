@@ -24,7 +24,8 @@ The page leaves the following open; the oracle takes the plainest reading:
   (Bjorck & Bowie 1971; Higham 1986, cited by "SignMuon: Communication-Efficient
   Distributed Muon Optimization", References), the quintic set
   (3.4445, -4.7750, 2.0315) is the one used by the Muon blog post cited there;
-* each tile is scaled by 1 / (||Y||_F + eps) before the first NS step;
+* each tile is scaled by 1 / (||Y||_F + eps) before the first NS step (a zero tile
+  stays zero, also at eps = 0);
 * a tile with more rows than columns is transposed, iterated, and transposed back;
   a square tile is not transposed;
 * tiles are anchored at (0, 0) in row-major order; the last tile row and column
@@ -66,9 +67,11 @@ def tiles(H: int, W: int, T: int | None):
 
 # ---------------------------------------------------------------- the NS map
 def frobenius_normalise(Y: np.ndarray, eps: float) -> np.ndarray:
-    """X0 = Y / (||Y||_F + eps); a zero tile maps to zero."""
+    """X0 = Y / (||Y||_F + eps).  A zero tile maps to zero, also when eps = 0 (the
+    divisor is then 0 and the tile is left as it is)."""
     Y = np.asarray(Y, dtype=np.float64)
-    return Y / (np.sqrt(np.sum(Y * Y)) + eps)
+    den = np.sqrt(np.sum(Y * Y)) + eps
+    return Y / den if den > 0 else np.zeros_like(Y)
 
 
 def ns_iterate(X: np.ndarray, K: int, coeffs) -> np.ndarray:
@@ -115,8 +118,7 @@ def tiled_ns(M: np.ndarray, T: int | None, K: int, coeffs, eps: float = 1e-7) ->
         # normalised, so a tile and its transpose see the same arithmetic
         Y = np.stack([np.ascontiguousarray(M[r0:r0 + h, c0:c0 + w].T if tall else M[r0:r0 + h, c0:c0 + w])
                       for r0, c0 in origins])
-        nrm = np.array([np.sqrt(np.sum(y * y)) for y in Y])
-        X = Y / (nrm + eps)[:, None, None]
+        X = np.stack([frobenius_normalise(y, eps) for y in Y])
         X = ns_iterate(X, K, coeffs)
         if tall:
             X = np.swapaxes(X, 1, 2)
@@ -132,13 +134,6 @@ def tiled_ns_loop(M: np.ndarray, T: int | None, K: int, coeffs, eps: float = 1e-
     for r0, c0, h, w in tiles(*M.shape, T):
         O[r0:r0 + h, c0:c0 + w] = ns_tile(M[r0:r0 + h, c0:c0 + w], K, coeffs, eps)
     return O
-
-
-def tiles_ns_sample(M: np.ndarray, T: int | None, K: int, coeffs, picks, eps: float = 1e-7):
-    """NS output of selected tiles only: picks is a list of (row0, col0, h, w)."""
-    M = np.asarray(M)
-    return [ns_tile(np.asarray(M[r0:r0 + h, c0:c0 + w], dtype=np.float64), K, coeffs, eps)
-            for r0, c0, h, w in picks]
 
 
 def phi(x, coeffs):

@@ -220,6 +220,28 @@ def test_reassembly_bit_exact(shape):
     assert np.array_equal(U.numpy(), O)
 
 
+@pytest.mark.parametrize("T", [1, 64, 128, 256, 0])
+@pytest.mark.parametrize("prec", [0, 2, 3])
+def test_zero_tiles_with_eps_zero(T, prec):
+    """eps = 0: a zero tile has divisor 0 and must come out as exact zeros (no NaN), on
+    the fused path (T <= 128), the large-tile path (T = 256) and full matrices (one zero
+    matrix); the other tiles follow the oracle as usual.  T = 1 maps zero entries to 0."""
+    state = torch.float32 if prec == 0 else torch.bfloat16
+    A = power_law(300, 520, 61)
+    A[:128, 256:384] = 0.0                                # a whole tile at T = 64, 128
+    A[256:, :256] = 0.0                                   # and at T = 256
+    A[0, 0] = 0.0
+    Z = torch.zeros(130, 200)
+    (res,), _ = gpu_step([A, Z], T, K=5, eps=0.0, prec=prec, state=state)
+    for (W, M, U) in res:
+        assert torch.isfinite(U).all() and torch.isfinite(W).all()
+        O = oracle.tiled_ns(M.double().numpy(), T, 5, Q, eps=0.0)
+        zero = O == 0.0
+        assert (U.numpy()[zero] == 0.0).all()
+        assert_bar(U, O, prec, tight=None if prec == 0 else 5e-3)
+    assert (res[1][2] == 0).all() and (res[1][0] == 0).all()
+
+
 IDENTITY_SHAPES = [(100, 113), (113, 100), (300, 170), (170, 300), (1, 257), (257, 1), (513, 129)]
 
 

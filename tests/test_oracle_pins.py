@@ -238,6 +238,15 @@ def test_zero_tile_maps_to_zero():
     M[:64, 64:] = 0.0
     O = oracle.tiled_ns(M, 64, 5, Q)
     assert (O[:64, 64:] == 0.0).all() and np.abs(O[64:, :64]).max() > 0
+    # with eps = 0 the divisor of a zero tile is 0; the tile still maps to zero (no NaN),
+    # while every other tile is the plain Y / ||Y||_F map
+    O0 = oracle.tiled_ns(M, 64, 5, Q, eps=0.0)
+    assert (O0[:64, 64:] == 0.0).all() and np.isfinite(O0).all()
+    Y = M[64:, :64]
+    np.testing.assert_allclose(O0[64:, :64], closed_form(Y, 5, Q, eps=0.0), atol=1e-13, rtol=0)
+    # T = 1 at eps = 0 is the sign map phi^K(sign(m)) with sign(0) = 0
+    np.testing.assert_array_equal(oracle.tiled_ns(np.array([[0.0, -2.0, 3.0]]), 1, 1, C, eps=0.0),
+                                  np.array([[0.0, -1.0, 1.0]]))
 
 
 # ------------------------------------------------------------------ P7 invariances
@@ -317,6 +326,34 @@ def test_momentum_first_step_is_gradient_and_second_step_combines():
     assert np.array_equal(oracle.momentum_stored(np.zeros((8, 9)), Gb, 0.95, "bf16"), Gb)
     m2 = oracle.momentum_stored(Gb, Gb, 0.95, "f32")
     np.testing.assert_allclose(m2, np.float32(0.95) * Gb.astype(np.float64) + Gb, rtol=6e-8)
+
+
+def test_momentum_stored_rounds_once_then_to_bf16():
+    """beta M + G is one fused multiply-add: rounded to float32 once, then (bf16 state)
+    rounded from that float32 value to bfloat16.  Values derived by hand in exact rational
+    arithmetic; a product rounded before the add, or a direct rounding to bf16, fails."""
+    from fractions import Fraction as Fr
+    b32 = Fr(15938355, 2 ** 24)                      # float32(0.95) = 0x3F733333
+    assert b32 == Fr(float(np.float32(0.95)))
+    # (1) M = 1 + 2^-23: beta M = 2^-24 (15938356 + 0.89999997...), which float32 rounds
+    # to 15938357 2^-24.  With G = -15938357 2^-24 a separate product and add give 0; the
+    # fused form keeps the product's rounding error, -838861 2^-47 (exact in float32).
+    M = np.array([[1 + 2.0 ** -23]], dtype=np.float32)
+    G = np.array([[-15938357 * 2.0 ** -24]], dtype=np.float32)
+    assert Fr(float(M[0, 0])) * b32 + Fr(float(G[0, 0])) == Fr(-838861, 2 ** 47)
+    out = oracle.momentum_stored(M, G, 0.95, "f32")
+    assert out.dtype == np.float32 and out[0, 0] == np.float32(-838861 * 2.0 ** -47)
+    assert np.float32(np.float32(b32) * M[0, 0]) + G[0, 0] == 0        # the two-rounding result
+    # (2) M = 1 + 5 2^-23: beta M = 2^-24 (15938364 + 0.49999988...), G = 904388 2^-24, so
+    # beta M + G = 1 + 2^-8 + 0.49999988 2^-24.  float32 rounds that to 1 + 2^-8 (the
+    # remainder is below half an ulp, 2^-24), a bf16 tie that goes to even: 1.0.  Rounded
+    # straight to bf16 it would be 1 + 2^-7.
+    M = np.array([[1 + 5 * 2.0 ** -23]], dtype=np.float32)
+    G = np.array([[904388 * 2.0 ** -24]], dtype=np.float32)
+    ex = Fr(float(M[0, 0])) * b32 + Fr(float(G[0, 0]))
+    assert 0 < ex - (1 + Fr(1, 256)) < Fr(1, 2 ** 24)
+    assert oracle.momentum_stored(M, G, 0.95, "f32")[0, 0] == np.float32(1 + 2.0 ** -8)
+    assert oracle.momentum_stored(M, G, 0.95, "bf16")[0, 0] == np.float32(1.0)
 
 
 def test_step_updates_weights_against_the_direction():

@@ -1258,7 +1258,9 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
 #pragma unroll
         for (int i = 1; i < G::WPT; ++i) ss += red[grp][i];
       }
-      inv = prm.identity ? 1.0f : 1.0f / (__builtin_sqrtf(ss) + prm.eps);
+      // a zero tile stays zero, also with eps = 0 (divisor 0)
+      const float den = __builtin_sqrtf(ss) + prm.eps;
+      inv = prm.identity ? 1.0f : (den > 0.f ? 1.0f / den : 0.f);
     }
 
     // X in registers (fp32, MFMA output layout of the update product: block holds X^T)

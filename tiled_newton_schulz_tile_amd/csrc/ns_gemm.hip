@@ -288,7 +288,9 @@ __global__ __launch_bounds__(THREADS) void gemm_norm_kernel(const GemmTile *__re
   float ss = 0.f;
   for (int q = threadIdx.x; q < t.nred; q += THREADS) ss += p[q];
   ss = block_sum(ss, red4);
-  if (threadIdx.x == 0) p[t.nred] = identity ? 1.0f : 1.0f / (__builtin_sqrtf(ss) + eps);
+  // a zero tile stays zero, also with eps = 0 (divisor 0)
+  const float den = __builtin_sqrtf(ss) + eps;
+  if (threadIdx.x == 0) p[t.nred] = identity ? 1.0f : (den > 0.f ? 1.0f / den : 0.f);
 }
 
 // ------------------------------------------------------------------ stage / apply
