@@ -73,11 +73,11 @@ typedef enum {
                              path run HIMUON_PREC_BF16X3.  On tiles that fill 64 x 64 or
                              128 x 128, the Gram product of NS step 0 (and at edge 64 the
                              square product of steps 0 and 1) uses the bf16 hi operands
-                             alone.  Its relative error on exactly low-rank tiles can
-                             exceed 1e-2 (the quintic map grows the e4m3 rounding noise in
-                             their empty directions); HIMUON_PREC_BF16X3 does not.
-                             himuon_plan returns HIMUON_EINVAL if the coefficients'
-                             iterates are unbounded.                                     */
+                             alone.  The a X term of each step is added in fp32 from X
+                             held to about 2^-17 (bf16 hi + lo, or fp32), not through the
+                             e4m3 operands, so rounding noise does not build up in the
+                             empty directions of low-rank tiles.  himuon_plan returns
+                             HIMUON_EINVAL if the coefficients' iterates are unbounded.   */
 } himuon_precision;
 
 #define HIMUON_TILE_FULL 0            /* one tile per matrix: full-matrix Muon        */

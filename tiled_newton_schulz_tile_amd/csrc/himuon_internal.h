@@ -74,7 +74,7 @@ constexpr int kF8Steps = 16;
 struct F8Exps {
   int8_t x[kF8Steps];   // X_k (input of step k); x[k + 1] for the X stored by step k
   int8_t a[kF8Steps];   // A_k = X_k X_k^T, stored as the operand of A^2 (c != 0)
-  int8_t b[kF8Steps];   // a I + b A_k + c A_k^2, the update's operand
+  int8_t b[kF8Steps];   // B_k = b A_k + c A_k^2, the update's operand (a X_k is added in fp32)
 };
 
 // PREC_BF16F8 on full e x e tiles of the fused kernel: the Gram product of the first

@@ -28,9 +28,11 @@
 //   Gram    A[p][q]   = sum_k X[p][k] X[q][k]
 //   square  S[p][q]   = sum_k A[p][k] A[q][k]            (A symmetric)
 //   update  D[j][i]   = sum_k X[k][j] B[i][k] = (B X)^T  (B symmetric)
-// With fp32 or split (hi + lo) operands, a is added to B's diagonal and the update is
-// one product X^T (a I + B); with plain bf16 operands the update accumulates on top of
-// a X^T held in fp32 registers, so only the product's operands are rounded.
+// With fp32 or bf16x3 (hi + lo) operands, a is added to B's diagonal and the update is
+// one product X^T (a I + B).  With plain bf16 operands, and with bf16 + e4m3 operands
+// (whose X carries only about 2^-13 of precision), the update accumulates X^T B on top
+// of a X^T formed in fp32 (from X in registers, or from bf16 hi + lo planes), so the
+// a X term does not see the operands' rounding.
 #include <type_traits>
 
 #include "device_common.h"
@@ -77,7 +79,19 @@ struct Geo {
   static constexpr int REGION = PREC == PREC_F32 ? TS * PF * 4
                               : PREC == PREC_BF16 ? TS * PB * 2
                               : PREC == PREC_BF16X3 ? TS * PB * 4 : TS * PB * 2 + 2 * TS * P8;
-  static constexpr int TILE_LDS = 2 * REGION > TS * PF * 4 ? 2 * REGION : TS * PF * 4;
+  // Tile area: [X] [AB] [X lo].  PREC_BF16F8 128-tiles keep a bf16 lo plane of X
+  // (x - hi, pitch PB, 32 KB) after AB, which fills the 160 KB of LDS; 64-tiles keep
+  // that precision in registers instead.
+  static constexpr int XLO = PREC == PREC_BF16F8 && TS == 128 ? TS * PB * 2 : 0;
+  // the fp32 staging copy (pitch PF) overlays the area from its start
+  static constexpr int ST_BYTES = TS * PF * 4;
+  static constexpr int BASE = 2 * REGION + XLO > ST_BYTES ? 2 * REGION + XLO : ST_BYTES;
+  // the norm's per-wave partial sums: the last words of AB where the staging copy does
+  // not reach them (AB is free from a tile's last barrier until its first A is stored),
+  // else a slot of their own after the tile's planes
+  static constexpr bool RED_IN_AB = 2 * REGION - 64 >= ST_BYTES;
+  static constexpr int RED_OFF = RED_IN_AB ? 2 * REGION - 4 * WPT : BASE;
+  static constexpr int TILE_LDS = BASE + (RED_IN_AB ? 0 : 64);
   // the chunk permutation of row r: the two 2-bit halves of r % 16 swapped
   static __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
   // column c of a row congruent to r16 modulo 16, as stored
@@ -679,39 +693,17 @@ __device__ __forceinline__ F8S f8s_of(int e) { return F8S{pow2i(-e), pow2i(-e - 
 // precision's format.  SCALE: the stored value is s_store * acc; BACK: afterwards acc <-
 // s_back * acc (one pass over the accumulators serves both).  MIRROR (symmetric
 // results): blocks off the diagonal are also stored untransposed, at [row][col].
-// DIAG: diag is added to the stored diagonal elements; the scaling and the addition are
-// then applied to acc in place (it is left holding the stored values, and BACK must be
-// off).  f8: the e4m3 planes' multipliers.
+// f8: the e4m3 planes' multipliers.  LO (PREC_BF16F8): the residual x - hi is also
+// stored as bf16 in the plane lo (same layout as hi), which with hi gives the value to
+// about 2^-17; only the storing wave reads it back.
 template <int TS, int PREC, bool SCALE = false, bool BACK = false, int NB = Geo<TS, PREC>::NI, bool MIRROR = false,
-          bool DIAG = false>
+          bool LO = false>
 __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>::NJ> &acc, const Mat<PREC> &m, int p0, int q0,
                                             int lane, float s_store = 1.f, float s_back = 1.f, F8S f8 = F8S{},
-                                            float diag = 0.f) {
+                                            __bf16 *lo = nullptr) {
   using G = Geo<TS, PREC>;
-  static_assert(!(DIAG && BACK), "DIAG rewrites the accumulators");
+  static_assert(!LO || PREC == PREC_BF16F8, "a separate lo plane only beside the e4m3 planes");
   const int li = lane & 31, half = lane >> 5;
-  if constexpr (DIAG) {
-    // Only blocks on the diagonal (a wave-uniform test, so a branch) pay for the lane
-    // test; element (g, e) of this lane sits on the diagonal iff li - 4 half == 8 g + e.
-#pragma unroll
-    for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-      for (int bj = 0; bj < G::NJ; ++bj) {
-        if (p0 + bi * 32 == q0 + bj * 32) {
-          int dk = li - 4 * half;
-          asm volatile("" : "+v"(dk));   // formed here, not hoisted as sixteen lane masks
-#pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const float x = acc.b[bi][bj][k];
-            acc.b[bi][bj][k] = __builtin_fmaf(SCALE ? s_store : 1.f, x, dk == 8 * (k / 4) + k % 4 ? diag : 0.f);
-          }
-        } else if constexpr (SCALE) {
-#pragma unroll
-          for (int k = 0; k < 16; ++k) acc.b[bi][bj][k] *= s_store;
-        }
-      }
-  }
-  constexpr bool SC = SCALE && !DIAG;   // scaling still to apply while storing
 #pragma unroll
   for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
@@ -724,7 +716,7 @@ __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x = acc.b[bi][bj][4 * g + e];
-          v[e] = SC ? x * s_store : x;
+          v[e] = SCALE ? x * s_store : x;
           if constexpr (BACK) acc.b[bi][bj][4 * g + e] = x * s_back;
         }
         if constexpr (PREC == PREC_BF16F8) {
@@ -739,6 +731,7 @@ __device__ __forceinline__ void store_acc_t(Acc<Geo<TS, PREC>::NI, Geo<TS, PREC>
           const int o8 = col * G::P8 + G::b8col(li & 15, row);
           *reinterpret_cast<unsigned *>(m.h8 + o8) = pack_fp8x4(v[0], v[1], v[2], v[3], f8.h);
           *reinterpret_cast<unsigned *>(m.l8 + o8) = pack_fp8x4(r0, r1, r2, r3, f8.l);
+          if constexpr (LO) *reinterpret_cast<u32x2 *>(lo + o) = u32x2{pack_bf16x2(r0, r1), pack_bf16x2(r2, r3)};
         } else if constexpr (PREC == PREC_F32) {
           *reinterpret_cast<f32x4 *>(m.f + col * G::PF + row) = v;
           if (MIRROR && p0 + bi * 32 != q0 + bj * 32) {   // off the diagonal (wave-uniform)
@@ -826,6 +819,51 @@ __device__ __forceinline__ void add_diag(const Mat<PREC> &m, int p0, int q0, int
     m.lo[o] = (__bf16)(v - (float)hi);
   }
 }
+
+// The a X term of the update (PREC_BF16F8): this wave's block of X read back from its hi
+// and lo planes (the positions store_acc_t<..., LO> writes), where hi + lo is exact in fp32
+// and holds X to about 2^-17.  The reads are issued before the barrier that ends the
+// update (X is unchanged until after it) and added to the accumulators after it, so the
+// wave does not wait for its MFMA results before the barrier.
+template <int TS>
+struct XPiece {
+  static constexpr int NI = Geo<TS, PREC_BF16F8>::NI, NJ = Geo<TS, PREC_BF16F8>::NJ;
+  u32x2 h[NI][NJ][4], l[NI][NJ][4];
+  __device__ __forceinline__ void load(const __bf16 *hi, const __bf16 *lo, int p0, int q0, int lane) {
+    using G = Geo<TS, PREC_BF16F8>;
+    // (the lane index is made opaque so that these addresses are formed here rather than
+    // hoisted out of the tile loop, where they would hold registers across every product)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int li = ln & 31, half = ln >> 5;
+#pragma unroll
+    for (int bi = 0; bi < NI; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NJ; ++bj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int o = (q0 + bj * 32 + li) * G::PB + G::bcol(li & 15, p0 + bi * 32 + 8 * g + 4 * half);
+          h[bi][bj][g] = *reinterpret_cast<const u32x2 *>(hi + o);
+          l[bi][bj][g] = *reinterpret_cast<const u32x2 *>(lo + o);
+        }
+  }
+  // acc += a (hi + lo)
+  __device__ __forceinline__ void add_to(Acc<NI, NJ> &acc, float a) const {
+#pragma unroll
+    for (int bi = 0; bi < NI; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < NJ; ++bj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const unsigned hw = h[bi][bj][g][e >> 1], lw = l[bi][bj][g][e >> 1];
+            const float hv = __builtin_bit_cast(float, (e & 1) ? (hw & 0xffff0000u) : (hw << 16));
+            const float lv = __builtin_bit_cast(float, (e & 1) ? (lw & 0xffff0000u) : (lw << 16));
+            acc.b[bi][bj][4 * g + e] = __builtin_fmaf(a, hv + lv, acc.b[bi][bj][4 * g + e]);
+          }
+  }
+};
 
 // fp32 staging (pitch PF) <-> accumulators, transposed as above; load scales by s.
 template <int TS, int PREC>
@@ -1185,7 +1223,6 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
   constexpr int NT = G::NT, NI = G::NI, NJ = G::NJ, PF = G::PF;
   constexpr bool PREFETCH = sizeof(S) == 2;
   __shared__ __attribute__((aligned(16))) char lds[G::TPB * G::TILE_LDS];
-  __shared__ float red[G::TPB][G::WPT];
 
   const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / NT);  // tile slot in the workgroup
   const int gt = threadIdx.x % NT;                                     // thread within the tile group
@@ -1199,6 +1236,8 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
   float *st = reinterpret_cast<float *>(area);          // fp32 staging, TS x PF
   const Mat<PREC> X = make_mat<TS, PREC>(area);
   const Mat<PREC> AB = make_mat<TS, PREC>(area + G::REGION);
+  __bf16 *const xlo = reinterpret_cast<__bf16 *>(area + 2 * G::REGION);   // G::XLO bytes
+  float *const red = reinterpret_cast<float *>(area + G::RED_OFF);   // G::WPT floats
   const int p0 = (wv / (TS / G::WBN)) * G::WBM;          // wave block origin (rows)
   const int q0 = (wv % (TS / G::WBN)) * G::WBN;          //                   (columns)
   const float ca = prm.a, cb = prm.b, cc = prm.c;
@@ -1216,7 +1255,8 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     // to the LDS copy of X straight from them.  Otherwise the tile is staged in fp32,
     // oriented on its short side and zero padded, and X0 formed from the staging copy.
     // (The summation order is fixed either way.)
-    constexpr bool DIRECT = DENSE && PREC != PREC_BF16;
+    // (PREC_BF16F8 64-tiles keep X in fp32 registers from X0 on, so they stage it)
+    constexpr bool DIRECT = DENSE && PREC != PREC_BF16 && !(PREC == PREC_BF16F8 && G::XLO == 0);
     float vd[DIRECT ? TileRegs<TS, NT, S>::GM_IT : 1][8];
     float ss = 0.f;
     if constexpr (DIRECT) {
@@ -1252,11 +1292,11 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
       if constexpr (G::WPT > 1) {
-        if (lane == 0) red[grp][wv] = ss;
+        if (lane == 0) red[wv] = ss;
         tile_sync<G::WPT>();
-        ss = red[grp][0];
+        ss = red[0];
 #pragma unroll
-        for (int i = 1; i < G::WPT; ++i) ss += red[grp][i];
+        for (int i = 1; i < G::WPT; ++i) ss += red[i];
       }
       // a zero tile stays zero, also with eps = 0 (divisor 0)
       const float den = __builtin_sqrtf(ss) + prm.eps;
@@ -1302,6 +1342,10 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
                                                         pack_fp8x4(xv[4], xv[5], xv[6], xv[7], f8.h)};
           *reinterpret_cast<u32x2 *>(X.l8 + o8) = u32x2{pack_fp8x4(rv[0], rv[1], rv[2], rv[3], f8.l),
                                                         pack_fp8x4(rv[4], rv[5], rv[6], rv[7], f8.l)};
+          if constexpr (G::XLO > 0)
+            *reinterpret_cast<u32x4 *>(xlo + G::bidx(r, c)) =
+                u32x4{pack_bf16x2(rv[0], rv[1]), pack_bf16x2(rv[2], rv[3]), pack_bf16x2(rv[4], rv[5]),
+                      pack_bf16x2(rv[6], rv[7])};
         } else {
           u32x4 hi, lo;
 #pragma unroll
@@ -1320,14 +1364,15 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     } else {
       load_acc_t<TS, PREC>(xr, st, p0, q0, lane, inv);
       tile_sync<G::WPT>();
-      store_acc_t<TS, PREC>(xr, X, p0, q0, lane, 1.f, 1.f, f8s_of(fx0));
+      store_acc_t<TS, PREC, false, false, NI, false, (G::XLO > 0)>(xr, X, p0, q0, lane, 1.f, 1.f, f8s_of(fx0), xlo);
       tile_sync<G::WPT>();
     }
 
     // ---- K Newton-Schulz steps ------------------------------------------------
     // FOLD_A (fp32 and bf16x3): X <- (a I + B) X with a folded into B's diagonal; the
     // LDS copy of X (fp32, or hi + lo bf16) carries X between steps.  Plain bf16 keeps
-    // X in fp32 registers and forms a X there, since its LDS copy is bf16-rounded.
+    // X in fp32 registers and forms a X there, since its LDS copy is bf16-rounded;
+    // bf16f8 (its own loop below) forms a X in fp32 as well.
     constexpr bool FOLD_A = PREC != PREC_BF16;
     // Dense tiles issue the loads of W before the last update product, so that their
     // HBM latency passes while it runs (the other variants, and PREC_BF16F8 with its
@@ -1368,8 +1413,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
             wave_gemm<TS, PREC, false, true, NB, AL>(acc, X, jb.p0, X, jb.q0, lane, 127 - (2 * ex + 8));
           }
           if (cc == 0.f) {
-            // B + a I = b A + a I
-            store_acc_t<TS, PREC, true, false, NB, true, true>(acc, AB, jb.p0, jb.q0, lane, cb, 1.f, f8s_of(eb), ca);
+            store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cb, 1.f, f8s_of(eb));   // B = b A
           } else if (pa) {
             store_acc_t<TS, PREC_BF16, false, true, NB, true>(acc, ABh, jb.p0, jb.q0, lane, 1.f, cb / cc);
           } else {
@@ -1406,7 +1450,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
         with_job<TS>(jb, [&](auto NBC, auto) {
           constexpr int NB = decltype(NBC)::value;
           if constexpr (F8) {
-            store_acc_t<TS, PREC, true, false, NB, true, true>(acc, AB, jb.p0, jb.q0, lane, cc, 1.f, f8s_of(eb), ca);
+            store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cc, 1.f, f8s_of(eb));   // B
           } else {
             store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cc);   // B
             if constexpr (FOLD_A) add_diag<TS, PREC, NB>(AB, jb.p0, jb.q0, lane, ca);       // B + a I
@@ -1418,16 +1462,45 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
       for (int it = 0; it < prm.steps; ++it) {
         sym_part(it);
         const int sxb = 127 - (fs.x() + fs.b() + 8);
+        // The a X term in fp32, from X accurate to about 2^-17: X itself, in registers since
+        // the last update (64-tiles), or the hi and lo planes of this wave's own block,
+        // added after the product (128-tiles).  Rounding noise in the a X term would grow
+        // by a factor of about a per step in the empty directions of a low-rank tile; in
+        // B X it does not.
+        constexpr bool XREG = G::XLO == 0;
+        if constexpr (XREG) {
+#pragma unroll
+          for (int bi = 0; bi < NI; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < NJ; ++bj)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) xr.b[bi][bj][e] *= ca;
+        }
         tile_sync<G::WPT>();
         if (it + 1 == prm.steps) {
           if constexpr (EARLY_W) io.template load_w<DENSE>(t, L, gt);
-          wave_gemm<TS, PREC, true, true>(xr, X, p0, AB, q0, lane, sxb);   // X^T <- X^T (aI + B)
-          tile_sync<G::WPT>();
+          wave_gemm<TS, PREC, true, !XREG>(xr, X, p0, AB, q0, lane, sxb);   // X^T <- a X^T + X^T B
+          if constexpr (!XREG) {
+            XPiece<TS> xp;
+            xp.load(X.hi, xlo, p0, q0, lane);
+            tile_sync<G::WPT>();
+            xp.add_to(xr, ca);
+          } else {
+            tile_sync<G::WPT>();
+          }
           break;
         }
-        wave_gemm<TS, PREC, true, true>(xr, X, p0, AB, q0, lane, sxb);     // X^T <- X^T (aI + B)
-        tile_sync<G::WPT>();
-        store_acc_t<TS, PREC>(xr, X, p0, q0, lane, 1.f, 1.f, f8s_of(fs.xn()));
+        wave_gemm<TS, PREC, true, !XREG>(xr, X, p0, AB, q0, lane, sxb);     // X^T <- a X^T + X^T B
+        if constexpr (!XREG) {
+          XPiece<TS> xp;
+          xp.load(X.hi, xlo, p0, q0, lane);
+          tile_sync<G::WPT>();
+          xp.add_to(xr, ca);
+        } else {
+          tile_sync<G::WPT>();
+        }
+        store_acc_t<TS, PREC, false, false, NI, false, (G::XLO > 0)>(xr, X, p0, q0, lane, 1.f, 1.f, f8s_of(fs.xn()),
+                                                                      xlo);
         tile_sync<G::WPT>();
         fs.advance();
       }

@@ -165,8 +165,8 @@ himuon_status plan_init(Plan &p, const himuon_layer *layers, int32_t n, const hi
 
 // Bounds on the entries of the matrices of each NS step, from bounds on singular values
 // (an entry never exceeds the largest singular value): X_0 = Y / (|Y|_F + eps) has
-// sigma_max < 1; A = X X^T has sigma_max(X)^2; a I + b A + c A^2 has the largest |a + b l
-// + c l^2| over eigenvalues l in [0, sigma_max(X)^2]; and X' = p(X) has the largest
+// sigma_max < 1; A = X X^T has sigma_max(X)^2; B = b A + c A^2 has the largest |b l +
+// c l^2| over eigenvalues l in [0, sigma_max(X)^2]; and X' = p(X) has the largest
 // |a s + b s^3 + c s^5| over s in [0, sigma_max(X)].  The maxima of these polynomials on
 // an interval are taken at its ends or at a real critical point inside it.
 namespace {
@@ -219,7 +219,8 @@ bool f8_exponents(double a, double b, double c, int steps, F8Exps &e) {
     if (k == n) break;
     const double as = xs * xs;
     e.a[i] = (int8_t)std::min<int>(e.a[i], f8_exp_for(as));
-    e.b[i] = (int8_t)std::min<int>(e.b[i], f8_exp_for(max_abs_quad(a, b, c, as)));
+    // the update's e4m3 operand is B = b A + c A^2 alone (its a X term is formed in fp32)
+    e.b[i] = (int8_t)std::min<int>(e.b[i], f8_exp_for(max_abs_quad(0.0, b, c, as)));
     xs = max_abs_odd5(a, b, c, xs);
   }
   return true;
