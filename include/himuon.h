@@ -139,13 +139,25 @@ typedef struct {
   int64_t row0, col0, rows, cols;/* tile origin and size inside its matrix             */
 } himuon_tile;
 
+/* Runtime calls a plan has made so far (for callers that must know which calls allocate
+   or wait): device allocations, pinned host allocations, and host waits on the GPU
+   (blocking copies, event waits).  himuon_step adds to none of them. */
+typedef struct {
+  int64_t device_allocs;
+  int64_t host_allocs;
+  int64_t host_waits;
+} himuon_runtime_counts;
+
 typedef struct himuon_plan_s himuon_plan_t;
 
 /* Validate the layers and config and build the tile-descriptor table over all layers
  * (row-major tiles, layers in order), the chunk list of the large-tile path and the
- * workspace layout.  Host work only: no device memory is touched until the first
- * himuon_step.  The layer array is copied.  EINVAL: bad shape/ld/pointer/config;
- * EBUDGET: the budget cannot hold the workspace of the largest single tile.  */
+ * workspace layout.  The plan binds to the current HIP device: it allocates the device
+ * copy of the tables there and uploads it with a blocking copy.  When no GPU is
+ * visible the plan is host-only (stats and tiles work; himuon_step returns EDEVICE).
+ * The layer array is copied; the layers' device pointers are not touched.  EINVAL: bad
+ * shape/ld/pointer/config; EBUDGET: the budget cannot hold the workspace of the largest
+ * single tile; ENOMEM / EDEVICE: the device tables could not be allocated or copied.  */
 HIMUON_API himuon_status himuon_plan(const himuon_layer *layers, int32_t n_layers,
                           const himuon_config *cfg, himuon_plan_t **out);
 
@@ -156,18 +168,27 @@ HIMUON_API himuon_status himuon_workspace_size(const himuon_plan_t *p, size_t *b
 /* Enqueue one full step (momentum, tiled NS, weight update) for every layer on
  * hip_stream (a hipStream_t; NULL = the default stream).  workspace is a device
  * buffer of at least himuon_workspace_size bytes (may be NULL when that is 0).
- * Does not synchronise.  The first step after himuon_plan or a tile-size change
- * uploads the descriptor table (allocating its device buffer when it grew);
- * later steps allocate nothing.  A plan must not be stepped on two streams
- * concurrently.  EDEVICE on a HIP error. */
+ * Enqueue only: it allocates nothing and never waits for the GPU, so it may be
+ * captured into a HIP graph.  Steps and tile-size changes of one plan go on one
+ * stream (or the caller orders them).  EINVAL: workspace too small, non-finite lr,
+ * another current device than the plan's; EDEVICE: a launch failed, or the plan is
+ * host-only. */
 HIMUON_API himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes,
                           float lr, void *hip_stream);
 
 /* Change T between steps (runtime tile-size schedule).  Rebuilds the tables on the
- * host; the next himuon_step uploads them, stream-ordered after earlier steps on
- * that stream.  A new T whose workspace exceeds the budget gives more chunks, not
- * an error, unless a single tile does not fit (EBUDGET). */
-HIMUON_API himuon_status himuon_set_tile_schedule(himuon_plan_t *p, int32_t tile);
+ * host and enqueues their upload on hip_stream into the plan's second device buffer
+ * (the one the steps before the last change read), so steps enqueued later on that
+ * stream use the new T and steps already queued keep theirs.  It allocates only when
+ * the new tables outgrow that buffer or its pinned staging (outgrown buffers are kept
+ * until himuon_plan_destroy), and waits only when the staging is still being read by
+ * the upload of the change before the previous one.  A new T whose workspace exceeds
+ * the budget gives more chunks, not an error, unless a single tile does not fit
+ * (EBUDGET); on any error the plan keeps its current T. */
+HIMUON_API himuon_status himuon_set_tile_schedule(himuon_plan_t *p, int32_t tile, void *hip_stream);
+
+/* Runtime calls (allocations, host waits) the plan has made since himuon_plan. */
+HIMUON_API himuon_status himuon_plan_runtime_counts(const himuon_plan_t *p, himuon_runtime_counts *out);
 
 /* Counters of the current partition. */
 HIMUON_API himuon_status himuon_plan_stats(const himuon_plan_t *p, himuon_stats *out);

@@ -222,13 +222,13 @@ def test_set_tile_schedule_rebuilds_table():
     p = plan_for(shapes, 64, workspace_budget=10 ** 9)
     try:
         for T in (128, 32, 256, 0, 64):
-            hm.himuon_set_tile_schedule(p, T)
+            hm.himuon_set_tile_schedule(p, T, 0)
             want = [(li, int(h > w), r0, c0, h, w) for li, (H, W) in enumerate(shapes)
                     for r0, c0, h, w in oracle.tiles(H, W, T)]
             assert hm.himuon_plan_tiles(p) == want
             assert hm.himuon_plan_stats(p)["tile"] == T
         with pytest.raises(hm.HiMuonError):
-            hm.himuon_set_tile_schedule(p, -3)
+            hm.himuon_set_tile_schedule(p, -3, 0)
         assert hm.himuon_plan_stats(p)["tile"] == 64  # unchanged after a failed change
     finally:
         hm.himuon_plan_destroy(p)
@@ -270,3 +270,20 @@ def test_null_arguments_rejected():
     assert hm._lib.himuon_step(None, None, 0, 0.02, None) == -1
     assert hm._lib.himuon_plan_stats(None, None) == -1
     hm._lib.himuon_plan_destroy(None)  # no-op
+
+
+def test_host_only_plan_counts_no_runtime_calls_and_refuses_to_step():
+    # without a GPU the plan is host-only: it made no allocation or wait, a tile-size
+    # change makes none either, and a step is refused with EDEVICE
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible: the plan binds to it (covered by the GPU tests)")
+    p = plan_for([(300, 170)], 64)
+    try:
+        assert hm.himuon_plan_runtime_counts(p) == {"device_allocs": 0, "host_allocs": 0, "host_waits": 0}
+        hm.himuon_set_tile_schedule(p, 128, 0)
+        assert hm.himuon_plan_runtime_counts(p) == {"device_allocs": 0, "host_allocs": 0, "host_waits": 0}
+        assert hm._lib.himuon_step(p, None, 0, 0.02, None) == -4
+        assert "no device tables" in hm.himuon_last_error()
+    finally:
+        hm.himuon_plan_destroy(p)

@@ -27,11 +27,21 @@ def test_split_params_convention():
     emb = torch.nn.Parameter(torch.zeros(16, 4))
     frozen = torch.nn.Parameter(torch.zeros(4, 4), requires_grad=False)
     conv = torch.nn.Parameter(torch.zeros(2, 2, 3, 3))
-    hm_p, other = split_params([{"params": [w1, b1, frozen, conv]}, {"params": [emb], "use_himuon": False}])
-    assert [id(p) for p in hm_p] == [id(w1)]
+    groups, other = split_params([{"params": [w1, b1, frozen, conv]}, {"params": [emb], "use_himuon": False}],
+                                 0.02)
+    assert [(lr, [id(p) for p in ps]) for lr, ps in groups] == [(0.02, [id(w1)])]
     assert {id(p) for p in other} == {id(b1), id(conv), id(emb)}
-    hm_p, other = split_params([w1, b1])
-    assert hm_p == [w1] and other == [b1]
+    groups, other = split_params([w1, b1], 0.02)
+    assert groups == [(0.02, [w1])] and other == [b1]
+
+
+def test_split_params_groups_by_learning_rate():
+    # a group with its own lr gets its own HiMuon group (and plan); equal lrs share one
+    a, b, c = (torch.nn.Parameter(torch.zeros(8, 4)) for _ in range(3))
+    groups, other = split_params([{"params": [a]}, {"params": [b], "lr": 0.01}, {"params": [c], "lr": 0.02}],
+                                 0.02)
+    assert [(lr, [id(p) for p in ps]) for lr, ps in groups] == [(0.02, [id(a), id(c)]), (0.01, [id(b)])]
+    assert other == []
 
 
 def test_optimizer_refuses_host_parameters():

@@ -17,7 +17,7 @@ __all__ = [
     "HiMuonError", "himuon_layer", "himuon_config", "himuon_stats", "himuon_tile",
     "himuon_plan", "himuon_workspace_size", "himuon_step", "himuon_set_tile_schedule",
     "himuon_plan_stats", "himuon_plan_tiles", "himuon_plan_destroy", "himuon_last_error",
-    "HiMuon", "CUBIC", "QUINTIC", "TILE_FULL", "F32", "BF16", "PREC_F32", "PREC_BF16",
+    "himuon_plan_runtime_counts", "himuon_runtime_counts", "HiMuon", "CUBIC", "QUINTIC", "TILE_FULL", "F32", "BF16", "PREC_F32", "PREC_BF16",
     "PREC_BF16X3", "PREC_BF16F8", "FLAG_WRITE_UPDATE", "FLAG_IDENTITY_MAP", "library_path", "EXPORTED",
 ]
 
@@ -35,7 +35,7 @@ STATUS = {0: "HIMUON_OK", -1: "HIMUON_EINVAL", -2: "HIMUON_EBUDGET", -3: "HIMUON
 # every entry point include/himuon.h declares
 EXPORTED = ("himuon_plan", "himuon_workspace_size", "himuon_step", "himuon_set_tile_schedule",
             "himuon_plan_stats", "himuon_plan_tiles", "himuon_plan_destroy", "himuon_last_error",
-            "himuon_sign_pack", "himuon_sign_vote")
+            "himuon_plan_runtime_counts", "himuon_sign_pack", "himuon_sign_vote")
 
 
 class HiMuonError(RuntimeError):
@@ -72,6 +72,11 @@ class himuon_stats(ctypes.Structure):
                 ("issued_flops", ctypes.c_double), ("step_bytes", ctypes.c_double)]
 
 
+class himuon_runtime_counts(ctypes.Structure):
+    _fields_ = [("device_allocs", ctypes.c_int64), ("host_allocs", ctypes.c_int64),
+                ("host_waits", ctypes.c_int64)]
+
+
 class himuon_tile(ctypes.Structure):
     _fields_ = [("layer", ctypes.c_int32), ("transposed", ctypes.c_int32),
                 ("row0", ctypes.c_int64), ("col0", ctypes.c_int64),
@@ -97,7 +102,8 @@ def _load() -> ctypes.CDLL:
                                 ctypes.POINTER(himuon_config), ctypes.POINTER(P)]
     lib.himuon_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.himuon_step.argtypes = [P, P, ctypes.c_size_t, ctypes.c_float, P]
-    lib.himuon_set_tile_schedule.argtypes = [P, ctypes.c_int32]
+    lib.himuon_set_tile_schedule.argtypes = [P, ctypes.c_int32, P]
+    lib.himuon_plan_runtime_counts.argtypes = [P, ctypes.POINTER(himuon_runtime_counts)]
     lib.himuon_plan_stats.argtypes = [P, ctypes.POINTER(himuon_stats)]
     lib.himuon_plan_tiles.argtypes = [P, ctypes.POINTER(himuon_tile), ctypes.c_int64,
                                       ctypes.POINTER(ctypes.c_int64)]
@@ -145,8 +151,14 @@ def himuon_step(plan, workspace_ptr: int, ws_bytes: int, lr: float, stream_ptr: 
     _check(_lib.himuon_step(plan, workspace_ptr or None, ws_bytes, lr, stream_ptr or None))
 
 
-def himuon_set_tile_schedule(plan, tile: int) -> None:
-    _check(_lib.himuon_set_tile_schedule(plan, tile))
+def himuon_set_tile_schedule(plan, tile: int, stream_ptr: int) -> None:
+    _check(_lib.himuon_set_tile_schedule(plan, tile, stream_ptr or None))
+
+
+def himuon_plan_runtime_counts(plan) -> dict:
+    c = himuon_runtime_counts()
+    _check(_lib.himuon_plan_runtime_counts(plan, ctypes.byref(c)))
+    return {name: getattr(c, name) for name, _ in himuon_runtime_counts._fields_}
 
 
 def himuon_plan_stats(plan) -> dict:
@@ -249,9 +261,16 @@ class HiMuon:
         himuon_step(self.plan, ws.data_ptr() if ws is not None else 0,
                     ws.numel() if ws is not None else 0, lr, s.cuda_stream)
 
-    def set_tile_schedule(self, tile: int) -> None:
-        himuon_set_tile_schedule(self.plan, tile)
+    def set_tile_schedule(self, tile: int, stream=None) -> None:
+        """Change T from the next step on; the table upload is enqueued on `stream` (the
+        current stream by default), the stream the following steps should use."""
+        torch = self._torch
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        himuon_set_tile_schedule(self.plan, tile, s.cuda_stream)
         self._alloc_workspace()
+
+    def runtime_counts(self) -> dict:
+        return himuon_plan_runtime_counts(self.plan)
 
     def stats(self) -> dict:
         return himuon_plan_stats(self.plan)

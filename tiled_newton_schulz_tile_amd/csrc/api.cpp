@@ -1,7 +1,9 @@
-// C ABI of libhimuon (include/himuon.h): plan lifetime, device upload of the
-// descriptor tables, and the launches of one step.
+// C ABI of libhimuon (include/himuon.h): plan lifetime, the double-buffered device copy
+// of the descriptor tables, and the launches of one step (which allocate nothing and
+// never wait for the GPU).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -12,19 +14,67 @@
 #include "himuon_internal.h"
 #include "plan.h"
 
+namespace {
+
+// Byte layout of the device copy of the tables: [LayerDesc... | FusedTile... | GemmTile... |
+// five GemmWork lists], each part 256-byte aligned.
+struct TableLayout {
+  size_t total = 0, off_ftiles = 0, off_gtiles = 0;
+  size_t off_w[5] = {0, 0, 0, 0, 0};  // work lists: momentum, stage, sym, update, apply
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+const std::vector<himuon::GemmWork> *work_list(const himuon::Plan &pl, int k) {
+  const std::vector<himuon::GemmWork> *wl[5] = {&pl.wmom, &pl.wstg, &pl.wsym, &pl.wupd, &pl.wapp};
+  return wl[k];
+}
+
+TableLayout layout_of(const himuon::Plan &pl) {
+  TableLayout t;
+  size_t off = align256(pl.ldesc.size() * sizeof(himuon::LayerDesc));
+  t.off_ftiles = off;
+  off += align256(pl.ftiles.size() * sizeof(himuon::FusedTile));
+  t.off_gtiles = off;
+  off += align256(pl.gtiles.size() * sizeof(himuon::GemmTile));
+  for (int k = 0; k < 5; ++k) {
+    t.off_w[k] = off;
+    off += align256(work_list(pl, k)->size() * sizeof(himuon::GemmWork));
+  }
+  t.total = std::max<size_t>(off, 256);
+  return t;
+}
+
+void fill_tables(char *dst, const himuon::Plan &pl, const TableLayout &t) {
+  std::memset(dst, 0, t.total);
+  std::memcpy(dst, pl.ldesc.data(), pl.ldesc.size() * sizeof(himuon::LayerDesc));
+  std::memcpy(dst + t.off_ftiles, pl.ftiles.data(), pl.ftiles.size() * sizeof(himuon::FusedTile));
+  std::memcpy(dst + t.off_gtiles, pl.gtiles.data(), pl.gtiles.size() * sizeof(himuon::GemmTile));
+  for (int k = 0; k < 5; ++k)
+    std::memcpy(dst + t.off_w[k], work_list(pl, k)->data(), work_list(pl, k)->size() * sizeof(himuon::GemmWork));
+}
+
+// One device copy of the tables and the pinned staging its last upload came from.
+struct TableBuf {
+  char *d = nullptr;
+  size_t cap = 0;
+  char *h = nullptr;
+  size_t hcap = 0;
+  hipEvent_t ev = nullptr;  // recorded after the last upload from h
+  bool pending = false;     // ev recorded and not yet seen complete
+  TableLayout lay;
+};
+
+}  // namespace
+
 struct himuon_plan_s {
   himuon::Plan plan;
-  // device copy of [LayerDesc... | FusedTile... | GemmTile...]
-  int device = -1;
-  char *d_buf = nullptr;
-  size_t d_cap = 0;
-  char *h_stage = nullptr;  // pinned staging for the upload
-  size_t h_cap = 0;
-  hipEvent_t ev = nullptr;  // completion of the last upload from h_stage
-  bool ev_pending = false;
-  bool dirty = true;
-  size_t off_ftiles = 0, off_gtiles = 0;
-  size_t off_w[5] = {0, 0, 0, 0, 0};  // work lists: momentum, stage, sym, update, apply
+  int device = -1;                 // device holding the tables; -1: no GPU at plan time
+  TableBuf buf[2];                 // double-buffered device tables
+  int active = 0;                  // the buffer the next step reads
+  std::vector<void *> retired_d;   // outgrown device buffers (possibly still read by queued
+  std::vector<void *> retired_h;   // steps) and pinned staging, released by destroy
+  himuon_runtime_counts counts{};
 };
 
 namespace {
@@ -41,78 +91,95 @@ himuon_status hip_fail(hipError_t e, const char *what) {
   return HIMUON_EDEVICE;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+himuon_status check_device(const himuon_plan_t *p) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != p->device) return fail(HIMUON_EINVAL, "plan is bound to another device than the current one");
+  return HIMUON_OK;
+}
 
-// Upload the tables if the partition changed since the last upload.
-himuon_status ensure_tables(himuon_plan_t *p, hipStream_t stream) {
+// Device tables of a new plan: allocated and uploaded with a blocking copy.  A process
+// without a GPU gets a host-only plan (device -1).
+himuon_status bind_device(himuon_plan_t *p) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();   // leave no stale error for the next launch check
+    p->device = -1;
+    return HIMUON_OK;
+  }
   hipError_t e;
   int dev = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (p->device >= 0 && dev != p->device)
-    return fail(HIMUON_EINVAL, "plan is bound to another device than the current one");
-  if (!p->dirty) return HIMUON_OK;
-  p->device = dev;
-  const himuon::Plan &pl = p->plan;
-  const size_t lb = align256(pl.ldesc.size() * sizeof(himuon::LayerDesc));
-  const size_t fb = align256(pl.ftiles.size() * sizeof(himuon::FusedTile));
-  const size_t gb = align256(pl.gtiles.size() * sizeof(himuon::GemmTile));
-  const std::vector<himuon::GemmWork> *wl[5] = {&pl.wmom, &pl.wstg, &pl.wsym, &pl.wupd, &pl.wapp};
-  size_t wb[5], wtot = 0;
-  for (int k = 0; k < 5; ++k) {
-    wb[k] = align256(wl[k]->size() * sizeof(himuon::GemmWork));
-    wtot += wb[k];
+  TableBuf &b = p->buf[0];
+  b.lay = layout_of(p->plan);
+  if ((e = hipMalloc(&b.d, b.lay.total)) != hipSuccess) {
+    b.d = nullptr;
+    return e == hipErrorOutOfMemory ? fail(HIMUON_ENOMEM, "hipMalloc of the tile table failed")
+                                    : hip_fail(e, "hipMalloc");
   }
-  const size_t total = std::max<size_t>(lb + fb + gb + wtot, 256);
-  if (!p->ev) {
-    if ((e = hipEventCreateWithFlags(&p->ev, hipEventDisableTiming)) != hipSuccess)
+  b.cap = b.lay.total;
+  ++p->counts.device_allocs;
+  std::vector<char> host(b.lay.total);
+  fill_tables(host.data(), p->plan, b.lay);
+  if ((e = hipMemcpy(b.d, host.data(), b.lay.total, hipMemcpyHostToDevice)) != hipSuccess)
+    return hip_fail(e, "hipMemcpy of the tile table");
+  ++p->counts.host_waits;
+  p->device = dev;
+  p->active = 0;
+  return HIMUON_OK;
+}
+
+// Puts the tables of `pl` into the spare buffer, stream-ordered on `stream`, and makes it
+// the active one.  Allocates only when the spare is too small; waits only when the
+// spare's staging is still being read by the upload of two schedule changes ago.
+himuon_status upload_spare(himuon_plan_t *p, const himuon::Plan &pl, hipStream_t stream) {
+  hipError_t e;
+  const int s = 1 - p->active;
+  TableBuf &b = p->buf[s];
+  const TableLayout lay = layout_of(pl);
+  if (!b.ev) {
+    if ((e = hipEventCreateWithFlags(&b.ev, hipEventDisableTiming)) != hipSuccess)
       return hip_fail(e, "hipEventCreate");
   }
-  if (total > p->d_cap) {
-    // the old table may still be read by queued steps on this stream
-    if (p->d_buf) {
-      if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-      (void)hipFree(p->d_buf);
-      p->d_buf = nullptr;
-      p->d_cap = 0;
-    }
-    if ((e = hipMalloc(&p->d_buf, total)) != hipSuccess) {
-      p->d_buf = nullptr;
+  if (lay.total > b.cap) {
+    const size_t cap = std::max(lay.total, b.cap + b.cap / 2);
+    char *d = nullptr;
+    if ((e = hipMalloc(&d, cap)) != hipSuccess)
       return e == hipErrorOutOfMemory ? fail(HIMUON_ENOMEM, "hipMalloc of the tile table failed")
                                       : hip_fail(e, "hipMalloc");
-    }
-    p->d_cap = total;
+    ++p->counts.device_allocs;
+    if (b.d) p->retired_d.push_back(b.d);   // queued steps may still read it
+    b.d = d;
+    b.cap = cap;
   }
-  if (p->ev_pending) {
-    if ((e = hipEventSynchronize(p->ev)) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-    p->ev_pending = false;
-  }
-  if (total > p->h_cap) {
-    if (p->h_stage) (void)hipHostFree(p->h_stage);
-    p->h_stage = nullptr;
-    p->h_cap = 0;
-    if ((e = hipHostMalloc((void **)&p->h_stage, total, hipHostMallocDefault)) != hipSuccess) {
-      p->h_stage = nullptr;
+  if (lay.total > b.hcap) {
+    const size_t cap = std::max(lay.total, b.hcap + b.hcap / 2);
+    char *h = nullptr;
+    if ((e = hipHostMalloc((void **)&h, cap, hipHostMallocDefault)) != hipSuccess)
       return fail(HIMUON_ENOMEM, "hipHostMalloc of the upload staging failed");
+    ++p->counts.host_allocs;
+    if (b.h) p->retired_h.push_back(b.h);   // a pending upload may still read it
+    b.h = h;
+    b.hcap = cap;
+    b.pending = false;
+  } else if (b.pending) {
+    e = hipEventQuery(b.ev);
+    if (e == hipErrorNotReady) {
+      if ((e = hipEventSynchronize(b.ev)) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+      ++p->counts.host_waits;
+    } else if (e != hipSuccess) {
+      return hip_fail(e, "hipEventQuery");
     }
-    p->h_cap = total;
+    b.pending = false;
   }
-  std::memset(p->h_stage, 0, total);
-  std::memcpy(p->h_stage, pl.ldesc.data(), pl.ldesc.size() * sizeof(himuon::LayerDesc));
-  std::memcpy(p->h_stage + lb, pl.ftiles.data(), pl.ftiles.size() * sizeof(himuon::FusedTile));
-  std::memcpy(p->h_stage + lb + fb, pl.gtiles.data(), pl.gtiles.size() * sizeof(himuon::GemmTile));
-  size_t off = lb + fb + gb;
-  for (int k = 0; k < 5; ++k) {
-    std::memcpy(p->h_stage + off, wl[k]->data(), wl[k]->size() * sizeof(himuon::GemmWork));
-    p->off_w[k] = off;
-    off += wb[k];
-  }
-  if ((e = hipMemcpyAsync(p->d_buf, p->h_stage, total, hipMemcpyHostToDevice, stream)) != hipSuccess)
+  fill_tables(b.h, pl, lay);
+  if ((e = hipMemcpyAsync(b.d, b.h, lay.total, hipMemcpyHostToDevice, stream)) != hipSuccess)
     return hip_fail(e, "hipMemcpyAsync of the tile table");
-  if ((e = hipEventRecord(p->ev, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  p->ev_pending = true;
-  p->off_ftiles = lb;
-  p->off_gtiles = lb + fb;
-  p->dirty = false;
+  if ((e = hipEventRecord(b.ev, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  b.pending = true;
+  b.lay = lay;
+  p->active = s;
   return HIMUON_OK;
 }
 
@@ -133,6 +200,11 @@ himuon_status himuon_plan(const himuon_layer *layers, int32_t n_layers, const hi
     delete p;
     return fail(s, err);
   }
+  if ((s = bind_device(p)) != HIMUON_OK) {
+    const std::string msg = g_err;
+    himuon_plan_destroy(p);
+    return fail(s, msg);
+  }
   *out = p;
   g_err.clear();
   return HIMUON_OK;
@@ -151,9 +223,11 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
   const himuon::Plan &pl = p->plan;
   if (pl.workspace_bytes && (!workspace || ws_bytes < pl.workspace_bytes))
     return fail(HIMUON_EINVAL, "workspace smaller than himuon_workspace_size");
+  if (p->device < 0) return fail(HIMUON_EDEVICE, "the plan has no device tables (no GPU was visible to himuon_plan)");
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-  himuon_status s = ensure_tables(p, stream);
+  himuon_status s = check_device(p);
   if (s != HIMUON_OK) return s;
+  const TableBuf &tb = p->buf[p->active];
   const himuon_config &c = pl.cfg;
   himuon::NSParams prm{};
   prm.a = (float)c.coeffs.a;
@@ -168,8 +242,8 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
   prm.f8 = pl.f8;
   // the e4m3 correction products exist for fused tiles of edge 64 and 128 only
   const int gemm_prec = c.precision == HIMUON_PREC_BF16F8 ? (int)HIMUON_PREC_BF16X3 : (int)c.precision;
-  const auto *dl = reinterpret_cast<const himuon::LayerDesc *>(p->d_buf);
-  const auto *dft = reinterpret_cast<const himuon::FusedTile *>(p->d_buf + p->off_ftiles);
+  const auto *dl = reinterpret_cast<const himuon::LayerDesc *>(tb.d);
+  const auto *dft = reinterpret_cast<const himuon::FusedTile *>(tb.d + tb.lay.off_ftiles);
   for (const himuon::FusedGroup &g : pl.fgroups) {
     const int fprec = c.precision == HIMUON_PREC_BF16F8 && g.ts < 64 ? (int)HIMUON_PREC_BF16X3 : (int)c.precision;
     hipError_t e = himuon::launch_fused(g.ts, fprec, c.state_dtype == HIMUON_BF16,
@@ -177,9 +251,9 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
     if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
   }
   if (!pl.chunks.empty()) {
-    const auto *dgt = reinterpret_cast<const himuon::GemmTile *>(p->d_buf + p->off_gtiles);
+    const auto *dgt = reinterpret_cast<const himuon::GemmTile *>(tb.d + tb.lay.off_gtiles);
     const himuon::GemmWork *dw[5];
-    for (int k = 0; k < 5; ++k) dw[k] = reinterpret_cast<const himuon::GemmWork *>(p->d_buf + p->off_w[k]);
+    for (int k = 0; k < 5; ++k) dw[k] = reinterpret_cast<const himuon::GemmWork *>(tb.d + tb.lay.off_w[k]);
     for (const himuon::GemmChunk &ch : pl.chunks) {
       himuon::GemmChunkLaunch cl{};
       cl.tile_first = ch.first;
@@ -205,15 +279,24 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
   return HIMUON_OK;
 }
 
-himuon_status himuon_set_tile_schedule(himuon_plan_t *p, int32_t tile) {
+himuon_status himuon_set_tile_schedule(himuon_plan_t *p, int32_t tile, void *hip_stream) {
   if (!p) return fail(HIMUON_EINVAL, "plan is NULL");
   if (tile == p->plan.tile) return HIMUON_OK;
   himuon::Plan trial = p->plan;
   std::string err;
   himuon_status s = himuon::plan_partition(trial, tile, err);
   if (s != HIMUON_OK) return fail(s, err);
+  if (p->device >= 0) {
+    if ((s = check_device(p)) != HIMUON_OK) return s;
+    if ((s = upload_spare(p, trial, reinterpret_cast<hipStream_t>(hip_stream))) != HIMUON_OK) return s;
+  }
   p->plan = std::move(trial);
-  p->dirty = true;
+  return HIMUON_OK;
+}
+
+himuon_status himuon_plan_runtime_counts(const himuon_plan_t *p, himuon_runtime_counts *out) {
+  if (!p || !out) return fail(HIMUON_EINVAL, "NULL argument");
+  *out = p->counts;
   return HIMUON_OK;
 }
 
@@ -234,12 +317,16 @@ himuon_status himuon_plan_tiles(const himuon_plan_t *p, himuon_tile *out, int64_
 
 void himuon_plan_destroy(himuon_plan_t *p) {
   if (!p) return;
-  if (p->ev) {
-    if (p->ev_pending) (void)hipEventSynchronize(p->ev);
-    (void)hipEventDestroy(p->ev);
+  for (TableBuf &b : p->buf) {
+    if (b.ev) {
+      if (b.pending) (void)hipEventSynchronize(b.ev);
+      (void)hipEventDestroy(b.ev);
+    }
+    if (b.d) (void)hipFree(b.d);
+    if (b.h) (void)hipHostFree(b.h);
   }
-  if (p->d_buf) (void)hipFree(p->d_buf);
-  if (p->h_stage) (void)hipHostFree(p->h_stage);
+  for (void *d : p->retired_d) (void)hipFree(d);
+  for (void *h : p->retired_h) (void)hipHostFree(h);
   delete p;
 }
 

@@ -4,15 +4,18 @@
 (Abstract) applies the tiled Newton-Schulz map to the momentum-gradient matrices of
 dense weights and names runtime tile-size schedules among what the tiling allows.
 Which parameters count as such matrices, and what updates the rest, is not on the
-pages; the convention here: every 2-D parameter goes through HiMuon (all of them in one
-plan, so one launch per kernel covers every layer), every other parameter through a
-plain torch optimizer (AdamW unless one is given).  A parameter group can opt out with
-``use_himuon=False``.
+pages; the convention here: every 2-D parameter goes through HiMuon, every other
+parameter through a plain torch optimizer (AdamW unless one is given).  A parameter
+group can opt out with ``use_himuon=False``.  HiMuon parameters that share a learning
+rate share one plan (one launch per kernel covers all of their layers); groups with
+their own ``lr`` get a plan each, and the step reads every group's current ``lr``, so
+learning-rate schedulers work as usual.
 
 The HiMuon state lives on the device: fp32 weights are the parameters themselves, the
-momentum is a tensor of the state dtype per matrix, and the gradient is copied into a
-persistent buffer of that dtype each step (torch may hand out a new .grad tensor every
-backward pass, while the plan holds device pointers).
+momentum is ``state[p]["momentum_buffer"]`` (the state dtype, saved and restored by
+``state_dict`` / ``load_state_dict``), and the gradient is copied into a persistent
+buffer of that dtype each step (torch may hand out a new .grad tensor every backward
+pass, while the plan holds device pointers).
 """
 from __future__ import annotations
 
@@ -50,20 +53,25 @@ class TileSchedule:
         return cls([(i * period, t) for i, t in enumerate(tiles)])
 
 
-def split_params(params):
-    """(himuon_params, other_params) under the convention above; `params` is an iterable
-    of tensors or of parameter-group dicts."""
+def split_params(params, lr: float):
+    """(himuon_groups, other_params) under the convention above.  `params` is an iterable
+    of tensors or of parameter-group dicts; himuon_groups is a list of (lr, [params]),
+    one per distinct learning rate, in order of first appearance."""
     groups = list(params)
     if groups and not isinstance(groups[0], dict):
         groups = [{"params": groups}]
-    hm_p, other = [], []
+    by_lr, other = {}, []
     for g in groups:
         use = g.get("use_himuon", True)
+        glr = float(g.get("lr", lr))
         for p in g["params"]:
             if not p.requires_grad:
                 continue
-            (hm_p if use and p.dim() == 2 else other).append(p)
-    return hm_p, other
+            if use and p.dim() == 2:
+                by_lr.setdefault(glr, []).append(p)
+            else:
+                other.append(p)
+    return list(by_lr.items()), other
 
 
 class HiMuonOptimizer(torch.optim.Optimizer):
@@ -72,18 +80,21 @@ class HiMuonOptimizer(torch.optim.Optimizer):
     lr, beta (momentum), steps (K), coeffs, eps and tile (an int or a TileSchedule) set
     the HiMuon step; state_dtype (torch.bfloat16 or torch.float32) is the dtype of the
     momentum and of the gradient copy; precision defaults to bf16x3.  `fallback` is a
-    factory taking the list of other parameters (default: AdamW with lr fallback_lr)."""
+    factory taking the list of other parameters (default: AdamW with lr fallback_lr).
+    The optimizer step count is saved with the state, so a restored optimizer resumes
+    the tile schedule where it stopped."""
 
     def __init__(self, params, lr: float = 0.02, beta: float = 0.95, tile=128, steps: int = 5,
                  coeffs=QUINTIC, eps: float = 1e-7, state_dtype=torch.bfloat16, precision=PREC_BF16X3,
                  workspace_budget: int = 4 * 10 ** 9, fallback=None, fallback_lr: float = 3e-4):
-        hm_p, other = split_params(params)
-        if not hm_p:
+        hm_groups, other = split_params(params, lr)
+        if not hm_groups:
             raise ValueError("no 2-D parameters for HiMuon")
-        for p in hm_p:
-            if p.dtype != torch.float32 or not p.is_cuda:
-                raise ValueError("HiMuon parameters must be float32 CUDA tensors")
-        super().__init__(hm_p, dict(lr=lr))
+        for _, ps in hm_groups:
+            for p in ps:
+                if p.dtype != torch.float32 or not p.is_cuda:
+                    raise ValueError("HiMuon parameters must be float32 CUDA tensors")
+        super().__init__([{"params": ps, "lr": glr} for glr, ps in hm_groups], dict(lr=lr, step_count=0))
         self.schedule = tile if isinstance(tile, TileSchedule) else TileSchedule(tile)
         self.steps, self.coeffs, self.beta, self.eps = steps, coeffs, beta, eps
         self.state_dtype, self.precision, self.budget = state_dtype, precision, workspace_budget
@@ -91,18 +102,34 @@ class HiMuonOptimizer(torch.optim.Optimizer):
         if other:
             self.fallback = (fallback(other) if fallback is not None
                              else torch.optim.AdamW(other, lr=fallback_lr))
-        self.step_count = 0
-        self._engine = None
-        self._bufs = None
+        self._engines = None
+        self._grads = None
+        self._tile = None
+
+    @property
+    def step_count(self) -> int:
+        return int(self.param_groups[0]["step_count"])
 
     def _build(self):
-        ps = self.param_groups[0]["params"]
-        self._bufs = [(torch.zeros(p.shape, dtype=self.state_dtype, device=p.device),
-                       torch.zeros(p.shape, dtype=self.state_dtype, device=p.device)) for p in ps]
-        self._tile = self.schedule(0)
-        self._engine = HiMuon([(p.data, m, g) for p, (m, g) in zip(ps, self._bufs)], self._tile,
-                              self.steps, self.coeffs, self.beta, self.eps, self.budget,
-                              precision=self.precision)
+        """One plan per parameter group over the group's weights, momentum buffers (made
+        here on first use, or restored by load_state_dict) and gradient buffers."""
+        self._tile = self.schedule(self.step_count)
+        self._engines, self._grads = [], []
+        for grp in self.param_groups:
+            layers, grads = [], []
+            for p in grp["params"]:
+                st = self.state[p]
+                if "momentum_buffer" not in st:
+                    st["momentum_buffer"] = torch.zeros(p.shape, dtype=self.state_dtype, device=p.device)
+                m = st["momentum_buffer"]
+                if m.dtype != self.state_dtype or m.shape != p.shape or not m.is_contiguous():
+                    raise ValueError("momentum_buffer must be a contiguous tensor of the state dtype")
+                g = torch.zeros(p.shape, dtype=self.state_dtype, device=p.device)
+                layers.append((p.data, m, g))
+                grads.append(g)
+            self._engines.append(HiMuon(layers, self._tile, self.steps, self.coeffs, self.beta, self.eps,
+                                        self.budget, precision=self.precision))
+            self._grads.append(grads)
 
     @torch.no_grad()
     def step(self, closure=None):
@@ -110,22 +137,24 @@ class HiMuonOptimizer(torch.optim.Optimizer):
         if closure is not None:
             with torch.enable_grad():
                 loss = closure()
-        if self._engine is None:
+        if self._engines is None:
             self._build()
         T = self.schedule(self.step_count)
         if T != self._tile:
-            self._engine.set_tile_schedule(T)
+            for eng in self._engines:
+                eng.set_tile_schedule(T)
             self._tile = T
-        ps = self.param_groups[0]["params"]
-        for p, (_, g) in zip(ps, self._bufs):
-            if p.grad is None:
-                g.zero_()
-            else:
-                g.copy_(p.grad)
-        self._engine.step(self.param_groups[0]["lr"])
+        for grp, eng, grads in zip(self.param_groups, self._engines, self._grads):
+            for p, g in zip(grp["params"], grads):
+                if p.grad is None:
+                    g.zero_()
+                else:
+                    g.copy_(p.grad)
+            eng.step(float(grp["lr"]))
         if self.fallback is not None:
             self.fallback.step()
-        self.step_count += 1
+        for grp in self.param_groups:
+            grp["step_count"] = self.step_count + 1
         return loss
 
     def zero_grad(self, set_to_none: bool = True):
@@ -133,14 +162,36 @@ class HiMuonOptimizer(torch.optim.Optimizer):
         if self.fallback is not None:
             self.fallback.zero_grad(set_to_none)
 
+    def state_dict(self):
+        sd = super().state_dict()
+        if self.fallback is not None:
+            sd["fallback"] = self.fallback.state_dict()
+        return sd
+
+    def load_state_dict(self, state_dict):
+        """Restores momentum, step count and the fallback's state; the plans are rebuilt
+        on the next step over the restored momentum tensors."""
+        state_dict = dict(state_dict)
+        fb = state_dict.pop("fallback", None)
+        self.close()
+        super().load_state_dict(state_dict)
+        for st in self.state.values():
+            m = st.get("momentum_buffer")
+            if m is not None and (m.dtype != self.state_dtype or not m.is_contiguous()):
+                st["momentum_buffer"] = m.to(self.state_dtype).contiguous()
+        if fb is not None and self.fallback is not None:
+            self.fallback.load_state_dict(fb)
+
     def momentum(self, p):
         """The HiMuon momentum tensor of 2-D parameter p."""
-        for q, (m, _) in zip(self.param_groups[0]["params"], self._bufs or []):
-            if q is p:
-                return m
-        raise KeyError("not a HiMuon parameter of this optimizer (or no step taken yet)")
+        st = self.state.get(p)
+        if not st or "momentum_buffer" not in st:
+            raise KeyError("not a HiMuon parameter of this optimizer (or no step taken yet)")
+        return st["momentum_buffer"]
 
     def close(self):
-        if self._engine is not None:
-            self._engine.close()
-            self._engine = None
+        if self._engines is not None:
+            for eng in self._engines:
+                eng.close()
+            self._engines = None
+            self._grads = None
