@@ -190,6 +190,21 @@ HIMUON_API himuon_status himuon_set_tile_schedule(himuon_plan_t *p, int32_t tile
 /* Runtime calls (allocations, host waits) the plan has made since himuon_plan. */
 HIMUON_API himuon_status himuon_plan_runtime_counts(const himuon_plan_t *p, himuon_runtime_counts *out);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): himuon_step with the large-tile
+ * path's workspace taken from a static per-device array of
+ * HIMUON_STATIC_WORKSPACE_BYTES (each GPU the library runs on holds its own copy until
+ * the process ends) instead of a caller buffer.  It allocates nothing and never waits
+ * for the GPU.  Plans that need no workspace (every tile in the fused kernel) run as
+ * with himuon_step.  Calls on one GPU share the array, so steps that overlap on one
+ * device (on different streams, or from different threads) race on it; the array
+ * needs no clearing (each step writes every workspace byte it reads).  EBUDGET: the
+ * plan's workspace exceeds HIMUON_STATIC_WORKSPACE_BYTES (plan with a workspace_budget
+ * at most that large: the large-tile path then runs in more chunks); other errors as
+ * for himuon_step. */
+#define HIMUON_STATIC_WORKSPACE_BYTES (64u << 20)
+HIMUON_API himuon_status himuon_step_static(himuon_plan_t *p, float lr, void *hip_stream);
+
 /* Counters of the current partition. */
 HIMUON_API himuon_status himuon_plan_stats(const himuon_plan_t *p, himuon_stats *out);
 

@@ -17,7 +17,8 @@ __all__ = [
     "HiMuonError", "himuon_layer", "himuon_config", "himuon_stats", "himuon_tile",
     "himuon_plan", "himuon_workspace_size", "himuon_step", "himuon_set_tile_schedule",
     "himuon_plan_stats", "himuon_plan_tiles", "himuon_plan_destroy", "himuon_last_error",
-    "himuon_plan_runtime_counts", "himuon_runtime_counts", "HiMuon", "CUBIC", "QUINTIC", "TILE_FULL", "F32", "BF16", "PREC_F32", "PREC_BF16",
+    "himuon_plan_runtime_counts", "himuon_runtime_counts", "himuon_step_static", "STATIC_WORKSPACE_BYTES",
+    "HiMuon", "CUBIC", "QUINTIC", "TILE_FULL", "F32", "BF16", "PREC_F32", "PREC_BF16",
     "PREC_BF16X3", "PREC_BF16F8", "FLAG_WRITE_UPDATE", "FLAG_IDENTITY_MAP", "library_path", "EXPORTED",
 ]
 
@@ -28,6 +29,7 @@ F32, BF16 = 0, 1
 PREC_F32, PREC_BF16, PREC_BF16X3, PREC_BF16F8 = 0, 1, 2, 3
 FLAG_WRITE_UPDATE = 1
 FLAG_IDENTITY_MAP = 2
+STATIC_WORKSPACE_BYTES = 64 << 20   # HIMUON_STATIC_WORKSPACE_BYTES
 
 STATUS = {0: "HIMUON_OK", -1: "HIMUON_EINVAL", -2: "HIMUON_EBUDGET", -3: "HIMUON_ENOMEM",
           -4: "HIMUON_EDEVICE", -5: "HIMUON_EUNSUPPORTED"}
@@ -35,7 +37,7 @@ STATUS = {0: "HIMUON_OK", -1: "HIMUON_EINVAL", -2: "HIMUON_EBUDGET", -3: "HIMUON
 # every entry point include/himuon.h declares
 EXPORTED = ("himuon_plan", "himuon_workspace_size", "himuon_step", "himuon_set_tile_schedule",
             "himuon_plan_stats", "himuon_plan_tiles", "himuon_plan_destroy", "himuon_last_error",
-            "himuon_plan_runtime_counts", "himuon_sign_pack", "himuon_sign_vote")
+            "himuon_plan_runtime_counts", "himuon_step_static", "himuon_sign_pack", "himuon_sign_vote")
 
 
 class HiMuonError(RuntimeError):
@@ -102,6 +104,7 @@ def _load() -> ctypes.CDLL:
                                 ctypes.POINTER(himuon_config), ctypes.POINTER(P)]
     lib.himuon_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.himuon_step.argtypes = [P, P, ctypes.c_size_t, ctypes.c_float, P]
+    lib.himuon_step_static.argtypes = [P, ctypes.c_float, P]
     lib.himuon_set_tile_schedule.argtypes = [P, ctypes.c_int32, P]
     lib.himuon_plan_runtime_counts.argtypes = [P, ctypes.POINTER(himuon_runtime_counts)]
     lib.himuon_plan_stats.argtypes = [P, ctypes.POINTER(himuon_stats)]
@@ -149,6 +152,10 @@ def himuon_workspace_size(plan) -> int:
 
 def himuon_step(plan, workspace_ptr: int, ws_bytes: int, lr: float, stream_ptr: int) -> None:
     _check(_lib.himuon_step(plan, workspace_ptr or None, ws_bytes, lr, stream_ptr or None))
+
+
+def himuon_step_static(plan, lr: float, stream_ptr: int) -> None:
+    _check(_lib.himuon_step_static(plan, lr, stream_ptr or None))
 
 
 def himuon_set_tile_schedule(plan, tile: int, stream_ptr: int) -> None:

@@ -185,6 +185,8 @@ himuon_status upload_spare(himuon_plan_t *p, const himuon::Plan &pl, hipStream_t
 
 }  // namespace
 
+himuon_status himuon::set_error(himuon_status s, const std::string &msg) { return fail(s, msg); }
+
 extern "C" {
 
 himuon_status himuon_plan(const himuon_layer *layers, int32_t n_layers, const himuon_config *cfg,

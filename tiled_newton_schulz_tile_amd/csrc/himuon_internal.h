@@ -7,6 +7,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
+#include "himuon.h"
+
 namespace himuon {
 
 // Per-layer device descriptor.
@@ -96,6 +100,9 @@ struct NSParams {
 // Fills e with the fp8 plane exponents for coefficients (a, b, c) over `steps` steps;
 // returns false if some bound is not finite (the coefficients blow up).
 bool f8_exponents(double a, double b, double c, int steps, F8Exps &e);
+
+// Sets the calling thread's himuon_last_error() message and returns s (api.cpp).
+himuon_status set_error(himuon_status s, const std::string &msg);
 
 // ---- launchers (ns_fused.hip) --------------------------------------------------
 // Runs momentum, K NS steps and the weight update for every tile of `tiles`
