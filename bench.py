@@ -8,10 +8,15 @@ Newton-Schulz and weight update over every matrix, inputs resident in HBM.
 
 Prints one JSON line.  `value` is the whole-step throughput in algorithmic NS
 TFLOP/s (sum over tiles of K (4 r^2 s + 2 r^3) per step / step time);
-`ms_per_step` is the step time.  A sweep over T (including FULL when the
-large-tile path is available) is reported in `sweep`.
+`ms_per_step` is the step time.  `roofline` prices the step's one fused-kernel
+launch against both of its bounds, MFMA (algorithmic flops at the bf16 dense peak)
+and HBM (14 algorithmic bytes per element at 8 TB/s), and names the larger as the
+bound.  `sweep` gives the same figures per T (including FULL, the full-matrix Muon
+baseline), `memory_pass` the identity-map step (momentum, gather, scatter and weight
+update of every tile with no Newton-Schulz step: the fused path's HBM stream alone),
+and `schemes` the step in each arithmetic scheme that holds the bf16 bar.
 
-    python bench.py [--steps K] [--warmup W] [--tile T] [--sweep 32,64,128] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--tile T] [--sweep 32,64,256,full] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -31,9 +36,9 @@ METRIC = "HiMuon step ms & NS TFLOP/s (% MFMA peak) vs T, 8B-shaped stack"
 # HBM bytes of one launch of the T=128 fused kernel (bf16f8) on this workload, from two
 # rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), scaled by the
 # readings of a 1 GiB elementwise copy (x2.0 read, x1.0 write).  Valid only for the
-# kernel source it was measured on (sha256 prefix of ns_fused.hip).
-TRAFFIC_T128 = {"source_sha256_16": "aa6cbb4a4531b882", "precision": "bf16f8", "fetch_kib": 27291179.125,
-                "write_kib": 40894464.0, "fetch_scale": 2.0, "write_scale": 1.0}
+# kernel source it was measured on (sha256 prefix of ns_fused.hip); null otherwise.
+TRAFFIC_T128 = {"source_sha256_16": "", "precision": "bf16f8", "fetch_kib": 0.0,
+                "write_kib": 0.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def measured_traffic():
@@ -42,7 +47,7 @@ def measured_traffic():
     with open(src, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()[:16]
     t = TRAFFIC_T128
-    if sha != t["source_sha256_16"]:
+    if not t["source_sha256_16"] or sha != t["source_sha256_16"]:
         return None
     return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
 
@@ -111,6 +116,21 @@ def time_steps(opt, steps, warmup, lr=0.02):
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def rates(st, ms):
+    """Both bounds of a step of `ms` milliseconds: algorithmic NS flops at the bf16 MFMA
+    peak and algorithmic HBM bytes at the HBM peak; the larger lower bound names it."""
+    tflops = st["ns_flops"] / (ms * 1e-3) / 1e12
+    gbps = st["step_bytes"] / (ms * 1e-3) / 1e9
+    t_mfma = st["ns_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
+    t_hbm = st["step_bytes"] / (HBM_PEAK_GBPS * 1e9) * 1e3
+    return {"ms": round(ms, 4), "ns_tflops": round(tflops, 3),
+            "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+            "hbm_gbps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+            "floor_ms": {"mfma": round(t_mfma, 4), "hbm": round(t_hbm, 4)},
+            "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+            "frac_of_roofline": round(max(t_mfma, t_hbm) / ms, 4)}
 
 
 def cpu_baseline(K, coeffs, tile, shapes):
@@ -252,6 +272,8 @@ def main():
     ap.add_argument("--sweep", type=str, default="32,64,256,full")
     ap.add_argument("--sweep-steps", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-memory-pass", action="store_true", help="skip the identity-map (HBM-only) leg")
+    ap.add_argument("--no-schemes", action="store_true", help="skip timing the other arithmetic scheme")
     ap.add_argument("--workload", type=str, default="llama3-8b-32L")
     ap.add_argument("--inputs", choices=["power-law", "randn"], default="power-law")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -285,8 +307,12 @@ def main():
     K, coeffs = 5, hm.QUINTIC
     layers = build_inputs(shapes, dev, kind=args.inputs)
     prec_const, prec_dtype, prec_text = PRECISIONS[args.precision]
-    opt = hm.HiMuon(layers, args.tile, K, coeffs, beta=0.95, eps=1e-7,
-                    workspace_budget=4 * 10 ** 9, precision=getattr(hm, prec_const))
+
+    def plan(tile, prec_name, identity=False):
+        return hm.HiMuon(layers, tile, K, coeffs, beta=0.95, eps=1e-7, workspace_budget=4 * 10 ** 9,
+                         precision=getattr(hm, PRECISIONS[prec_name][0]), identity=identity)
+
+    opt = plan(args.tile, args.precision)
     st = opt.stats()
     log(f"[bench] plan: {st['tiles']} tiles, kernel tile {st['kernel_tile']}, "
         f"{st['ns_flops']:.4e} NS flops/step, workspace {st['workspace_bytes']} B")
@@ -296,9 +322,9 @@ def main():
     tflops = st["ns_flops"] / (ms_mean * 1e-3) / 1e12
     issued = st["issued_flops"] / (ms_mean * 1e-3) / 1e12
     gbps = st["step_bytes"] / (ms_mean * 1e-3) / 1e9
+    head = rates(st, ms_mean)
 
-    sweep = [{"tile": args.tile, "ms": ms_mean, "ns_tflops": tflops,
-              "pct_mfma_peak": 100 * tflops / MFMA_BF16_PEAK_TFLOPS}]
+    sweep = [dict({"tile": args.tile}, **head)]
     for tok in [t for t in args.sweep.split(",") if t.strip()]:
         T = 0 if tok.strip().lower() == "full" else int(tok)
         if T == args.tile:
@@ -308,14 +334,46 @@ def main():
             s2 = opt.stats()
             m2 = time_steps(opt, args.sweep_steps, 1)
             m2 = sum(m2) / len(m2)
-            tf2 = s2["ns_flops"] / (m2 * 1e-3) / 1e12
-            sweep.append({"tile": "full" if T == 0 else T, "ms": m2, "ns_tflops": tf2,
-                          "pct_mfma_peak": 100 * tf2 / MFMA_BF16_PEAK_TFLOPS})
-            log(f"[bench] sweep T={tok}: {m2:.3f} ms/step, {tf2:.1f} NS TFLOP/s")
+            r2 = rates(s2, m2)
+            sweep.append(dict({"tile": "full" if T == 0 else T,
+                               "path": "fused" if s2["gemm_tiles"] == 0 else "large-tile"}, **r2))
+            log(f"[bench] sweep T={tok}: {m2:.3f} ms/step, {r2['ns_tflops']:.1f} NS TFLOP/s "
+                f"({r2['pct_mfma_peak']:.1f} % MFMA), {r2['hbm_gbps']:.0f} GB/s ({r2['pct_hbm_peak']:.1f} % HBM), "
+                f"{r2['bound']}-bound, {100 * r2['frac_of_roofline']:.1f} % of its roofline")
         except hm.HiMuonError as e:
             sweep.append({"tile": tok, "error": str(e)})
             log(f"[bench] sweep T={tok}: {e}")
     opt.close()
+
+    # the fused path's HBM stream alone: the identity-map step at the headline T
+    mem = None
+    if not args.no_memory_pass:
+        idp = plan(args.tile, args.precision, identity=True)
+        mi = time_steps(idp, args.steps, args.warmup)
+        mi = sum(mi) / len(mi)
+        ist = idp.stats()
+        idp.close()
+        mgbps = ist["step_bytes"] / (mi * 1e-3) / 1e9
+        mem = {"ms": round(mi, 4), "bytes_per_step": ist["step_bytes"], "hbm_gbps": round(mgbps, 1),
+               "pct_hbm_peak": round(100 * mgbps / HBM_PEAK_GBPS, 2),
+               "what": "HIMUON_FLAG_IDENTITY_MAP: momentum, gather, scatter and W update of every tile, "
+                       "no NS step; 14 B per element"}
+        log(f"[bench] memory pass (identity map) T={args.tile}: {mi:.3f} ms, {mgbps:.0f} GB/s "
+            f"({100 * mgbps / HBM_PEAK_GBPS:.1f} % of HBM peak)")
+
+    # the other scheme that holds the bf16 bar, same T
+    schemes = {args.precision: {"ms": round(ms_mean, 4), "ns_tflops": round(tflops, 3)}}
+    if not args.no_schemes:
+        for other in sorted(PRECISIONS):
+            if other == args.precision:
+                continue
+            op2 = plan(args.tile, other)
+            m3 = time_steps(op2, args.steps, args.warmup)
+            op2.close()
+            m3 = sum(m3) / len(m3)
+            schemes[other] = {"ms": round(m3, 4), "ns_tflops": round(st["ns_flops"] / (m3 * 1e-3) / 1e12, 3)}
+            log(f"[bench] scheme {other} T={args.tile}: {m3:.3f} ms/step")
+
     if args.copy_calibration:
         copy_calibration(dev)
 
@@ -329,31 +387,33 @@ def main():
 
     n_params = sum(h * w for h, w in shapes)
     kt = st["kernel_tile"]
+    terms = {"mfma": {"achieved": head["ns_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(head["pct_mfma_peak"] / 100, 4), "floor_ms": head["floor_ms"]["mfma"]},
+             "hbm": {"achieved": head["hbm_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(head["pct_hbm_peak"] / 100, 4), "floor_ms": head["floor_ms"]["hbm"]}}
+    bound = head["bound"]
     if kt > 0 and st["gemm_tiles"] == 0:
         # one launch of the fused kernel per step: the step time is its duration
         kprec = args.precision if (args.precision != "bf16f8" or kt >= 64) else "bf16x3"
-        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "traffic": measured_traffic() if (kt == 128 and args.tile == 128
-                                                      and args.workload == "llama3-8b-32L"
-                                                      and args.precision == TRAFFIC_T128["precision"])
-                    else None,
-                    "kernel": f"fused_step_kernel<{kt}, {kprec}, bf16 state>",
-                    "launches_per_step": 1, "algorithmic_flops_per_launch": st["ns_flops"],
-                    "issued_flops_per_launch": st["issued_flops"],
-                    "algorithmic_bytes_per_launch": st["step_bytes"]}
+        roofline = dict(terms[bound], bound=bound, terms=terms,
+                        traffic=measured_traffic() if (kt == 128 and args.tile == 128
+                                                       and args.workload == "llama3-8b-32L"
+                                                       and args.precision == TRAFFIC_T128["precision"])
+                        else None,
+                        kernel=f"fused_step_kernel<{kt}, {kprec}, bf16 state>", launches_per_step=1,
+                        algorithmic_flops_per_launch=st["ns_flops"], issued_flops_per_launch=st["issued_flops"],
+                        algorithmic_bytes_per_launch=st["step_bytes"])
     else:
         # the large-tile path: per chunk, momentum, norm, stage and apply launches plus the
         # products of every NS step (Gram, square, update; bf16x3 arithmetic); rates are
         # over the whole step, not one kernel
-        roofline = {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                    "kernel": "large-tile path (GEMM products in bf16x3: gemm_t256_kernel for 256x256 "
-                              "tiles, gemm_b256_kernel for sides that are multiples of 256, else "
-                              "gemm_ns_kernel; whole step)",
-                    "launches_per_step": int(st["chunks"]) * (4 + 3 * K),
-                    "algorithmic_flops_per_step": st["ns_flops"], "issued_flops_per_step": st["issued_flops"],
-                    "algorithmic_bytes_per_step": st["step_bytes"]}
+        roofline = dict(terms[bound], bound=bound, terms=terms, traffic=None,
+                        kernel="large-tile path (GEMM products in bf16x3: gemm_t256_kernel for 256x256 "
+                               "tiles, gemm_b256_kernel for sides that are multiples of 256, else "
+                               "gemm_ns_kernel; whole step)",
+                        launches_per_step=int(st["chunks"]) * (4 + 3 * K),
+                        algorithmic_flops_per_step=st["ns_flops"], issued_flops_per_step=st["issued_flops"],
+                        algorithmic_bytes_per_step=st["step_bytes"])
 
     out = {
         "metric": METRIC,
@@ -381,6 +441,8 @@ def main():
         "hbm_gbps": round(gbps, 1),
         "roofline": roofline,
         "sweep": sweep,
+        "memory_pass": mem,
+        "schemes": schemes,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -92,6 +92,8 @@ struct Geo {
   static constexpr bool RED_IN_AB = 2 * REGION - 64 >= ST_BYTES;
   static constexpr int RED_OFF = RED_IN_AB ? 2 * REGION - 4 * WPT : BASE;
   static constexpr int TILE_LDS = BASE + (RED_IN_AB ? 0 : 64);
+  // the instance without NS steps holds only the fp32 staging copy and the partial sums
+  static constexpr int K0_RED_OFF = ST_BYTES, K0_LDS = ST_BYTES + 64;
   // the chunk permutation of row r: the two 2-bit halves of r % 16 swapped
   static __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
   // column c of a row congruent to r16 modulo 16, as stored
@@ -1156,10 +1158,10 @@ struct TileRegs {
     }
   }
 
-  // W <- W - lr O (and U <- O) from the staged fp32 output tile.
+  // W <- W - lr O (and U <- O) from the staged fp32 output tile, O = oscale * staged.
   template <int PF, bool DENSE>
   __device__ __forceinline__ void update(TileView t, const LayerView &L, int gt, float lr, bool write_u,
-                         const float *st) const {
+                         const float *st, float oscale = 1.f) const {
     const bool vec = DENSE || (L.vec_w && (t.col0 % 4 == 0));
     const bool tall = !DENSE && t.h > t.w;
     const float nlr = -lr;
@@ -1173,10 +1175,10 @@ struct TileRegs {
       if (!tall) {
         const f32x4 v = *reinterpret_cast<const f32x4 *>(st + r * PF + c);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = v[e];
+        for (int e = 0; e < 4; ++e) o[e] = v[e] * oscale;
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = st[(c + e) * PF + r];
+        for (int e = 0; e < 4; ++e) o[e] = st[(c + e) * PF + r] * oscale;
       }
       float nw[4];
 #pragma unroll
@@ -1213,16 +1215,20 @@ struct TileRegs {
 // ------------------------------------------------------------------ the kernel
 // Persistent: each tile group of a workgroup walks tiles tix, tix + stride, ...  While
 // tile i iterates, the loads of tile i+1's G and M are in flight (bf16 state), so their
-// HBM latency hides behind the MFMA work.
-template <int TS, int PREC, typename S, bool DENSE>
+// HBM latency hides behind the MFMA work.  NS false: the instance for K = 0 (and the
+// identity test mode), with no Newton-Schulz code: W's loads go out early without their
+// registers being held across an iteration, and with a quarter of the LDS and at most
+// 128 registers (dense tiles) twice as many tile groups stay resident per CU.
+template <int TS, int PREC, typename S, bool DENSE, bool NS>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, Geo<TS, PREC>::THREADS)))
-__attribute__((amdgpu_waves_per_eu(2, 2)))
+__attribute__((amdgpu_waves_per_eu(NS || !DENSE ? 2 : 4, NS || !DENSE ? 2 : 4)))
 void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__restrict__ tiles,
                        int64_t ntiles, NSParams prm) {
   using G = Geo<TS, PREC>;
   constexpr int NT = G::NT, NI = G::NI, NJ = G::NJ, PF = G::PF;
   constexpr bool PREFETCH = sizeof(S) == 2;
-  __shared__ __attribute__((aligned(16))) char lds[G::TPB * G::TILE_LDS];
+  constexpr int AREA = NS ? G::TILE_LDS : G::K0_LDS;   // LDS bytes per tile group
+  __shared__ __attribute__((aligned(16))) char lds[G::TPB * AREA];
 
   const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / NT);  // tile slot in the workgroup
   const int gt = threadIdx.x % NT;                                     // thread within the tile group
@@ -1232,12 +1238,12 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
   int64_t tix = (int64_t)blockIdx.x * G::TPB + grp;
   if (tix >= ntiles) return;                                           // uniform per tile group
 
-  char *area = lds + grp * G::TILE_LDS;
+  char *area = lds + grp * AREA;
   float *st = reinterpret_cast<float *>(area);          // fp32 staging, TS x PF
   const Mat<PREC> X = make_mat<TS, PREC>(area);
   const Mat<PREC> AB = make_mat<TS, PREC>(area + G::REGION);
   __bf16 *const xlo = reinterpret_cast<__bf16 *>(area + 2 * G::REGION);   // G::XLO bytes
-  float *const red = reinterpret_cast<float *>(area + G::RED_OFF);   // G::WPT floats
+  float *const red = reinterpret_cast<float *>(area + (NS ? G::RED_OFF : G::K0_RED_OFF));   // G::WPT floats
   const int p0 = (wv / (TS / G::WBN)) * G::WBM;          // wave block origin (rows)
   const int q0 = (wv % (TS / G::WBN)) * G::WBN;          //                   (columns)
   const float ca = prm.a, cb = prm.b, cc = prm.c;
@@ -1256,7 +1262,9 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     // oriented on its short side and zero padded, and X0 formed from the staging copy.
     // (The summation order is fixed either way.)
     // (PREC_BF16F8 64-tiles keep X in fp32 registers from X0 on, so they stage it)
-    constexpr bool DIRECT = DENSE && PREC != PREC_BF16 && !(PREC == PREC_BF16F8 && G::XLO == 0);
+    // (the instance without NS steps always stages: the staged momentum is its output, O =
+    // inv * M, scaled in the weight update)
+    constexpr bool DIRECT = NS && DENSE && PREC != PREC_BF16 && !(PREC == PREC_BF16F8 && G::XLO == 0);
     float vd[DIRECT ? TileRegs<TS, NT, S>::GM_IT : 1][8];
     float ss = 0.f;
     if constexpr (DIRECT) {
@@ -1264,6 +1272,10 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     } else {
       io.template momentum<PF, DENSE>(t, L, gt, prm.beta, st);
     }
+    // Without NS steps (K = 0, and the identity test mode) W's loads go out now, ahead of
+    // the next tile's prefetch, so their latency passes during the staging below; with
+    // NS steps they go out at the end (their registers are busy meanwhile).
+    if constexpr (!NS) io.template load_w<DENSE>(t, L, gt);
     const int64_t nxt = tix + stride;
     TileView tn = t;
     LayerView Ln = L;
@@ -1274,21 +1286,21 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
         io.template load_gm<DENSE>(tn, Ln, gt);
       }
     }
-    if constexpr (!DIRECT) {
-      tile_sync<G::WPT>();
-      constexpr int C4 = TS * TS / 4;
+    if constexpr (!DIRECT) tile_sync<G::WPT>();   // the staging copy is complete
+    float inv = 1.0f;
+    if (!prm.identity) {   // (uniform) the identity test mode takes no norm
+      if constexpr (!DIRECT) {
+        constexpr int C4 = TS * TS / 4;
 #pragma unroll 4
-      for (int q = gt; q < C4; q += NT) {
-        const int r = q / (TS / 4), c = (q % (TS / 4)) * 4;
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(st + r * PF + c);
-        ss = __builtin_fmaf(v[0], v[0], ss);
-        ss = __builtin_fmaf(v[1], v[1], ss);
-        ss = __builtin_fmaf(v[2], v[2], ss);
-        ss = __builtin_fmaf(v[3], v[3], ss);
+        for (int q = gt; q < C4; q += NT) {
+          const int r = q / (TS / 4), c = (q % (TS / 4)) * 4;
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(st + r * PF + c);
+          ss = __builtin_fmaf(v[0], v[0], ss);
+          ss = __builtin_fmaf(v[1], v[1], ss);
+          ss = __builtin_fmaf(v[2], v[2], ss);
+          ss = __builtin_fmaf(v[3], v[3], ss);
+        }
       }
-    }
-    float inv;
-    {
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
       if constexpr (G::WPT > 1) {
@@ -1300,7 +1312,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
       }
       // a zero tile stays zero, also with eps = 0 (divisor 0)
       const float den = __builtin_sqrtf(ss) + prm.eps;
-      inv = prm.identity ? 1.0f : (den > 0.f ? 1.0f / den : 0.f);
+      inv = den > 0.f ? 1.0f / den : 0.f;
     }
 
     // X in registers (fp32, MFMA output layout of the update product: block holds X^T)
@@ -1311,7 +1323,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
       for (int i = 0; i < TileRegs<TS, NT, S>::GM_IT; ++i) {
         const int q = gt + i * NT;
         const int r = q / CPR, c = (q % CPR) * 8;
-        if (prm.steps == 0) {
+        if constexpr (!NS) {
           // no iteration: the output is X0 itself, staged for the update in fp32
 #pragma unroll
           for (int e = 0; e < 8; ++e) st[r * PF + c + e] = vd[i][e] * inv;
@@ -1362,10 +1374,13 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
       }
       tile_sync<G::WPT>();
     } else {
-      load_acc_t<TS, PREC>(xr, st, p0, q0, lane, inv);
-      tile_sync<G::WPT>();
-      store_acc_t<TS, PREC, false, false, NI, false, (G::XLO > 0)>(xr, X, p0, q0, lane, 1.f, 1.f, f8s_of(fx0), xlo);
-      tile_sync<G::WPT>();
+      if constexpr (NS) {
+        load_acc_t<TS, PREC>(xr, st, p0, q0, lane, inv);
+        tile_sync<G::WPT>();
+        store_acc_t<TS, PREC, false, false, NI, false, (G::XLO > 0)>(xr, X, p0, q0, lane, 1.f, 1.f, f8s_of(fx0),
+                                                                      xlo);
+        tile_sync<G::WPT>();
+      }
     }
 
     // ---- K Newton-Schulz steps ------------------------------------------------
@@ -1458,7 +1473,9 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
         });
       }
     };
-    if constexpr (F8) {
+    if constexpr (!NS) {
+      // no Newton-Schulz steps
+    } else if constexpr (F8) {
       for (int it = 0; it < prm.steps; ++it) {
         sym_part(it);
         const int sxb = 127 - (fs.x() + fs.b() + 8);
@@ -1528,15 +1545,15 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
         tile_sync<G::WPT>();
       }
     }
-    if (!EARLY_W || prm.steps == 0) io.template load_w<DENSE>(t, L, gt);
+    if constexpr (NS && !EARLY_W) io.template load_w<DENSE>(t, L, gt);
 
     // ---- reassembly and weight update ------------------------------------------
-    if (!DIRECT || prm.steps > 0) {
+    if constexpr (NS) {
       tile_sync<G::WPT>();
       store_acc_t_f32<TS, PREC>(xr, st, p0, q0, lane);
     }
     tile_sync<G::WPT>();
-    io.template update<PF, DENSE>(t, L, gt, prm.lr, prm.write_update != 0, st);
+    io.template update<PF, DENSE>(t, L, gt, prm.lr, prm.write_update != 0, st, NS ? 1.f : inv);
     if (nxt >= ntiles) break;
     tile_sync<G::WPT>();                 // staging fully read before the next tile lands
     tix = nxt;
@@ -1567,11 +1584,11 @@ int resident_groups(F kernel, int threads) {
   return cus * (per_cu > 0 ? per_cu : 1);
 }
 
-template <int TS, int PREC, typename S, bool DENSE>
+template <int TS, int PREC, typename S, bool DENSE, bool NS = true>
 hipError_t launch_one(const LayerDesc *layers, const FusedTile *tiles, int64_t n,
                       const NSParams &p, hipStream_t stream) {
   using G = Geo<TS, PREC>;
-  auto kern = fused_step_kernel<TS, PREC, S, DENSE>;
+  auto kern = fused_step_kernel<TS, PREC, S, DENSE, NS>;
   int64_t blocks = (n + G::TPB - 1) / G::TPB;
   const int resident = resident_groups(kern, G::THREADS);
   if (resident <= 0) return hipErrorInvalidDevice;
@@ -1580,19 +1597,22 @@ hipError_t launch_one(const LayerDesc *layers, const FusedTile *tiles, int64_t n
   return hipGetLastError();
 }
 
-template <int TS, int PREC>
+template <int TS, int PREC, bool NS = true>
 hipError_t launch_state(int state_bf16, bool dense, const LayerDesc *layers, const FusedTile *tiles,
                         int64_t n, const NSParams &p, hipStream_t stream) {
   if (state_bf16)
-    return dense ? launch_one<TS, PREC, __bf16, true>(layers, tiles, n, p, stream)
-                 : launch_one<TS, PREC, __bf16, false>(layers, tiles, n, p, stream);
-  return dense ? launch_one<TS, PREC, float, true>(layers, tiles, n, p, stream)
-               : launch_one<TS, PREC, float, false>(layers, tiles, n, p, stream);
+    return dense ? launch_one<TS, PREC, __bf16, true, NS>(layers, tiles, n, p, stream)
+                 : launch_one<TS, PREC, __bf16, false, NS>(layers, tiles, n, p, stream);
+  return dense ? launch_one<TS, PREC, float, true, NS>(layers, tiles, n, p, stream)
+               : launch_one<TS, PREC, float, false, NS>(layers, tiles, n, p, stream);
 }
 
 template <int TS>
 hipError_t launch_prec(int prec, int state_bf16, bool dense, const LayerDesc *layers,
                        const FusedTile *tiles, int64_t n, const NSParams &p, hipStream_t stream) {
+  // without NS steps no product runs, so the arithmetic scheme does not matter: one
+  // instance (fp32 staging) serves them all
+  if (p.steps == 0) return launch_state<TS, PREC_F32, false>(state_bf16, dense, layers, tiles, n, p, stream);
   switch (prec) {
     case PREC_F32: return launch_state<TS, PREC_F32>(state_bf16, dense, layers, tiles, n, p, stream);
     case PREC_BF16: return launch_state<TS, PREC_BF16>(state_bf16, dense, layers, tiles, n, p, stream);
