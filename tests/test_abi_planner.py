@@ -287,3 +287,22 @@ def test_host_only_plan_counts_no_runtime_calls_and_refuses_to_step():
         assert "no device tables" in hm.himuon_last_error()
     finally:
         hm.himuon_plan_destroy(p)
+
+
+def test_256_tiles_run_in_place():
+    # 256 x 256 tiles iterate in place: one X buffer and one A/B buffer (4 B per element
+    # each), half the workspace of the other large tiles, which alternate two X buffers
+    p = plan_for([(512, 512)], 256, workspace_budget=10 ** 9)
+    # ragged: in table order two 256 x 256 tiles, then a 256 x 8 edge tile (two X buffers),
+    # per tile row; chunks are cut where the kind changes, so four chunks
+    q = plan_for([(512, 520)], 256, workspace_budget=10 ** 9)
+    try:
+        per_tile = 2 * 256 * 256 * 4 + 256                       # X, A/B, partial sums (8 + 1 floats)
+        assert hm.himuon_workspace_size(p) == 4 * per_tile
+        st = hm.himuon_plan_stats(q)
+        edge = 2 * 8 * 256 * 4 + 2 * 8 * 64 * 4 + 256            # r = 8, ldx = 256, lda = 64
+        assert st["gemm_tiles"] == 6 and st["chunks"] == 4
+        assert hm.himuon_workspace_size(q) == max(2 * per_tile, edge)
+    finally:
+        hm.himuon_plan_destroy(p)
+        hm.himuon_plan_destroy(q)

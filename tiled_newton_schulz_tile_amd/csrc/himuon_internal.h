@@ -36,8 +36,9 @@ static_assert(sizeof(FusedTile) == 16, "FusedTile layout");
 
 // One tile (or whole matrix) of the large-tile GEMM path.  Its workspace holds the
 // oriented tile X (r x s, two buffers), A and B (r x r) as row-major planes with
-// leading dimensions ldx = roundup(s, 32) and lda = roundup(r, 32) (zero padded):
+// leading dimensions ldx = roundup(s, 64) and lda = roundup(r, 64) (zero padded):
 // fp32 planes for PREC_F32, else a bf16 "hi" plane followed by a bf16 "lo" plane.
+// 256 x 256 tiles run in place: one X buffer (ws_x1 = ws_x0) and B over A (ws_b = ws_a).
 struct GemmTile {
   int32_t layer;
   int32_t row0, col0;

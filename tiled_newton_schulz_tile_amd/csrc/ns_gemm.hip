@@ -18,7 +18,8 @@
 // is long, of 64 (one stage) are staged through LDS from registers loaded one slice
 // ahead; four waves each own a 64 x 64 block (2 x 2 MFMA 32x32 tiles).  Chunks whose
 // sides are multiples of 256 use 256 x 256 blocks of eight waves (gemm_b256_kernel), and
-// chunks of 256 x 256 tiles one workgroup per tile and product (gemm_t256_kernel).
+// chunks of 256 x 256 tiles one workgroup per tile for all K steps, in place
+// (gemm_t256_ns_kernel).
 // Operands are read with plain (not non-temporal) loads: a K slice of 32 bf16 is half
 // of a 128-byte line, and the other half is read by the next slice, from L2.
 #include <type_traits>
@@ -878,6 +879,7 @@ __global__ __launch_bounds__(THREADS) void gemm_ns_kernel(const GemmTile *__rest
 // two operand panels leave no registers for more.  bf16 and bf16x3 planes.
 constexpr int T2 = 256, T2_THREADS = 512;
 
+
 template <int PREC, int MODE>
 struct T2Lds {
   static constexpr int BK = MODE == MODE_UPDATE ? 32 : 64;  // K slice
@@ -897,22 +899,27 @@ struct T2Lds {
   static_assert(BYTES <= 160 * 1024, "LDS");
 };
 
+// One product of a 256 x 256 tile by the whole workgroup, in place: X is read from and
+// written back to the x0 planes, and B to the planes of A.  That is safe because the K
+// loop has read every operand before the epilogue writes, and each output element is
+// written by the thread that reads its addend (A for the square, X for the update
+// without a folded a) just before.
 template <int PREC, int MODE>
-__global__ __launch_bounds__(T2_THREADS) void gemm_t256_kernel(const GemmTile *__restrict__ tiles, int first,
-                                                               char *ws, GemmParams gp) {
+__device__ __forceinline__ void t256_product(const TileG &t, char *ws, const GemmParams &gp, char *lds) {
   static_assert(PREC == PREC_BF16 || PREC == PREC_BF16X3, "bf16 planes");
   using LD = T2Lds<PREC, MODE>;
-  __shared__ __attribute__((aligned(16))) char lds[LD::BYTES];
-  // every tile of the chunk is 256 x 256 with ldx = lda = 256 (the planner's chunk kind)
-  const TileG t = tile_of(tiles, first + (int)blockIdx.x);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the thread index is made opaque so that the addresses derived from it are formed
+  // inside each product rather than hoisted out of the NS loop for all three at once)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;   // rows 64 wm.., columns 128 wn..
   const int li = lane & 31, half = lane >> 5;
 
-  const Planes<PREC> Xc{ws + (gp.xsel ? t.x1 : t.x0), T2, T2};
-  const Planes<PREC> Xn{ws + (gp.xsel ? t.x0 : t.x1), T2, T2};
+  const Planes<PREC> Xc{ws + t.x0, T2, T2};
+  const Planes<PREC> Xn = Xc;
   const Planes<PREC> A{ws + t.a, T2, T2};
-  const Planes<PREC> B{ws + t.b, T2, T2};
+  const Planes<PREC> B = A;
   // row operand: X (Gram), A (square), B (update); the symmetric products' column
   // operand is the same panel, the update's is X read along its columns
   const Planes<PREC> Lp = MODE == MODE_GRAM ? Xc : (MODE == MODE_SQUARE ? A : B);
@@ -1070,6 +1077,31 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_t256_kernel(const GemmTile *_
       O.put16(i, j, v);
     }
     __syncthreads();   // the staging read before the next half lands
+  }
+}
+
+// All K Newton-Schulz steps of one 256 x 256 tile per workgroup (every tile of the chunk
+// is 256 x 256 with ldx = lda = 256, the planner's chunk kind): Gram, square and update
+// in turn, in place (X in its x0 planes, A then B in the planes of A).  The tile's
+// 512 KB of planes are written and read back by one CU between the products, so they
+// come back from the L2 and the Infinity Cache rather than HBM.
+template <int PREC>
+constexpr int t256_ns_lds() {
+  constexpr int g = T2Lds<PREC, MODE_GRAM>::BYTES, s = T2Lds<PREC, MODE_SQUARE>::BYTES,
+                u = T2Lds<PREC, MODE_UPDATE>::BYTES;
+  return g > s ? (g > u ? g : u) : (s > u ? s : u);
+}
+template <int PREC>
+__global__ __launch_bounds__(T2_THREADS) void gemm_t256_ns_kernel(const GemmTile *__restrict__ tiles, int first,
+                                                                  char *ws, GemmParams gp, int steps) {
+  __shared__ __attribute__((aligned(16))) char lds[t256_ns_lds<PREC>()];
+  const TileG t = tile_of(tiles, first + (int)blockIdx.x);
+  for (int it = 0; it < steps; ++it) {
+    // (each product ends at a barrier after its last global stores, so the next one's
+    // loads see them: one workgroup, one CU, one L1)
+    t256_product<PREC, MODE_GRAM>(t, ws, gp, lds);
+    if (gp.c != 0.f) t256_product<PREC, MODE_SQUARE>(t, ws, gp, lds);
+    t256_product<PREC, MODE_UPDATE>(t, ws, gp, lds);
   }
 }
 
@@ -1354,14 +1386,8 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
   };
   if constexpr (PREC == PREC_BF16 || PREC == PREC_BF16X3) {
     if (c.t256) {
-      for (int it = 0; it < p.steps; ++it) {
-        gp.xsel = it & 1;
-        const dim3 g((unsigned)c.tile_n), bl(T2_THREADS);
-        const int f = (int)c.tile_first;
-        hipLaunchKernelGGL((gemm_t256_kernel<PREC, MODE_GRAM>), g, bl, 0, stream, tiles, f, ws, gp);
-        if (p.c != 0.f) hipLaunchKernelGGL((gemm_t256_kernel<PREC, MODE_SQUARE>), g, bl, 0, stream, tiles, f, ws, gp);
-        hipLaunchKernelGGL((gemm_t256_kernel<PREC, MODE_UPDATE>), g, bl, 0, stream, tiles, f, ws, gp);
-      }
+      hipLaunchKernelGGL((gemm_t256_ns_kernel<PREC>), dim3((unsigned)c.tile_n), dim3(T2_THREADS), 0, stream, tiles,
+                         (int)c.tile_first, ws, gp, p.steps);
     }
   }
   if constexpr (PREC == PREC_BF16 || PREC == PREC_BF16X3) {
@@ -1383,9 +1409,11 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
   } else {
     products(std::integral_constant<int, 32>{});
   }
+  // the 256-tile kernel leaves X in the x0 planes; the per-product launches alternate
+  const int xfinal = c.t256 ? 0 : (p.steps & 1);
   if (c.n_app)
     hipLaunchKernelGGL((gemm_apply_kernel<PREC>), grid(c.n_app), dim3(THREADS), 0, stream, layers, tiles, c.app, ws,
-                       p.steps & 1, p.lr, p.write_update);
+                       xfinal, p.lr, p.write_update);
   return hipGetLastError();
 }
 

@@ -63,12 +63,15 @@ int gemm_kind(const GemmTile &g, int prec) {
   if (g.r == 256 && g.s == 256) return 1;
   return g.r % 256 == 0 && g.s % 256 == 0 ? 2 : 0;
 }
+
+// Workspace of one tile of the given kind: 256 x 256 tiles run their NS steps in place
+// (one X and one A/B buffer), the others alternate two X buffers and keep A and B apart.
+size_t tile_workspace(const GemmTile &g, int prec) {
+  const GemmSizes z = gemm_sizes(g.h, g.w);
+  return gemm_kind(g, prec) == 1 ? z.x + z.ab + z.red : 2 * z.x + 2 * z.ab + z.red;
+}
 }  // namespace
 
-size_t gemm_tile_workspace(int64_t h, int64_t w) {
-  const GemmSizes z = gemm_sizes(h, w);
-  return 2 * z.x + 2 * z.ab + z.red;
-}
 
 himuon_status plan_init(Plan &p, const himuon_layer *layers, int32_t n, const himuon_config *cfg,
                         std::string &err) {
@@ -295,7 +298,7 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
           g.lda = (int32_t)z.lda;
           g.nred = (int32_t)z.nred;
           gt.push_back(g);
-          max_ws = std::max(max_ws, gemm_tile_workspace(h, w));
+          max_ws = std::max(max_ws, tile_workspace(g, prec));
           const int kind = gemm_kind(g, prec);
           if (kind == 1) {
             // one workgroup per tile and product, every 256 x 256 block computed
@@ -397,7 +400,7 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
       ws_max = std::max(ws_max, cur);
     };
     for (size_t i = 0; i < gt.size(); ++i) {
-      const size_t need = gemm_tile_workspace(gt[i].h, gt[i].w);
+      const size_t need = tile_workspace(gt[i], prec);
       const bool kind_change = i > (size_t)first && gemm_kind(gt[i], prec) != gemm_kind(gt[(size_t)first], prec);
       if ((cur + need > c.workspace_budget || kind_change) && i > (size_t)first) {
         close_chunk((int64_t)i);
@@ -405,11 +408,17 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
         cur = 0;
       }
       const GemmSizes z = gemm_sizes(gt[i].h, gt[i].w);
-      gt[i].ws_x0 = (int64_t)cur;
-      gt[i].ws_x1 = (int64_t)(cur + z.x);
-      gt[i].ws_a = (int64_t)(cur + 2 * z.x);
-      gt[i].ws_b = (int64_t)(cur + 2 * z.x + z.ab);
-      gt[i].ws_red = (int64_t)(cur + 2 * z.x + 2 * z.ab);
+      if (gemm_kind(gt[i], prec) == 1) {   // in place: x1 and b alias x0 and a
+        gt[i].ws_x0 = gt[i].ws_x1 = (int64_t)cur;
+        gt[i].ws_a = gt[i].ws_b = (int64_t)(cur + z.x);
+        gt[i].ws_red = (int64_t)(cur + z.x + z.ab);
+      } else {
+        gt[i].ws_x0 = (int64_t)cur;
+        gt[i].ws_x1 = (int64_t)(cur + z.x);
+        gt[i].ws_a = (int64_t)(cur + 2 * z.x);
+        gt[i].ws_b = (int64_t)(cur + 2 * z.x + z.ab);
+        gt[i].ws_red = (int64_t)(cur + 2 * z.x + 2 * z.ab);
+      }
       cur += need;
     }
     if (!gt.empty()) close_chunk((int64_t)gt.size());

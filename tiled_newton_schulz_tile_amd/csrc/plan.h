@@ -60,7 +60,4 @@ himuon_status plan_init(Plan &p, const himuon_layer *layers, int32_t n, const hi
 // (Re)builds the partition for tile size T (0 = FULL).
 himuon_status plan_partition(Plan &p, int32_t tile, std::string &err);
 
-// Workspace bytes the GEMM path needs for one h x w tile.
-size_t gemm_tile_workspace(int64_t h, int64_t w);
-
 }  // namespace himuon
