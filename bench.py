@@ -37,8 +37,8 @@ METRIC = "HiMuon step ms & NS TFLOP/s (% MFMA peak) vs T, 8B-shaped stack"
 # rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), scaled by the
 # readings of a 1 GiB elementwise copy (x2.0 read, x1.0 write).  Valid only for the
 # kernel source it was measured on (sha256 prefix of ns_fused.hip); null otherwise.
-TRAFFIC_T128 = {"source_sha256_16": "", "precision": "bf16f8", "fetch_kib": 0.0,
-                "write_kib": 0.0, "fetch_scale": 2.0, "write_scale": 1.0}
+TRAFFIC_T128 = {"source_sha256_16": "dc42a87ecfb81f7e", "precision": "bf16f8", "fetch_kib": 27291256.625,
+                "write_kib": 40894464.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def measured_traffic():
@@ -116,6 +116,38 @@ def time_steps(opt, steps, warmup, lr=0.02):
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def stream_reference(dev, step_bytes, n, steps, warmup, lr=0.02):
+    """The memory pass's bytes as one flat stream: himuon_stream_step (M <- beta M + G
+    stored in bf16, W <- W - lr M) over n contiguous elements in buffers of its own,
+    timed with HIP events like a step; the HBM rate this read/write mix reaches."""
+    import torch
+    import tiled_newton_schulz_tile_amd as hm
+    g = torch.randn(n, dtype=torch.bfloat16, device=dev, generator=torch.Generator(device=dev).manual_seed(91))
+    m = torch.zeros(n, dtype=torch.bfloat16, device=dev)
+    w = torch.randn(n, dtype=torch.float32, device=dev, generator=torch.Generator(device=dev).manual_seed(92))
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        hm.himuon_stream_step(m.data_ptr(), g.data_ptr(), w.data_ptr(), n, hm.BF16, 0.95, lr, stream.cuda_stream)
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        launch()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) / steps
+    del g, m, w
+    torch.cuda.empty_cache()
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "hbm_gbps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+            "what": "himuon_stream_step over one flat run of the stack's element count: the same 14 B "
+                    "per element (G, M read; M written; W read and written) with no tiling"}
 
 
 def rates(st, ms):
@@ -360,6 +392,11 @@ def main():
                        "no NS step; 14 B per element"}
         log(f"[bench] memory pass (identity map) T={args.tile}: {mi:.3f} ms, {mgbps:.0f} GB/s "
             f"({100 * mgbps / HBM_PEAK_GBPS:.1f} % of HBM peak)")
+        ref = stream_reference(dev, ist["step_bytes"], sum(h * w for h, w in shapes), args.steps, args.warmup)
+        mem["stream_reference"] = ref
+        mem["frac_of_stream_reference"] = round(ref["ms"] / mi, 4)
+        log(f"[bench] flat stream of the same bytes: {ref['ms']:.3f} ms, {ref['hbm_gbps']:.0f} GB/s; "
+            f"memory pass at {100 * ref['ms'] / mi:.1f} % of it")
 
     # the other scheme that holds the bf16 bar, same T
     schemes = {args.precision: {"ms": round(ms_mean, 4), "ns_tflops": round(tflops, 3)}}
@@ -405,13 +442,13 @@ def main():
                         algorithmic_bytes_per_launch=st["step_bytes"])
     else:
         # the large-tile path: per chunk, momentum, norm, stage and apply launches plus the
-        # products of every NS step (Gram, square, update; bf16x3 arithmetic); rates are
-        # over the whole step, not one kernel
+        # NS products (bf16x3 arithmetic); rates are over the whole step, not one kernel
         roofline = dict(terms[bound], bound=bound, terms=terms, traffic=None,
-                        kernel="large-tile path (GEMM products in bf16x3: gemm_t256_kernel for 256x256 "
-                               "tiles, gemm_b256_kernel for sides that are multiples of 256, else "
-                               "gemm_ns_kernel; whole step)",
-                        launches_per_step=int(st["chunks"]) * (4 + 3 * K),
+                        kernel="large-tile path (GEMM products in bf16x3: gemm_t256_ns_kernel runs all K "
+                               "steps of a 256x256 tile in one workgroup, one launch per chunk; "
+                               "gemm_b256_kernel (sides multiples of 256) or gemm_ns_kernel run one launch "
+                               "per product and NS step; whole step)",
+                        chunks_per_step=int(st["chunks"]),
                         algorithmic_flops_per_step=st["ns_flops"], issued_flops_per_step=st["issued_flops"],
                         algorithmic_bytes_per_step=st["step_bytes"])
 

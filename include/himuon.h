@@ -220,6 +220,22 @@ HIMUON_API void himuon_plan_destroy(himuon_plan_t *p);
 /* Message of the last failure on this thread ("" if none). */
 HIMUON_API const char *himuon_last_error(void);
 
+/* The momentum and weight update of the step with the map O = M, over one flat run of n
+   elements and no tiling: M <- beta M + G (one fp32 fused multiply-add, stored in
+   state_dtype with round-to-nearest-even), W <- W - lr M (M as stored).  It moves the
+   bytes of a step's memory pass (the momentum and weight lines of the step described at
+   the top of this file) and nothing else, so its rate is the HBM rate that read/write mix
+   reaches on the device: the reference against which the tiled step's memory pass is
+   measured.  For the same values its M and W are bit-exact to himuon_step's with
+   HIMUON_FLAG_IDENTITY_MAP (bf16 state, or fp32 state with HIMUON_PREC_F32).  m, g: device arrays of n elements of
+   state_dtype (HIMUON_F32 or HIMUON_BF16); w: device fp32, n elements; when all three
+   are 16-byte aligned the kernel moves 8 elements per thread and turn.  Enqueued on
+   hip_stream.  EINVAL: NULL pointers with n > 0, n < 0, a bad dtype, non-finite beta or
+   lr.  EDEVICE: launch failure.                                                       */
+HIMUON_API himuon_status himuon_stream_step(void *m, const void *g, float *w, int64_t n,
+                                            himuon_dtype state_dtype, float beta, float lr,
+                                            void *hip_stream);
+
 /* ---- Sign-Muon, local pieces ----------------------------------------------------
    "Sign-Muon: Communication-Efficient Distributed Muon Optimization" (Figures 1 and 6):
    a worker forms the entrywise sign S in {-1, +1} of its Newton-Schulz direction, packs

@@ -18,6 +18,7 @@ __all__ = [
     "himuon_plan", "himuon_workspace_size", "himuon_step", "himuon_set_tile_schedule",
     "himuon_plan_stats", "himuon_plan_tiles", "himuon_plan_destroy", "himuon_last_error",
     "himuon_plan_runtime_counts", "himuon_runtime_counts", "himuon_step_static", "STATIC_WORKSPACE_BYTES",
+    "himuon_stream_step",
     "HiMuon", "CUBIC", "QUINTIC", "TILE_FULL", "F32", "BF16", "PREC_F32", "PREC_BF16",
     "PREC_BF16X3", "PREC_BF16F8", "FLAG_WRITE_UPDATE", "FLAG_IDENTITY_MAP", "library_path", "EXPORTED",
 ]
@@ -37,7 +38,8 @@ STATUS = {0: "HIMUON_OK", -1: "HIMUON_EINVAL", -2: "HIMUON_EBUDGET", -3: "HIMUON
 # every entry point include/himuon.h declares
 EXPORTED = ("himuon_plan", "himuon_workspace_size", "himuon_step", "himuon_set_tile_schedule",
             "himuon_plan_stats", "himuon_plan_tiles", "himuon_plan_destroy", "himuon_last_error",
-            "himuon_plan_runtime_counts", "himuon_step_static", "himuon_sign_pack", "himuon_sign_vote")
+            "himuon_plan_runtime_counts", "himuon_step_static", "himuon_stream_step", "himuon_sign_pack",
+            "himuon_sign_vote")
 
 
 class HiMuonError(RuntimeError):
@@ -112,6 +114,7 @@ def _load() -> ctypes.CDLL:
                                       ctypes.POINTER(ctypes.c_int64)]
     lib.himuon_plan_destroy.argtypes = [P]
     lib.himuon_plan_destroy.restype = None
+    lib.himuon_stream_step.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_float, P]
     lib.himuon_sign_pack.argtypes = [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P]
     lib.himuon_sign_vote.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                      P, ctypes.c_float, P]
@@ -184,6 +187,12 @@ def himuon_plan_tiles(plan) -> list:
 
 def himuon_plan_destroy(plan) -> None:
     _lib.himuon_plan_destroy(plan)
+
+
+def himuon_stream_step(m_ptr: int, g_ptr: int, w_ptr: int, n: int, state_dtype: int, beta: float, lr: float,
+                       stream_ptr: int) -> None:
+    _check(_lib.himuon_stream_step(m_ptr or None, g_ptr or None, w_ptr or None, n, state_dtype, beta, lr,
+                                   stream_ptr or None))
 
 
 def himuon_sign_pack(o_ptr: int, rows: int, cols: int, ld: int, bits_ptr: int, stream_ptr: int) -> None:

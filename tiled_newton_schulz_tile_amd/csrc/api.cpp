@@ -336,6 +336,19 @@ const char *himuon_last_error(void) { return g_err.c_str(); }
 
 }  // extern "C"
 
+extern "C" HIMUON_API himuon_status himuon_stream_step(void *m, const void *g, float *w, int64_t n,
+                                                       himuon_dtype state_dtype, float beta, float lr,
+                                                       void *hip_stream) {
+  if (n < 0) return fail(HIMUON_EINVAL, "n must be >= 0");
+  if (state_dtype != HIMUON_F32 && state_dtype != HIMUON_BF16) return fail(HIMUON_EINVAL, "state_dtype");
+  if (!std::isfinite(beta) || !std::isfinite(lr)) return fail(HIMUON_EINVAL, "beta and lr must be finite");
+  if (n == 0) return HIMUON_OK;
+  if (!m || !g || !w) return fail(HIMUON_EINVAL, "NULL pointer");
+  hipError_t e = himuon::launch_stream_step(m, g, w, n, state_dtype == HIMUON_BF16, beta, lr,
+                                            reinterpret_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? HIMUON_OK : hip_fail(e, "stream step launch");
+}
+
 extern "C" HIMUON_API himuon_status himuon_sign_pack(const float *o, int64_t rows, int64_t cols, int64_t ld,
                                                      uint8_t *bits, void *hip_stream) {
   if (rows < 0 || cols < 0 || ld < cols) return fail(HIMUON_EINVAL, "sizes must be >= 0 and ld >= cols");

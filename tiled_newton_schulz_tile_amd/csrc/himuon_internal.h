@@ -137,6 +137,11 @@ hipError_t launch_gemm_chunk(int prec, int state_bf16, const LayerDesc *layers, 
                              const GemmChunkLaunch &c, char *workspace, const NSParams &p,
                              hipStream_t stream);
 
+// ---- flat memory-pass reference (stream.hip) -------------------------------------
+// M <- beta M + G (stored in the state dtype), W <- W - lr M over n contiguous elements.
+hipError_t launch_stream_step(void *m, const void *g, float *w, int64_t n, bool state_bf16, float beta, float lr,
+                              hipStream_t stream);
+
 // ---- Sign-Muon local kernels (sign.hip) -----------------------------------------
 // Sign of a rows x cols fp32 matrix (leading dimension ld) packed to one bit per entry
 // (row-major entry k at byte k / 8, bit k % 8; 1 = non-negative).  bits: 8-byte aligned,
