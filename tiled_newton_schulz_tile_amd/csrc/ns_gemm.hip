@@ -902,10 +902,14 @@ struct T2Lds {
 // One product of a 256 x 256 tile by the whole workgroup, in place: X is read from and
 // written back to the x0 planes, and B to the planes of A.  That is safe because the K
 // loop has read every operand before the epilogue writes, and each output element is
-// written by the thread that reads its addend (A for the square, X for the update
-// without a folded a) just before.
+// written by the thread that reads its addend (X for the update without a folded a)
+// just before.  The accumulators belong to the caller: with c != 0 the Gram product
+// leaves (b / c) A in them (fp32, as accumulated) after storing A, and the square
+// product accumulates A A^T onto that, so B = c ((b / c) A + A^2) needs no second read
+// of A; the Gram and update products start from zero.
 template <int PREC, int MODE>
-__device__ __forceinline__ void t256_product(const TileG &t, char *ws, const GemmParams &gp, char *lds) {
+__device__ __forceinline__ void t256_product(const TileG &t, char *ws, const GemmParams &gp, char *lds,
+                                             f32x16 (&acc)[2][4]) {
   static_assert(PREC == PREC_BF16 || PREC == PREC_BF16X3, "bf16 planes");
   using LD = T2Lds<PREC, MODE>;
   // (the thread index is made opaque so that the addresses derived from it are formed
@@ -959,11 +963,12 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
     }
   };
 
-  f32x16 acc[2][4];
+  if constexpr (MODE != MODE_SQUARE) {
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = f32x16{};
+      for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = f32x16{};
+  }
   auto compute = [&](const char *stage) {
     const __bf16 *L0 = reinterpret_cast<const __bf16 *>(stage);
     const __bf16 *L1 = reinterpret_cast<const __bf16 *>(stage + LD::ROWT);
@@ -1049,9 +1054,7 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
       const int i = u >> 3, jl = (u & 7) * 16;   // row i, columns 128 h + jl .. +15
       const int j = h * (T2 / 2) + jl;
       float e[16];
-      if constexpr (MODE == MODE_SQUARE) {
-        A.get16(i, j, e);
-      } else if constexpr (MODE == MODE_UPDATE) {
+      if constexpr (MODE == MODE_UPDATE) {
         if (!fold) Xc.get16(i, j, e);
       }
       float dv[16];
@@ -1069,7 +1072,7 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
         if constexpr (MODE == MODE_GRAM) {
           v[q] = c != 0.f ? d : b * d + (dg ? a : 0.f);
         } else if constexpr (MODE == MODE_SQUARE) {
-          v[q] = __builtin_fmaf(c, d, b * e[q]) + (dg ? a : 0.f);
+          v[q] = c * d + (dg ? a : 0.f);   // d = (b / c) A + A^2
         } else {
           v[q] = fold ? d : __builtin_fmaf(a, e[q], d);
         }
@@ -1077,6 +1080,17 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
       O.put16(i, j, v);
     }
     __syncthreads();   // the staging read before the next half lands
+  }
+  if constexpr (MODE == MODE_GRAM) {
+    if (c != 0.f) {   // (uniform) seed the square product with (b / c) A
+      const float bc = b / c;
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[bi][bj][e] *= bc;
+    }
   }
 }
 
@@ -1096,12 +1110,13 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_t256_ns_kernel(const GemmTile
                                                                   char *ws, GemmParams gp, int steps) {
   __shared__ __attribute__((aligned(16))) char lds[t256_ns_lds<PREC>()];
   const TileG t = tile_of(tiles, first + (int)blockIdx.x);
+  f32x16 acc[2][4];
   for (int it = 0; it < steps; ++it) {
     // (each product ends at a barrier after its last global stores, so the next one's
     // loads see them: one workgroup, one CU, one L1)
-    t256_product<PREC, MODE_GRAM>(t, ws, gp, lds);
-    if (gp.c != 0.f) t256_product<PREC, MODE_SQUARE>(t, ws, gp, lds);
-    t256_product<PREC, MODE_UPDATE>(t, ws, gp, lds);
+    t256_product<PREC, MODE_GRAM>(t, ws, gp, lds, acc);
+    if (gp.c != 0.f) t256_product<PREC, MODE_SQUARE>(t, ws, gp, lds, acc);
+    t256_product<PREC, MODE_UPDATE>(t, ws, gp, lds, acc);
   }
 }
 
