@@ -156,8 +156,11 @@ typedef struct himuon_plan_s himuon_plan_t;
  * copy of the tables there and uploads it with a blocking copy.  When no GPU is
  * visible the plan is host-only (stats and tiles work; himuon_step returns EDEVICE).
  * The layer array is copied; the layers' device pointers are not touched.  EINVAL: bad
- * shape/ld/pointer/config; EBUDGET: the budget cannot hold the workspace of the largest
- * single tile; ENOMEM / EDEVICE: the device tables could not be allocated or copied.  */
+ * shape/ld/pointer/config, including coefficients that are not finite in fp32, a
+ * nonzero c that rounds to zero in fp32, or |b / c| > 2^100 (the kernels accumulate
+ * c A^2 + b A as c ((b / c) A + A^2) in fp32); EBUDGET: the budget cannot hold the
+ * workspace of the largest single tile; ENOMEM / EDEVICE: the device tables could not be
+ * allocated or copied.  */
 HIMUON_API himuon_status himuon_plan(const himuon_layer *layers, int32_t n_layers,
                           const himuon_config *cfg, himuon_plan_t **out);
 

@@ -245,6 +245,11 @@ def test_set_tile_schedule_rebuilds_table():
     (lambda L, c: setattr(c, "state_dtype", 5), "state_dtype"),
     (lambda L, c: setattr(c, "flags", 8), "flag"),
     (lambda L, c: setattr(c, "eps", float("nan")), "finite"),
+    # the kernels take B = c ((b / c) A + A^2) in fp32: b / c must stay far from overflow,
+    # a nonzero c must not round to zero, and every coefficient must be finite in fp32
+    (lambda L, c: setattr(c, "coeffs", hm.himuon_coeffs(3.4445, -4.775, 1e-37)), "b / c"),
+    (lambda L, c: setattr(c, "coeffs", hm.himuon_coeffs(3.4445, -4.775, 1e-50)), "b / c"),
+    (lambda L, c: setattr(c, "coeffs", hm.himuon_coeffs(1e39, -0.5, 0.0)), "fp32"),
     (lambda L, c: setattr(L[0], "update", None) or setattr(c, "flags", 1), "NULL"),
 ])
 def test_invalid_arguments_are_einval(mutate, msg):

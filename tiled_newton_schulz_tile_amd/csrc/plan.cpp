@@ -98,6 +98,18 @@ himuon_status plan_init(Plan &p, const himuon_layer *layers, int32_t n, const hi
     err = "coefficients, beta and eps must be finite (eps >= 0)";
     return HIMUON_EINVAL;
   }
+  {
+    // The kernels take the coefficients in fp32, and with c != 0 form B = c ((b / c) A +
+    // A^2) (the square accumulated onto (b / c) A, whose entries are at most 1 in
+    // magnitude): the fp32 values must be finite, a nonzero c must stay nonzero, and
+    // b / c must stay far from the fp32 range so that the accumulators cannot overflow.
+    const float fa = (float)c.coeffs.a, fb = (float)c.coeffs.b, fc = (float)c.coeffs.c;
+    if (!std::isfinite(fa) || !std::isfinite(fb) || !std::isfinite(fc) || (c.coeffs.c != 0.0 && fc == 0.f) ||
+        (fc != 0.f && !(std::fabs(fb / fc) <= 0x1p100f))) {
+      err = "coefficients must be finite in fp32, a nonzero c must be representable, and |b / c| <= 2^100";
+      return HIMUON_EINVAL;
+    }
+  }
   if (c.state_dtype != HIMUON_F32 && c.state_dtype != HIMUON_BF16) {
     err = "state_dtype must be HIMUON_F32 or HIMUON_BF16";
     return HIMUON_EINVAL;
