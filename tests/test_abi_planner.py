@@ -277,6 +277,21 @@ def test_null_arguments_rejected():
     hm._lib.himuon_plan_destroy(None)  # no-op
 
 
+def test_stream_step_validates_before_touching_a_device():
+    # argument checks return before any HIP call, so they run without a GPU
+    P = 256   # a non-null address that is never dereferenced
+    lib = hm._lib
+    assert lib.himuon_stream_step(P, P, P, -1, hm.BF16, 0.95, 0.02, None) == -1
+    assert lib.himuon_stream_step(None, P, P, 8, hm.BF16, 0.95, 0.02, None) == -1
+    assert lib.himuon_stream_step(P, None, P, 8, hm.F32, 0.95, 0.02, None) == -1
+    assert lib.himuon_stream_step(P, P, None, 8, hm.F32, 0.95, 0.02, None) == -1
+    assert lib.himuon_stream_step(P, P, P, 8, 9, 0.95, 0.02, None) == -1
+    assert lib.himuon_stream_step(P, P, P, 8, hm.BF16, float("nan"), 0.02, None) == -1
+    assert lib.himuon_stream_step(P, P, P, 8, hm.BF16, 0.95, float("inf"), None) == -1
+    assert "finite" in hm.himuon_last_error()
+    assert lib.himuon_stream_step(None, None, None, 0, hm.BF16, 0.95, 0.02, None) == 0   # nothing to do
+
+
 def test_host_only_plan_counts_no_runtime_calls_and_refuses_to_step():
     # without a GPU the plan is host-only: it made no allocation or wait, a tile-size
     # change makes none either, and a step is refused with EDEVICE
