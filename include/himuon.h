@@ -108,7 +108,12 @@ typedef struct {
   himuon_coeffs coeffs;          /* (a, b, c)                                          */
   float beta;                    /* momentum factor, e.g. 0.95                         */
   float eps;                     /* normaliser guard, e.g. 1e-7 (>= 0); a zero tile maps
-                                    to zero for every eps, 0 included                  */
+                                    to zero for every eps, 0 included.  ||Y||_F is
+                                    formed in fp32; where the sum of squares leaves
+                                    [2^-100, 2^100] it is recomputed from the tile
+                                    scaled by a power of two, so very large and very
+                                    small tiles normalise as in exact arithmetic (on
+                                    the large-tile path while ||Y||_F < 2^126)         */
   size_t workspace_budget;       /* bytes of caller workspace the plan may use         */
   himuon_dtype state_dtype;      /* dtype of momentum and grad, same for all layers    */
   himuon_precision precision;    /* arithmetic of the NS products                      */

@@ -235,6 +235,28 @@ def test_zero_tiles_with_eps_zero(T, prec):
     assert (res[1][2] == 0).all() and (res[1][0] == 0).all()
 
 
+@pytest.mark.parametrize("T", [32, 64, 128, 256, 0])
+@pytest.mark.parametrize("scale", [1e-30, 1e-20, 1e20, 1e30])
+@pytest.mark.parametrize("eps", [0.0, 1e-7])
+@pytest.mark.parametrize("prec", [0, 2, 3])
+@pytest.mark.parametrize("K", [0, 5])
+def test_extreme_magnitudes(T, scale, eps, prec, K):
+    """The map is scale invariant for eps = 0 (X0 = Y / |Y|), and for eps > 0 a tile far
+    below eps maps to about a^K Y / eps.  Tiles whose entries are near the ends of the
+    fp32 range (squares that overflow, or fall below the normal range) must still follow
+    the oracle, on the fused path (dense and ragged tiles; K = 0 runs its own instance)
+    and the large-tile path."""
+    state = torch.float32 if prec == 0 else torch.bfloat16
+    mats = [power_law(256, 384, 71) * scale, power_law(200, 300, 72) * scale]
+    (res,), _ = gpu_step(mats, T, K=K, eps=eps, prec=prec, state=state)
+    for (W, M, U) in res:
+        assert torch.isfinite(U).all()
+        O = oracle.tiled_ns(M.double().numpy(), T, K, Q, eps=eps)
+        mx, rf = errs(U, O)
+        assert rf <= (1e-4 if prec == 0 else 1e-2), (mx, rf)
+        assert mx <= (1e-4 if prec == 0 else 2e-2) * max(1.0, float(np.abs(O).max())), (mx, rf)
+
+
 IDENTITY_SHAPES = [(100, 113), (113, 100), (300, 170), (170, 300), (1, 257), (257, 1), (513, 129)]
 
 

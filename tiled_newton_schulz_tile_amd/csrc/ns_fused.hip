@@ -180,6 +180,36 @@ __device__ __forceinline__ void tile_sync() {
   }
 }
 
+// Sum (resp. maximum) of one float per thread over the WPT waves of a tile, in a fixed
+// order; every thread gets the result.  red holds WPT floats; the caller separates two
+// uses of it by a tile_sync.
+template <int WPT>
+__device__ __forceinline__ float tile_sum(float v, float *red, int lane, int wv) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  if constexpr (WPT > 1) {
+    if (lane == 0) red[wv] = v;
+    tile_sync<WPT>();
+    v = red[0];
+#pragma unroll
+    for (int i = 1; i < WPT; ++i) v += red[i];
+  }
+  return v;
+}
+template <int WPT>
+__device__ __forceinline__ float tile_max(float v, float *red, int lane, int wv) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+  if constexpr (WPT > 1) {
+    if (lane == 0) red[wv] = v;
+    tile_sync<WPT>();
+    v = red[0];
+#pragma unroll
+    for (int i = 1; i < WPT; ++i) v = __builtin_fmaxf(v, red[i]);
+  }
+  return v;
+}
+
 // Transposing operand read (see dev::tr_frag) in the tile's bf16 layout G::bidx.  The
 // 8-byte pieces stay inside one 16-byte chunk, so the chunk permutation moves them whole.
 template <class G>
@@ -1301,17 +1331,67 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
           ss = __builtin_fmaf(v[3], v[3], ss);
         }
       }
+      ss = tile_sum<G::WPT>(ss, red, lane, wv);
+      // Outside [2^-100, 2^100] (a zero tile, entries beyond about 1e15 or below 1e-17 on
+      // a full tile, an overflow) the fp32 sum of squares is recomputed from the values
+      // scaled by the power of two s = s1 s2 that brings the largest magnitude into
+      // [1/2, 1): X0 = (s Y) / (s |Y| + s eps) is the same map, and no square overflows
+      // or falls below the normal range.  The scaled values replace the unscaled ones
+      // (in registers, or in the staging copy), so X0 below takes them as they are.
+      float es1 = 1.f, es2 = 1.f;   // s = es1 es2 for the eps term
+      if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {   // (uniform over the tile)
+        float mx = 0.f;
+        if constexpr (DIRECT) {
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-      if constexpr (G::WPT > 1) {
-        if (lane == 0) red[wv] = ss;
-        tile_sync<G::WPT>();
-        ss = red[0];
+          for (int i = 0; i < TileRegs<TS, NT, S>::GM_IT; ++i)
 #pragma unroll
-        for (int i = 1; i < G::WPT; ++i) ss += red[i];
+            for (int e = 0; e < 8; ++e) mx = __builtin_fmaxf(mx, __builtin_fabsf(vd[i][e]));
+        } else {
+#pragma unroll 1
+          for (int q = gt; q < TS * TS / 4; q += NT) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(st + (q / (TS / 4)) * PF + (q % (TS / 4)) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[e]));
+          }
+        }
+        tile_sync<G::WPT>();   // every wave has read the partial sums
+        mx = tile_max<G::WPT>(mx, red, lane, wv);
+        if (mx > 0.f && mx <= 0x1.fffffep127f) {   // (uniform) nonzero and finite
+          int ex;
+          (void)__builtin_frexpf(mx, &ex);
+          const float s1 = __builtin_ldexpf(1.f, (-ex) / 2), s2 = __builtin_ldexpf(1.f, -ex - (-ex) / 2);
+          float s2s = 0.f;
+          if constexpr (DIRECT) {
+#pragma unroll
+            for (int i = 0; i < TileRegs<TS, NT, S>::GM_IT; ++i)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                vd[i][e] = vd[i][e] * s1 * s2;
+                s2s = __builtin_fmaf(vd[i][e], vd[i][e], s2s);
+              }
+          } else {
+#pragma unroll 1
+            for (int q = gt; q < TS * TS / 4; q += NT) {
+              f32x4 *pv = reinterpret_cast<f32x4 *>(st + (q / (TS / 4)) * PF + (q % (TS / 4)) * 4);
+              f32x4 v = *pv;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                v[e] = v[e] * s1 * s2;
+                s2s = __builtin_fmaf(v[e], v[e], s2s);
+              }
+              *pv = v;
+            }
+          }
+          tile_sync<G::WPT>();   // every wave has read the maximum (and the staging copy is rescaled)
+          ss = tile_sum<G::WPT>(s2s, red, lane, wv);
+          es1 = s1;
+          es2 = s2;
+        }
       }
-      // a zero tile stays zero, also with eps = 0 (divisor 0)
-      const float den = __builtin_sqrtf(ss) + prm.eps;
+      // a zero tile stays zero, also with eps = 0 (divisor 0); (eps s1) s2 may round to
+      // infinity for a tile far below eps, whose X0 is then 0 (its true size is below
+      // the fp32 range)
+      const float den = __builtin_sqrtf(ss) + (prm.eps * es1) * es2;
       inv = den > 0.f ? 1.0f / den : 0.f;
     }
 

@@ -279,9 +279,26 @@ __global__ __launch_bounds__(THREADS) void gemm_momentum_kernel(const LayerDesc 
 }
 
 // ------------------------------------------------------------------ norm
+// Fixed-order workgroup maximum (4 waves); every thread gets the result.
+__device__ __forceinline__ float block_max(float v, float *red4) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float m = __builtin_fmaxf(__builtin_fmaxf(red4[0], red4[1]), __builtin_fmaxf(red4[2], red4[3]));
+  __syncthreads();
+  return m;
+}
+
 // One workgroup per tile: the partial sums in a fixed order; stores 1 / (sqrt(ss) + eps)
-// (1 in the identity test mode).
-__global__ __launch_bounds__(THREADS) void gemm_norm_kernel(const GemmTile *__restrict__ tiles, int first,
+// (1 in the identity test mode).  Outside [2^-100, 2^100] (a zero tile, entries beyond
+// about 1e15 or very small ones, an overflow) the fp32 sum of squares is recomputed from
+// the stored momentum scaled by the power of two s = s1 s2 that brings its largest
+// magnitude into [1/2, 1), and 1 / (|Y| + eps) = s / (s |Y| + s eps).  (That factor
+// leaves the fp32 normal range only for |Y| beyond about 2^126.)
+template <typename S>
+__global__ __launch_bounds__(THREADS) void gemm_norm_kernel(const LayerDesc *__restrict__ layers,
+                                                            const GemmTile *__restrict__ tiles, int first,
                                                             char *ws, float eps, int identity) {
   __shared__ float red4[4];
   const TileG t = tile_of(tiles, first + (int)blockIdx.x);
@@ -289,9 +306,44 @@ __global__ __launch_bounds__(THREADS) void gemm_norm_kernel(const GemmTile *__re
   float ss = 0.f;
   for (int q = threadIdx.x; q < t.nred; q += THREADS) ss += p[q];
   ss = block_sum(ss, red4);
-  // a zero tile stays zero, also with eps = 0 (divisor 0)
-  const float den = __builtin_sqrtf(ss) + eps;
-  if (threadIdx.x == 0) p[t.nred] = identity ? 1.0f : (den > 0.f ? 1.0f / den : 0.f);
+  float inv;
+  if (!identity && !(ss >= 0x1p-100f && ss <= 0x1p100f)) {   // uniform over the workgroup
+    const LayerDesc *L = layers + t.layer;
+    const S *mb = reinterpret_cast<const S *>(L->m);
+    const int64_t total = (int64_t)t.h * t.w, ldm = L->ld_m;
+    auto at = [&](int64_t e) -> float {
+      const int64_t o = (int64_t)(t.row0 + e / t.w) * ldm + t.col0 + e % t.w;
+      if constexpr (sizeof(S) == 2) {
+        return bf16_bits_to_f32(gmem(reinterpret_cast<const unsigned short *>(mb))[o]);
+      } else {
+        return gmem(mb)[o];
+      }
+    };
+    float mx = 0.f;
+    for (int64_t e = threadIdx.x; e < total; e += THREADS) mx = __builtin_fmaxf(mx, __builtin_fabsf(at(e)));
+    mx = block_max(mx, red4);
+    float s1 = 1.f, s2 = 1.f;
+    if (mx > 0.f && mx <= 0x1.fffffep127f) {   // nonzero and finite
+      int ex;
+      (void)__builtin_frexpf(mx, &ex);
+      s1 = __builtin_ldexpf(1.f, (-ex) / 2);
+      s2 = __builtin_ldexpf(1.f, -ex - (-ex) / 2);
+      float s2s = 0.f;
+      for (int64_t e = threadIdx.x; e < total; e += THREADS) {
+        const float v = at(e) * s1 * s2;
+        s2s = __builtin_fmaf(v, v, s2s);
+      }
+      ss = block_sum(s2s, red4);
+    }
+    // a zero tile stays zero, also with eps = 0 (divisor 0)
+    const float den = __builtin_sqrtf(ss) + (eps * s1) * s2;
+    inv = den > 0.f ? (s1 / den) * s2 : 0.f;
+  } else {
+    // a zero tile stays zero, also with eps = 0 (divisor 0)
+    const float den = __builtin_sqrtf(ss) + eps;
+    inv = den > 0.f ? 1.0f / den : 0.f;
+  }
+  if (threadIdx.x == 0) p[t.nred] = identity ? 1.0f : inv;
 }
 
 // ------------------------------------------------------------------ stage / apply
@@ -1386,7 +1438,7 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
     return hipErrorInvalidValue;
   if ((c.t256 || c.b256) && PREC != PREC_BF16 && PREC != PREC_BF16X3) return hipErrorInvalidValue;
   if (c.n_mom) hipLaunchKernelGGL(gemm_momentum_kernel<S>, grid(c.n_mom), dim3(THREADS), 0, stream, layers, tiles, c.mom, ws, p.beta);
-  if (c.tile_n) hipLaunchKernelGGL(gemm_norm_kernel, grid(c.tile_n), dim3(THREADS), 0, stream, tiles, (int)c.tile_first, ws, p.eps, p.identity);
+  if (c.tile_n) hipLaunchKernelGGL(gemm_norm_kernel<S>, grid(c.tile_n), dim3(THREADS), 0, stream, layers, tiles, (int)c.tile_first, ws, p.eps, p.identity);
   if (c.n_stg) hipLaunchKernelGGL((gemm_stage_kernel<S, PREC>), grid(c.n_stg), dim3(THREADS), 0, stream, layers, tiles, c.stg, ws);
   GemmParams gp{p.a, p.b, p.c, 0, PREC != PREC_BF16};
   auto products = [&](auto bkc) {
