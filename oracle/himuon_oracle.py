@@ -25,7 +25,7 @@ The page leaves the following open; the oracle takes the plainest reading:
   Distributed Muon Optimization", References), the quintic set
   (3.4445, -4.7750, 2.0315) is the one used by the Muon blog post cited there;
 * each tile is scaled by 1 / (||Y||_F + eps) before the first NS step (a zero tile
-  stays zero, also at eps = 0);
+  stays zero, also at eps = 0; a tile holding a NaN becomes all NaN);
 * a tile with more rows than columns is transposed, iterated, and transposed back;
   a square tile is not transposed;
 * tiles are anchored at (0, 0) in row-major order; the last tile row and column
@@ -68,10 +68,11 @@ def tiles(H: int, W: int, T: int | None):
 # ---------------------------------------------------------------- the NS map
 def frobenius_normalise(Y: np.ndarray, eps: float) -> np.ndarray:
     """X0 = Y / (||Y||_F + eps).  A zero tile maps to zero, also when eps = 0 (the
-    divisor is then 0 and the tile is left as it is)."""
+    divisor is then 0 and the tile is left as it is).  A tile holding a NaN has a NaN
+    norm, and the division passes it on to every entry, as IEEE arithmetic does."""
     Y = np.asarray(Y, dtype=np.float64)
     den = np.sqrt(np.sum(Y * Y)) + eps
-    return Y / den if den > 0 else np.zeros_like(Y)
+    return np.zeros_like(Y) if den == 0 else Y / den
 
 
 def ns_iterate(X: np.ndarray, K: int, coeffs) -> np.ndarray:

@@ -257,6 +257,25 @@ def test_extreme_magnitudes(T, scale, eps, prec, K):
         assert mx <= (1e-4 if prec == 0 else 2e-2) * max(1.0, float(np.abs(O).max())), (mx, rf)
 
 
+@pytest.mark.parametrize("T", [32, 64, 128, 256])
+@pytest.mark.parametrize("prec", [0, 2, 3])
+def test_nan_stays_in_its_tile(T, prec):
+    """A NaN entry makes its tile's output NaN (its norm is NaN) and leaves every other
+    tile as the oracle has it, on the fused path and the large-tile path."""
+    state = torch.float32 if prec == 0 else torch.bfloat16
+    G = power_law(300, 520, 81)
+    G[70, 130] = float("nan")
+    (res,), _ = gpu_step([G], T, K=5, prec=prec, state=state)
+    W, M, U = res[0]
+    O = oracle.tiled_ns(M.double().numpy(), T, 5, Q)
+    nan = np.isnan(O)
+    assert nan.sum() == (min(T, 300 - 70 // T * T) * min(T, 520 - 130 // T * T))
+    assert np.array_equal(np.isnan(U.numpy()), nan)
+    d = U.double().numpy()[~nan] - O[~nan]
+    mx, rf = float(np.abs(d).max()), float(np.linalg.norm(d) / np.linalg.norm(O[~nan]))
+    assert mx <= (1e-4 if prec == 0 else 2e-2) and rf <= (1e-4 if prec == 0 else 1e-2), (mx, rf)
+
+
 IDENTITY_SHAPES = [(100, 113), (113, 100), (300, 170), (170, 300), (1, 257), (257, 1), (513, 129)]
 
 

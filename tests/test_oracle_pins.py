@@ -249,6 +249,22 @@ def test_zero_tile_maps_to_zero():
                                   np.array([[0.0, -1.0, 1.0]]))
 
 
+def test_nan_stays_in_its_tile():
+    # a NaN entry makes its tile's norm NaN, and IEEE division passes it to every entry
+    # of that tile; tile locality keeps every other tile as it was (also at eps = 0)
+    M = rng_matrix(128, 192, 14)
+    ref = oracle.tiled_ns(M, 64, 5, Q)
+    M[70, 130] = np.nan
+    for eps in (1e-7, 0.0):
+        O = oracle.tiled_ns(M, 64, 5, Q, eps=eps)
+        assert np.isnan(O[64:, 128:]).all()
+        mask = np.ones_like(O, dtype=bool)
+        mask[64:, 128:] = False
+        assert np.isfinite(O[mask]).all()
+        if eps:
+            assert np.array_equal(O[mask], ref[mask])
+
+
 # ------------------------------------------------------------------ P7 invariances
 def test_scale_sign_and_orthogonal_invariance():
     Y = rng_matrix(48, 80, 12)

@@ -1392,7 +1392,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
       // infinity for a tile far below eps, whose X0 is then 0 (its true size is below
       // the fp32 range)
       const float den = __builtin_sqrtf(ss) + (prm.eps * es1) * es2;
-      inv = den > 0.f ? 1.0f / den : 0.f;
+      inv = den > 0.f ? 1.0f / den : (den == 0.f ? 0.f : den);   // a NaN (from NaN entries) passes on
     }
 
     // X in registers (fp32, MFMA output layout of the update product: block holds X^T)

@@ -337,11 +337,11 @@ __global__ __launch_bounds__(THREADS) void gemm_norm_kernel(const LayerDesc *__r
     }
     // a zero tile stays zero, also with eps = 0 (divisor 0)
     const float den = __builtin_sqrtf(ss) + (eps * s1) * s2;
-    inv = den > 0.f ? (s1 / den) * s2 : 0.f;
+    inv = den > 0.f ? (s1 / den) * s2 : (den == 0.f ? 0.f : den);   // a NaN (from NaN entries) passes on
   } else {
     // a zero tile stays zero, also with eps = 0 (divisor 0)
     const float den = __builtin_sqrtf(ss) + eps;
-    inv = den > 0.f ? 1.0f / den : 0.f;
+    inv = den > 0.f ? 1.0f / den : (den == 0.f ? 0.f : den);   // a NaN (from NaN entries) passes on
   }
   if (threadIdx.x == 0) p[t.nred] = identity ? 1.0f : inv;
 }
