@@ -37,7 +37,7 @@ METRIC = "HiMuon step ms & NS TFLOP/s (% MFMA peak) vs T, 8B-shaped stack"
 # rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), scaled by the
 # readings of a 1 GiB elementwise copy (x2.0 read, x1.0 write).  Valid only for the
 # kernel source it was measured on (sha256 prefix of ns_fused.hip); null otherwise.
-TRAFFIC_T128 = {"source_sha256_16": "77c1e85fc5955fe8", "precision": "bf16f8", "fetch_kib": 27291201.875,
+TRAFFIC_T128 = {"source_sha256_16": "520b407949a22600", "precision": "bf16f8", "fetch_kib": 27291209.4375,
                 "write_kib": 40894464.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 
