@@ -959,9 +959,18 @@ struct T2Lds {
 // leaves (b / c) A in them (fp32, as accumulated) after storing A, and the square
 // product accumulates A A^T onto that, so B = c ((b / c) A + A^2) needs no second read
 // of A; the Gram and update products start from zero.
-template <int PREC, int MODE>
+// The W update of a 256-tile, fused into the epilogue of its last update product: the
+// step's O is X_K in fp32 as the epilogue forms it (256-tiles are square, so never
+// transposed), W <- W - lr O by one fused multiply-add, and O itself to U when asked.
+struct T256Apply {
+  const LayerDesc *layers;
+  float lr;
+  int write_u;
+};
+
+template <int PREC, int MODE, bool APPLY = false>
 __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const GemmParams &gp, char *lds,
-                                             f32x16 (&acc)[2][4]) {
+                                             f32x16 (&acc)[2][4], const T256Apply &ap = T256Apply{}) {
   static_assert(PREC == PREC_BF16 || PREC == PREC_BF16X3, "bf16 planes");
   using LD = T2Lds<PREC, MODE>;
   // (the thread index is made opaque so that the addresses derived from it are formed
@@ -1129,7 +1138,34 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
           v[q] = fold ? d : __builtin_fmaf(a, e[q], d);
         }
       }
-      O.put16(i, j, v);
+      if constexpr (APPLY) {
+        const LayerDesc *L = ap.layers + t.layer;
+        float *wrow = L->w + (int64_t)(t.row0 + i) * L->ld_w + t.col0 + j;
+        const float nlr = -ap.lr;
+        if (L->vec_w) {   // 16-byte aligned rows (the tile's columns start at a multiple of 256)
+          GLOBAL_AS f32x4 *pw = reinterpret_cast<GLOBAL_AS f32x4 *>(gmem(wrow));
+          f32x4 w4[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) w4[m] = pw[m];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) w4[m][e2] = __builtin_fmaf(nlr, v[4 * m + e2], w4[m][e2]);
+            pw[m] = w4[m];
+          }
+        } else {
+          GLOBAL_AS float *pw = gmem(wrow);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) pw[q] = __builtin_fmaf(nlr, v[q], pw[q]);
+        }
+        if (ap.write_u) {
+          GLOBAL_AS float *pu = gmem(L->u + (int64_t)(t.row0 + i) * L->ld_u + t.col0 + j);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) pu[q] = v[q];
+        }
+      } else {
+        O.put16(i, j, v);
+      }
     }
     __syncthreads();   // the staging read before the next half lands
   }
@@ -1159,7 +1195,8 @@ constexpr int t256_ns_lds() {
 }
 template <int PREC>
 __global__ __launch_bounds__(T2_THREADS) void gemm_t256_ns_kernel(const GemmTile *__restrict__ tiles, int first,
-                                                                  char *ws, GemmParams gp, int steps) {
+                                                                  char *ws, GemmParams gp, int steps,
+                                                                  T256Apply ap) {
   __shared__ __attribute__((aligned(16))) char lds[t256_ns_lds<PREC>()];
   const TileG t = tile_of(tiles, first + (int)blockIdx.x);
   f32x16 acc[2][4];
@@ -1168,7 +1205,11 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_t256_ns_kernel(const GemmTile
     // loads see them: one workgroup, one CU, one L1)
     t256_product<PREC, MODE_GRAM>(t, ws, gp, lds, acc);
     if (gp.c != 0.f) t256_product<PREC, MODE_SQUARE>(t, ws, gp, lds, acc);
-    t256_product<PREC, MODE_UPDATE>(t, ws, gp, lds, acc);
+    if (it + 1 < steps) {
+      t256_product<PREC, MODE_UPDATE>(t, ws, gp, lds, acc);
+    } else {   // the last update applies O to W instead of storing X_K
+      t256_product<PREC, MODE_UPDATE, true>(t, ws, gp, lds, acc, ap);
+    }
   }
 }
 
@@ -1452,9 +1493,9 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
     }
   };
   if constexpr (PREC == PREC_BF16 || PREC == PREC_BF16X3) {
-    if (c.t256) {
+    if (c.t256 && p.steps > 0) {
       hipLaunchKernelGGL((gemm_t256_ns_kernel<PREC>), dim3((unsigned)c.tile_n), dim3(T2_THREADS), 0, stream, tiles,
-                         (int)c.tile_first, ws, gp, p.steps);
+                         (int)c.tile_first, ws, gp, p.steps, T256Apply{layers, p.lr, p.write_update});
     }
   }
   if constexpr (PREC == PREC_BF16 || PREC == PREC_BF16X3) {
@@ -1476,7 +1517,9 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
   } else {
     products(std::integral_constant<int, 32>{});
   }
-  // the 256-tile kernel leaves X in the x0 planes; the per-product launches alternate
+  // the 256-tile kernel applies W itself after its last step (with no steps, X0 is
+  // applied from the x0 planes); the per-product launches alternate the X buffers
+  if (c.t256 && p.steps > 0) return hipGetLastError();
   const int xfinal = c.t256 ? 0 : (p.steps & 1);
   if (c.n_app)
     hipLaunchKernelGGL((gemm_apply_kernel<PREC>), grid(c.n_app), dim3(THREADS), 0, stream, layers, tiles, c.app, ws,
