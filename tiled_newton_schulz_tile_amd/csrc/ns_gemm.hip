@@ -959,14 +959,139 @@ struct T2Lds {
 // leaves (b / c) A in them (fp32, as accumulated) after storing A, and the square
 // product accumulates A A^T onto that, so B = c ((b / c) A + A^2) needs no second read
 // of A; the Gram and update products start from zero.
-// The W update of a 256-tile, fused into the epilogue of its last update product: the
-// step's O is X_K in fp32 as the epilogue forms it (256-tiles are square, so never
-// transposed), W <- W - lr O by one fused multiply-add, and O itself to U when asked.
+// The step's ends for a 256-tile, fused into the tile's workgroup: the momentum, the
+// norm and X0 before the first product, and the W update in the epilogue of the last
+// update product (the step's O is X_K in fp32 as that epilogue forms it; 256-tiles are
+// square, so never transposed): W <- W - lr O by one fused multiply-add, and O itself to
+// U when asked.
 struct T256Apply {
   const LayerDesc *layers;
   float lr;
   int write_u;
+  float beta, eps;
 };
+
+// Fixed-order sum and maximum over the 8 waves of a 256-tile workgroup; every thread
+// gets the result.
+__device__ __forceinline__ float t256_sum(float v, float *red8) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red8[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = ((red8[0] + red8[1]) + (red8[2] + red8[3])) + ((red8[4] + red8[5]) + (red8[6] + red8[7]));
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ float t256_max(float v, float *red8) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, off, 64));
+  if ((threadIdx.x & 63) == 0) red8[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red8[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) r = __builtin_fmaxf(r, red8[k]);
+  __syncthreads();
+  return r;
+}
+
+// M <- beta M + G for the 256-tile (stored in the state dtype), 1 / (|M|_F + eps) of the
+// stored values, and X0 = M inv into the x0 planes.  Thread t takes 8 columns of rows
+// t / 32 + 16 k, k < 16, in every pass, so each thread re-reads only what it stored.  The
+// norm is rescaled by a power of two where its sum of squares leaves [2^-100, 2^100], as
+// in the norm kernel.
+template <typename S, int PREC>
+__device__ __forceinline__ void t256_front(const TileG &t, char *ws, const T256Apply &io, float *red8) {
+  const LayerDesc *L = io.layers + t.layer;
+  S *mb = reinterpret_cast<S *>(L->m);
+  const S *gb = reinterpret_cast<const S *>(L->g);
+  const int64_t ldm = L->ld_m, ldg = L->ld_g;
+  const int cc = (threadIdx.x & 31) * 8, rr = threadIdx.x >> 5;
+  const bool vec = L->vec_ok;   // rows 16-byte aligned (the tile's columns start at a multiple of 256)
+  const float beta = io.beta;
+  float ss = 0.f;
+  for (int k = 0; k < T2 / 16; ++k) {
+    const int i = rr + 16 * k;
+    S *mp = mb + (int64_t)(t.row0 + i) * ldm + t.col0 + cc;
+    const S *gp = gb + (int64_t)(t.row0 + i) * ldg + t.col0 + cc;
+    float v[8];
+    if constexpr (sizeof(S) == 2) {
+      unsigned short code[8];
+      if (vec) {
+        const u32x4 m = *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(mp));
+        const u32x4 g = *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(gp));
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const unsigned mw = m[q >> 1], gw = g[q >> 1];
+          code[q] = to_bf16_bits(__builtin_fmaf(beta, __builtin_bit_cast(float, (q & 1) ? (mw & 0xffff0000u) : (mw << 16)),
+                                                __builtin_bit_cast(float, (q & 1) ? (gw & 0xffff0000u) : (gw << 16))));
+        }
+        *reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(mp)) =
+            u32x4{code[0] | (unsigned)code[1] << 16, code[2] | (unsigned)code[3] << 16,
+                  code[4] | (unsigned)code[5] << 16, code[6] | (unsigned)code[7] << 16};
+      } else {
+        GLOBAL_AS unsigned short *m16 = gmem(reinterpret_cast<unsigned short *>(mp));
+        const GLOBAL_AS unsigned short *g16 = gmem(reinterpret_cast<const unsigned short *>(gp));
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          code[q] = to_bf16_bits(__builtin_fmaf(beta, bf16_bits_to_f32(m16[q]), bf16_bits_to_f32(g16[q])));
+          m16[q] = code[q];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = bf16_bits_to_f32(code[q]);
+    } else {
+      GLOBAL_AS float *m32 = gmem(mp);
+      const GLOBAL_AS float *g32 = gmem(gp);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        v[q] = __builtin_fmaf(beta, m32[q], g32[q]);
+        m32[q] = v[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ss = __builtin_fmaf(v[q], v[q], ss);
+  }
+  ss = t256_sum(ss, red8);
+  float s1 = 1.f, s2 = 1.f;
+  if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {   // uniform over the workgroup
+    float mx = 0.f;
+    for (int k = 0; k < T2 / 16; ++k) {
+      float v[8];
+      load_state8<S>(L, mb, ldm, t, rr + 16 * k, cc, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) mx = __builtin_fmaxf(mx, __builtin_fabsf(v[q]));
+    }
+    mx = t256_max(mx, red8);
+    if (mx > 0.f && mx <= 0x1.fffffep127f) {   // nonzero and finite
+      int ex;
+      (void)__builtin_frexpf(mx, &ex);
+      s1 = __builtin_ldexpf(1.f, (-ex) / 2);
+      s2 = __builtin_ldexpf(1.f, -ex - (-ex) / 2);
+      float s2s = 0.f;
+      for (int k = 0; k < T2 / 16; ++k) {
+        float v[8];
+        load_state8<S>(L, mb, ldm, t, rr + 16 * k, cc, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float x = v[q] * s1 * s2;
+          s2s = __builtin_fmaf(x, x, s2s);
+        }
+      }
+      ss = t256_sum(s2s, red8);
+    }
+  }
+  // a zero tile stays zero, also with eps = 0 (divisor 0); a NaN passes on
+  const float den = __builtin_sqrtf(ss) + (io.eps * s1) * s2;
+  const float inv = den > 0.f ? (s1 / den) * s2 : (den == 0.f ? 0.f : den);
+  const Planes<PREC> X{ws + t.x0, t.r, t.ldx};
+  for (int k = 0; k < T2 / 16; ++k) {
+    float v[8];
+    load_state8<S>(L, mb, ldm, t, rr + 16 * k, cc, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] *= inv;
+    X.put8(rr + 16 * k, cc, v);
+  }
+  __syncthreads();   // X0 complete before the first product reads it
+}
 
 template <int PREC, int MODE, bool APPLY = false>
 __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const GemmParams &gp, char *lds,
@@ -1193,12 +1318,14 @@ constexpr int t256_ns_lds() {
                 u = T2Lds<PREC, MODE_UPDATE>::BYTES;
   return g > s ? (g > u ? g : u) : (s > u ? s : u);
 }
-template <int PREC>
+template <typename S, int PREC>
 __global__ __launch_bounds__(T2_THREADS) void gemm_t256_ns_kernel(const GemmTile *__restrict__ tiles, int first,
                                                                   char *ws, GemmParams gp, int steps,
                                                                   T256Apply ap) {
   __shared__ __attribute__((aligned(16))) char lds[t256_ns_lds<PREC>()];
+  __shared__ float red8[8];
   const TileG t = tile_of(tiles, first + (int)blockIdx.x);
+  t256_front<S, PREC>(t, ws, ap, red8);
   f32x16 acc[2][4];
   for (int it = 0; it < steps; ++it) {
     // (each product ends at a barrier after its last global stores, so the next one's
@@ -1478,9 +1605,12 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
       c.n_app > 0x7fffffff || c.tile_first + c.tile_n > 0x7fffffff)
     return hipErrorInvalidValue;
   if ((c.t256 || c.b256) && PREC != PREC_BF16 && PREC != PREC_BF16X3) return hipErrorInvalidValue;
-  if (c.n_mom) hipLaunchKernelGGL(gemm_momentum_kernel<S>, grid(c.n_mom), dim3(THREADS), 0, stream, layers, tiles, c.mom, ws, p.beta);
-  if (c.tile_n) hipLaunchKernelGGL(gemm_norm_kernel<S>, grid(c.tile_n), dim3(THREADS), 0, stream, layers, tiles, (int)c.tile_first, ws, p.eps, p.identity);
-  if (c.n_stg) hipLaunchKernelGGL((gemm_stage_kernel<S, PREC>), grid(c.n_stg), dim3(THREADS), 0, stream, layers, tiles, c.stg, ws);
+  // 256-tile chunks with NS steps run the momentum, the norm and X0 inside their NS
+  // kernel (the identity mode has no NS steps)
+  const bool front = c.t256 && p.steps > 0;
+  if (c.n_mom && !front) hipLaunchKernelGGL(gemm_momentum_kernel<S>, grid(c.n_mom), dim3(THREADS), 0, stream, layers, tiles, c.mom, ws, p.beta);
+  if (c.tile_n && !front) hipLaunchKernelGGL(gemm_norm_kernel<S>, grid(c.tile_n), dim3(THREADS), 0, stream, layers, tiles, (int)c.tile_first, ws, p.eps, p.identity);
+  if (c.n_stg && !front) hipLaunchKernelGGL((gemm_stage_kernel<S, PREC>), grid(c.n_stg), dim3(THREADS), 0, stream, layers, tiles, c.stg, ws);
   GemmParams gp{p.a, p.b, p.c, 0, PREC != PREC_BF16};
   auto products = [&](auto bkc) {
     constexpr int BK = decltype(bkc)::value;
@@ -1494,8 +1624,8 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
   };
   if constexpr (PREC == PREC_BF16 || PREC == PREC_BF16X3) {
     if (c.t256 && p.steps > 0) {
-      hipLaunchKernelGGL((gemm_t256_ns_kernel<PREC>), dim3((unsigned)c.tile_n), dim3(T2_THREADS), 0, stream, tiles,
-                         (int)c.tile_first, ws, gp, p.steps, T256Apply{layers, p.lr, p.write_update});
+      hipLaunchKernelGGL((gemm_t256_ns_kernel<S, PREC>), dim3((unsigned)c.tile_n), dim3(T2_THREADS), 0, stream, tiles,
+                         (int)c.tile_first, ws, gp, p.steps, T256Apply{layers, p.lr, p.write_update, p.beta, p.eps});
     }
   }
   if constexpr (PREC == PREC_BF16 || PREC == PREC_BF16X3) {
