@@ -414,6 +414,41 @@ def test_leading_dimension(ld_extra, prec):
     assert (Ub[:, W:] == 0).all() and (Wb[:, W:] == 0).all() and (Mb[:, W:] == 0).all()
 
 
+@pytest.mark.parametrize("ld_extra", [0, 3, 8])
+@pytest.mark.parametrize("state", [torch.bfloat16, torch.float32])
+def test_leading_dimension_256_tiles(ld_extra, state):
+    """256 x 256 tiles run the whole step in one workgroup (momentum, norm, X0, the NS
+    steps and the W update); rows that are not 16-byte aligned take its element paths.
+    Momentum bit for bit, O within the bar, padding columns untouched."""
+    _need_gpu()
+    H, W = 512, 768
+    G = power_law(H, W, 17)
+    M0 = 0.5 * power_law(H, W, 18)
+    ld = W + ld_extra
+    Gb = torch.zeros(H, ld, dtype=state, device=DEV)
+    Mb = torch.zeros(H, ld, dtype=state, device=DEV)
+    Wb = torch.zeros(H, ld, dtype=torch.float32, device=DEV)
+    Ub = torch.zeros(H, ld, dtype=torch.float32, device=DEV)
+    Gb[:, :W] = G.to(state).to(DEV)
+    Mb[:, :W] = M0.to(state).to(DEV)
+    m_prev = Mb[:, :W].float().cpu().numpy()
+    g = Gb[:, :W].float().cpu().numpy()
+    views = [t[:, :W] for t in (Wb, Mb, Gb, Ub)]
+    prec = hm.PREC_BF16X3
+    opt = hm.HiMuon([tuple(views)], 256, 5, Q, precision=prec)
+    assert opt.stats()["gemm_tiles"] == 6
+    opt.step(0.02)
+    torch.cuda.synchronize()
+    opt.close()
+    want_m = oracle.momentum_stored(m_prev, g, 0.95, "bf16" if state == torch.bfloat16 else "f32")
+    assert np.array_equal(views[1].float().cpu().numpy(), want_m)
+    O = oracle.tiled_ns(want_m.astype(np.float64), 256, 5, Q)
+    assert_bar(views[3].cpu(), O, prec, tight=2e-3)
+    W1 = views[0].double().cpu().numpy()
+    assert np.abs(W1 + 0.02 * views[3].double().cpu().numpy()).max() <= 1e-7
+    assert (Ub[:, W:] == 0).all() and (Wb[:, W:] == 0).all() and (Mb[:, W:] == 0).all()
+
+
 def test_plan_stats_and_empty_layer_on_gpu():
     _need_gpu()
     Wt = torch.zeros(0, 5, device=DEV)
