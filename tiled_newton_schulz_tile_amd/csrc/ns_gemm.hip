@@ -928,7 +928,9 @@ __global__ __launch_bounds__(THREADS) void gemm_ns_kernel(const GemmTile *__rest
 // once per 128-block (three or four times).  The symmetric products compute every block
 // (no mirror); K = 256 through two LDS stages, in slices of 64 (whole 128-byte lines,
 // twice the bytes in flight) for the symmetric products and of 32 for the update, whose
-// two operand panels leave no registers for more.  bf16 and bf16x3 planes.
+// two operand panels leave no registers for more.  bf16 and bf16x3 planes.  With c != 0
+// the Gram writes only columns 128.. of A to the workspace and hands rows 0..127 (by
+// symmetry the square's first two K slices) to the square through LDS.
 constexpr int T2 = 256, T2_THREADS = 512;
 
 
@@ -1198,18 +1200,34 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
     }
   };
 
-  // the next slice's loads are in flight while the MFMAs read the current stage
-  load(0);
-  store(lds);
-  __syncthreads();
-  int cur = 0;
-  for (int kb = 0; kb < T2; kb += LD::BK) {
-    const bool more = kb + LD::BK < T2;
-    if (more) load(kb + LD::BK);
-    compute(lds + cur * LD::STAGE);
-    if (more) store(lds + (cur ^ 1) * LD::STAGE);
+  if constexpr (MODE == MODE_SQUARE) {
+    // Slices 0 and 1 (k < 128) are already in stages 0 and 1, written there from the
+    // Gram's accumulators; slice n + 2 is loaded while slice n is multiplied and takes
+    // its stage after it.
+    constexpr int NSL = T2 / LD::BK;
+    static_assert(NSL == 4, "two slices handed over, two loaded");
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) {
+      const bool more = n + 2 < NSL;
+      if (more) load((n + 2) * LD::BK);
+      compute(lds + (n & 1) * LD::STAGE);
+      __syncthreads();
+      if (more) store(lds + (n & 1) * LD::STAGE);
+    }
+  } else {
+    // the next slice's loads are in flight while the MFMAs read the current stage
+    load(0);
+    store(lds);
     __syncthreads();
-    cur ^= 1;
+    int cur = 0;
+    for (int kb = 0; kb < T2; kb += LD::BK) {
+      const bool more = kb + LD::BK < T2;
+      if (more) load(kb + LD::BK);
+      compute(lds + cur * LD::STAGE);
+      if (more) store(lds + (cur ^ 1) * LD::STAGE);
+      __syncthreads();
+      cur ^= 1;
+    }
   }
 
   // ---- epilogue, one column half at a time: the half staged in LDS (fp32), then rows
@@ -1218,8 +1236,13 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
   const float a = gp.a, b = gp.b, c = gp.c;
   const bool fold = gp.fold != 0;
   const Planes<PREC> O = MODE == MODE_GRAM ? (c != 0.f ? A : B) : (MODE == MODE_SQUARE ? B : Xn);
+  // With c != 0 the Gram's A goes to the square product alone: its columns 128.. (the
+  // square's last two K slices) through the workspace, its rows 0..127 (by symmetry the
+  // first two slices) straight into the square's LDS stages below.
+  const bool handover = MODE == MODE_GRAM && c != 0.f;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
+    if (handover && h == 0) continue;   // (uniform)
     if (wn == h) {
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi)
@@ -1295,6 +1318,39 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
     __syncthreads();   // the staging read before the next half lands
   }
   if constexpr (MODE == MODE_GRAM) {
+    if (handover) {
+      // Element (i, k) of the square's row panel is A(k, i): rows k < 128 of A, held by
+      // the waves with wm < 2, are slice wm of that panel.  Each lane holds four
+      // consecutive k of one i, one 8-byte piece of a panel row, in the square's stage
+      // layout and split into hi and lo as the workspace planes would hold them.  (The
+      // accumulated A(k, i) and A(i, k) can differ in the last fp32 bits: the bf16x3
+      // correction terms reach them in opposite orders.)
+      using LS = T2Lds<PREC, MODE_SQUARE>;
+      if (wm < 2) {
+        char *stage = lds + wm * LS::STAGE;
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int kl = bi * 32 + 8 * g + 4 * half;   // k - 64 wm
+              const int i = wn * 128 + bj * 32 + li;
+              const float x[4] = {acc[bi][bj][4 * g], acc[bi][bj][4 * g + 1], acc[bi][bj][4 * g + 2],
+                                  acc[bi][bj][4 * g + 3]};
+              const u32x2 hi = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+              const int o = (i * LS::RP + kl) * 2;
+              *reinterpret_cast<u32x2 *>(stage + o) = hi;
+              if constexpr (LS::NPL == 2)
+                *reinterpret_cast<u32x2 *>(stage + LS::ROWT + o) =
+                    u32x2{pack_bf16x2(x[0] - __builtin_bit_cast(float, hi[0] << 16),
+                                      x[1] - __builtin_bit_cast(float, hi[0] & 0xffff0000u)),
+                          pack_bf16x2(x[2] - __builtin_bit_cast(float, hi[1] << 16),
+                                      x[3] - __builtin_bit_cast(float, hi[1] & 0xffff0000u))};
+            }
+      }
+      __syncthreads();   // both stages complete before the square reads them
+    }
     if (c != 0.f) {   // (uniform) seed the square product with (b / c) A
       const float bc = b / c;
 #pragma unroll
