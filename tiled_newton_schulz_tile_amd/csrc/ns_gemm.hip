@@ -1095,6 +1095,47 @@ __device__ __forceinline__ void t256_front(const TileG &t, char *ws, const T256A
   __syncthreads();   // X0 complete before the first product reads it
 }
 
+// Hand the rows k < 64 NW of a symmetric product's result (held in the accumulators
+// of the waves with wm < NW) to the next product as the first K slices of its row
+// panel: element (i, k) of that panel is R(k, i), so each lane's four consecutive rows
+// k of one column i are one 8-byte piece of panel row i, in the consumer's stage layout
+// LS (slice k / BK in stage k / BK) and split into hi and lo as the workspace planes
+// would hold them.  val(d, k, i) forms the result from the accumulated d, as the
+// producer's epilogue does.  (The accumulated R(k, i) and R(i, k) can differ in the
+// last fp32 bits: the bf16x3 correction terms reach them in opposite orders.)
+template <class LS, int NW, class F>
+__device__ __forceinline__ void t256_hand_over(const f32x16 (&acc)[2][4], char *lds, int wm, int wn, int li, int half,
+                                               F &&val) {
+  static_assert(64 * NW <= 2 * LS::BK, "the handed-over slices fit the two stages");
+  if (wm < NW) {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+      const int k0 = wm * 64 + bi * 32;   // a multiple of 32: one slice per bi
+      char *stage = lds + (k0 / LS::BK) * LS::STAGE;
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int k = k0 + 8 * g + 4 * half;
+          const int i = wn * 128 + bj * 32 + li;
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = val(acc[bi][bj][4 * g + e], k + e, i);
+          const u32x2 hi = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+          const int o = (i * LS::RP + k % LS::BK) * 2;
+          *reinterpret_cast<u32x2 *>(stage + o) = hi;
+          if constexpr (LS::NPL == 2)
+            *reinterpret_cast<u32x2 *>(stage + LS::ROWT + o) =
+                u32x2{pack_bf16x2(x[0] - __builtin_bit_cast(float, hi[0] << 16),
+                                  x[1] - __builtin_bit_cast(float, hi[0] & 0xffff0000u)),
+                      pack_bf16x2(x[2] - __builtin_bit_cast(float, hi[1] << 16),
+                                  x[3] - __builtin_bit_cast(float, hi[1] & 0xffff0000u))};
+        }
+    }
+  }
+  __syncthreads();   // the stages are complete before the next product reads them
+}
+
 template <int PREC, int MODE, bool APPLY = false>
 __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const GemmParams &gp, char *lds,
                                              f32x16 (&acc)[2][4], const T256Apply &ap = T256Apply{}) {
@@ -1214,6 +1255,44 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
       __syncthreads();
       if (more) store(lds + (n & 1) * LD::STAGE);
     }
+  } else if constexpr (MODE == MODE_UPDATE) {
+    // The B row panels of slices 0 and 1 (k < 64) are already in stages 0 and 1, written
+    // there by the product that formed B; their X column panels are loaded first (slice
+    // 1's into the row registers, which these slices do not need).  Then slice n + 2 is
+    // loaded while slice n is multiplied and takes its stage after it.
+    constexpr int NSL = T2 / LD::BK;
+#pragma unroll
+    for (int pl = 0; pl < LD::NPL; ++pl) {
+      const __bf16 *xb = pl ? Xc.lo() : Xc.hi();
+#pragma unroll
+      for (int q = 0; q < LD::NQ; ++q) {
+        const int idx = tid + q * T2_THREADS;
+        const int kr = idx / (T2 / 8), cc = idx % (T2 / 8);
+        rr_[pl * LD::NQ + q] = *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(xb + (int64_t)kr * T2 + cc * 8));
+        rl_[pl * LD::NQ + q] =
+            *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(xb + (int64_t)(LD::BK + kr) * T2 + cc * 8));
+      }
+    }
+#pragma unroll
+    for (int pl = 0; pl < LD::NPL; ++pl) {
+#pragma unroll
+      for (int q = 0; q < LD::NQ; ++q) {
+        const int idx = tid + q * T2_THREADS;
+        const int kr = idx / (T2 / 8), cc = idx % (T2 / 8);
+        const int o = LD::NPL * LD::ROWT + pl * LD::COLT + (kr * LD::CP + cc * 8) * 2;
+        *reinterpret_cast<u32x4 *>(lds + o) = rr_[pl * LD::NQ + q];
+        *reinterpret_cast<u32x4 *>(lds + LD::STAGE + o) = rl_[pl * LD::NQ + q];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) {
+      const bool more = n + 2 < NSL;
+      if (more) load((n + 2) * LD::BK);
+      compute(lds + (n & 1) * LD::STAGE);
+      __syncthreads();
+      if (more) store(lds + (n & 1) * LD::STAGE);
+    }
   } else {
     // the next slice's loads are in flight while the MFMAs read the current stage
     load(0);
@@ -1238,11 +1317,14 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
   const Planes<PREC> O = MODE == MODE_GRAM ? (c != 0.f ? A : B) : (MODE == MODE_SQUARE ? B : Xn);
   // With c != 0 the Gram's A goes to the square product alone: its columns 128.. (the
   // square's last two K slices) through the workspace, its rows 0..127 (by symmetry the
-  // first two slices) straight into the square's LDS stages below.
-  const bool handover = MODE == MODE_GRAM && c != 0.f;
+  // first two slices) straight into the square's LDS stages below.  B (from the square,
+  // or from the Gram when c = 0) goes to the update the same way: columns 64.. through
+  // the workspace, rows 0..63 into the update's first two stages.
+  const bool hand_a = MODE == MODE_GRAM && c != 0.f;
+  const bool hand_b = MODE == MODE_SQUARE || (MODE == MODE_GRAM && c == 0.f);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    if (handover && h == 0) continue;   // (uniform)
+    if (hand_a && h == 0) continue;   // (uniform)
     if (wn == h) {
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi)
@@ -1312,44 +1394,18 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
           for (int q = 0; q < 16; ++q) pu[q] = v[q];
         }
       } else {
-        O.put16(i, j, v);
+        if (!(hand_b && j < 64)) O.put16(i, j, v);
       }
     }
     __syncthreads();   // the staging read before the next half lands
   }
   if constexpr (MODE == MODE_GRAM) {
-    if (handover) {
-      // Element (i, k) of the square's row panel is A(k, i): rows k < 128 of A, held by
-      // the waves with wm < 2, are slice wm of that panel.  Each lane holds four
-      // consecutive k of one i, one 8-byte piece of a panel row, in the square's stage
-      // layout and split into hi and lo as the workspace planes would hold them.  (The
-      // accumulated A(k, i) and A(i, k) can differ in the last fp32 bits: the bf16x3
-      // correction terms reach them in opposite orders.)
-      using LS = T2Lds<PREC, MODE_SQUARE>;
-      if (wm < 2) {
-        char *stage = lds + wm * LS::STAGE;
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-          for (int bj = 0; bj < 4; ++bj)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int kl = bi * 32 + 8 * g + 4 * half;   // k - 64 wm
-              const int i = wn * 128 + bj * 32 + li;
-              const float x[4] = {acc[bi][bj][4 * g], acc[bi][bj][4 * g + 1], acc[bi][bj][4 * g + 2],
-                                  acc[bi][bj][4 * g + 3]};
-              const u32x2 hi = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-              const int o = (i * LS::RP + kl) * 2;
-              *reinterpret_cast<u32x2 *>(stage + o) = hi;
-              if constexpr (LS::NPL == 2)
-                *reinterpret_cast<u32x2 *>(stage + LS::ROWT + o) =
-                    u32x2{pack_bf16x2(x[0] - __builtin_bit_cast(float, hi[0] << 16),
-                                      x[1] - __builtin_bit_cast(float, hi[0] & 0xffff0000u)),
-                          pack_bf16x2(x[2] - __builtin_bit_cast(float, hi[1] << 16),
-                                      x[3] - __builtin_bit_cast(float, hi[1] & 0xffff0000u))};
-            }
-      }
-      __syncthreads();   // both stages complete before the square reads them
+    if (hand_a) {
+      t256_hand_over<T2Lds<PREC, MODE_SQUARE>, 2>(acc, lds, wm, wn, li, half, [](float d, int, int) { return d; });
+    } else {
+      t256_hand_over<T2Lds<PREC, MODE_UPDATE>, 1>(acc, lds, wm, wn, li, half, [&](float d, int r, int q) {
+        return b * d + ((fold && r == q) ? a : 0.f);
+      });
     }
     if (c != 0.f) {   // (uniform) seed the square product with (b / c) A
       const float bc = b / c;
@@ -1360,6 +1416,11 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc[bi][bj][e] *= bc;
     }
+  }
+  if constexpr (MODE == MODE_SQUARE) {
+    t256_hand_over<T2Lds<PREC, MODE_UPDATE>, 1>(acc, lds, wm, wn, li, half, [&](float d, int r, int q) {
+      return c * d + ((fold && r == q) ? a : 0.f);   // d = (b / c) A + A^2
+    });
   }
 }
 
