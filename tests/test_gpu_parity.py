@@ -449,6 +449,24 @@ def test_leading_dimension_256_tiles(ld_extra, state):
     assert (Ub[:, W:] == 0).all() and (Wb[:, W:] == 0).all() and (Mb[:, W:] == 0).all()
 
 
+@pytest.mark.parametrize("coeffs", [C, Q], ids=["cubic", "quintic"])
+@pytest.mark.parametrize("K", [1, 2, 3])
+@pytest.mark.parametrize("prec", [hm.PREC_BF16X3, hm.PREC_BF16])
+def test_256_tiles_short_iterations(coeffs, K, prec):
+    """The 256-tile kernel passes part of each symmetric result to the next product
+    through LDS (rows 0..127 of A to the square; rows 0..63 of B to the update, from the
+    square or, with c = 0, from the Gram) and the rest through the workspace.  One to
+    three NS steps reach every hand-over, including the one into the last update, which
+    applies W.  O within the bar on matrices with 256-tiles beside ragged ones."""
+    if prec == hm.PREC_BF16 and coeffs == Q:
+        pytest.skip("plain bf16 operands with quintic coefficients are outside the bf16 bar")
+    mats = [power_law(512, 768, 1500), power_law(700, 300, 1501), power_law(256, 256, 1502)]
+    (res,), _ = gpu_step(mats, 256, K=K, coeffs=coeffs, prec=prec)
+    for (W, M, U) in res:
+        O = oracle.tiled_ns(M.double().numpy(), 256, K, coeffs)
+        assert_bar(U, O, prec, tight=5e-3 if prec == hm.PREC_BF16X3 else None)
+
+
 def test_plan_stats_and_empty_layer_on_gpu():
     _need_gpu()
     Wt = torch.zeros(0, 5, device=DEV)
