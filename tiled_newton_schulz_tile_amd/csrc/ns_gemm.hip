@@ -54,6 +54,18 @@ __device__ __forceinline__ TileG tile_of(const GemmTile *tiles, int i) {
                t->ldx,   t->lda,  t->nred, t->ws_x0, t->ws_x1, t->ws_a, t->ws_b, t->ws_red};
 }
 
+// Eight fp32 values as bf16 hi = RNE(v) and lo = RNE(v - hi), two elements per
+// conversion; v - hi is exact in fp32, and hi is read back from the packed pair (low
+// half: shift up, high half: mask) rather than converted again.
+__device__ __forceinline__ void split8(const float (&v)[8], u32x4 &hb, u32x4 &lb) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hb[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+    lb[q] = pack_bf16x2(v[2 * q] - __builtin_bit_cast(float, hb[q] << 16),
+                        v[2 * q + 1] - __builtin_bit_cast(float, hb[q] & 0xffff0000u));
+  }
+}
+
 // A matrix of `rows` rows and leading dimension ld in the workspace, in the
 // precision's plane format.
 template <int PREC>
@@ -131,18 +143,10 @@ struct Planes {
       d[0] = f32x4{v[0], v[1], v[2], v[3]};
       d[1] = f32x4{v[4], v[5], v[6], v[7]};
     } else {
-      unsigned short hb[8], lb[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        hb[q] = to_bf16_bits(v[q]);
-        lb[q] = to_bf16_bits(v[q] - bf16_bits_to_f32(hb[q]));
-      }
-      *reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(hi() + o)) =
-          u32x4{hb[0] | (unsigned)hb[1] << 16, hb[2] | (unsigned)hb[3] << 16, hb[4] | (unsigned)hb[5] << 16,
-                hb[6] | (unsigned)hb[7] << 16};
-      *reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(lo() + o)) =
-          u32x4{lb[0] | (unsigned)lb[1] << 16, lb[2] | (unsigned)lb[3] << 16, lb[4] | (unsigned)lb[5] << 16,
-                lb[6] | (unsigned)lb[7] << 16};
+      u32x4 hb, lb;
+      split8(v, hb, lb);
+      *reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(hi() + o)) = hb;
+      if constexpr (PREC == PREC_BF16X3 || PREC == PREC_BF16) *reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(lo() + o)) = lb;
     }
   }
   // store 16 consecutive values of row i starting at column j (j multiple of 16,
@@ -154,21 +158,15 @@ struct Planes {
 #pragma unroll
       for (int q = 0; q < 4; ++q) d[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
     } else {
-      unsigned short hb[16], lb[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        hb[q] = to_bf16_bits(v[q]);
-        lb[q] = to_bf16_bits(v[q] - bf16_bits_to_f32(hb[q]));
-      }
       GLOBAL_AS u32x4 *dh = reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(hi() + o));
       GLOBAL_AS u32x4 *dl = reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(lo() + o));
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        dh[q] = u32x4{hb[8 * q] | (unsigned)hb[8 * q + 1] << 16, hb[8 * q + 2] | (unsigned)hb[8 * q + 3] << 16,
-                      hb[8 * q + 4] | (unsigned)hb[8 * q + 5] << 16, hb[8 * q + 6] | (unsigned)hb[8 * q + 7] << 16};
-        if constexpr (PREC == PREC_BF16X3 || PREC == PREC_BF16)
-          dl[q] = u32x4{lb[8 * q] | (unsigned)lb[8 * q + 1] << 16, lb[8 * q + 2] | (unsigned)lb[8 * q + 3] << 16,
-                        lb[8 * q + 4] | (unsigned)lb[8 * q + 5] << 16, lb[8 * q + 6] | (unsigned)lb[8 * q + 7] << 16};
+        const float(&w)[8] = *reinterpret_cast<const float(*)[8]>(&v[8 * q]);
+        u32x4 hb, lb;
+        split8(w, hb, lb);
+        dh[q] = hb;
+        if constexpr (PREC == PREC_BF16X3 || PREC == PREC_BF16) dl[q] = lb;
       }
     }
   }
@@ -943,9 +941,10 @@ struct T2Lds {
   static constexpr int ROWT = T2 * RP * 2;                  // one plane of the row panel
   static constexpr int COLT = BK * CP * 2;                  // one plane of the column panel
   static constexpr int STAGE = NPL * (ROWT + (MODE == MODE_UPDATE ? COLT : 0));
-  // fp32 staging of one column half of D, row-major: rows 4 apart (the two lane halves
-  // of an accumulator) fall 32 banks apart, and a row's 16-column pieces are 16-byte reads
-  static constexpr int SP = T2 / 2 + 8;
+  // fp32 staging of one column half of D, row-major, pitch 4 mod 32 words: eight
+  // consecutive rows written at one column (16-byte pieces) and two rows of 8-column
+  // pieces read by eight lanes each fall on distinct banks
+  static constexpr int SP = T2 / 2 + 4;
   static constexpr int STG = T2 * SP * 4;
   static constexpr int BYTES = 2 * STAGE > STG ? 2 * STAGE : STG;
   static constexpr int NQ = T2 * (BK / 8) / T2_THREADS;     // 16-byte chunks per thread, plane, operand
@@ -1310,7 +1309,7 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
   }
 
   // ---- epilogue, one column half at a time: the half staged in LDS (fp32), then rows
-  // written with 16-element stores
+  // written as 8-element pieces, eight lanes to 128 contiguous bytes of a row
   float *st = reinterpret_cast<float *>(lds);
   const float a = gp.a, b = gp.b, c = gp.c;
   const bool fold = gp.fold != 0;
@@ -1322,10 +1321,31 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
   // the workspace, rows 0..63 into the update's first two stages.
   const bool hand_a = MODE == MODE_GRAM && c != 0.f;
   const bool hand_b = MODE == MODE_SQUARE || (MODE == MODE_GRAM && c == 0.f);
+  // The Gram and square results are symmetric, so column half h of D is row half h
+  // transposed: the waves holding rows 128 h.. stage their blocks at the transposed
+  // positions, a lane's four consecutive rows of one column as one 16-byte piece.  (The
+  // value staged for (i, j) is then the one accumulated at (j, i); the two differ only
+  // in the order the correction terms reached them.)  The update's result is staged
+  // at its own positions, by the waves holding columns 128 h.., one element at a time.
+  constexpr bool SYM = MODE != MODE_UPDATE;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     if (hand_a && h == 0) continue;   // (uniform)
-    if (wn == h) {
+    if constexpr (SYM) {
+      if ((wm >> 1) == h) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int jl = (wm & 1) * 64 + bi * 32 + 8 * g + 4 * half;   // row of D, less 128 h
+              const int i = wn * 128 + bj * 32 + li;                        // column of D
+              *reinterpret_cast<f32x4 *>(st + i * LD::SP + jl) =
+                  f32x4{acc[bi][bj][4 * g], acc[bi][bj][4 * g + 1], acc[bi][bj][4 * g + 2], acc[bi][bj][4 * g + 3]};
+            }
+      }
+    } else if (wn == h) {
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -1339,62 +1359,68 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
           }
     }
     __syncthreads();
+    // thread u takes row u / 8 and, in that row, the 8-element pieces at columns
+    // 8 (u % 8) and 8 (u % 8) + 64 of the half
 #pragma unroll
     for (int q4 = 0; q4 < T2 * (T2 / 2 / 16) / T2_THREADS; ++q4) {
       const int u = tid + q4 * T2_THREADS;
-      const int i = u >> 3, jl = (u & 7) * 16;   // row i, columns 128 h + jl .. +15
-      const int j = h * (T2 / 2) + jl;
-      float e[16];
-      if constexpr (MODE == MODE_UPDATE) {
-        if (!fold) Xc.get16(i, j, e);
-      }
-      float dv[16];
+      const int i = u >> 3;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(st + i * LD::SP + jl + 4 * m);
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) dv[4 * m + e2] = x[e2];
-      }
-      float v[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const float d = dv[q];
-        const bool dg = fold && i == j + q;
-        if constexpr (MODE == MODE_GRAM) {
-          v[q] = c != 0.f ? d : b * d + (dg ? a : 0.f);
-        } else if constexpr (MODE == MODE_SQUARE) {
-          v[q] = c * d + (dg ? a : 0.f);   // d = (b / c) A + A^2
-        } else {
-          v[q] = fold ? d : __builtin_fmaf(a, e[q], d);
+      for (int pc = 0; pc < 2; ++pc) {
+        const int jl = (u & 7) * 8 + 64 * pc;
+        const int j = h * (T2 / 2) + jl;
+        float e[8];
+        if constexpr (MODE == MODE_UPDATE) {
+          if (!fold) Xc.get8(i, j, e);
         }
-      }
-      if constexpr (APPLY) {
-        const LayerDesc *L = ap.layers + t.layer;
-        float *wrow = L->w + (int64_t)(t.row0 + i) * L->ld_w + t.col0 + j;
-        const float nlr = -ap.lr;
-        if (L->vec_w) {   // 16-byte aligned rows (the tile's columns start at a multiple of 256)
-          GLOBAL_AS f32x4 *pw = reinterpret_cast<GLOBAL_AS f32x4 *>(gmem(wrow));
-          f32x4 w4[4];
+        float dv[8];
 #pragma unroll
-          for (int m = 0; m < 4; ++m) w4[m] = pw[m];
+        for (int m = 0; m < 2; ++m) {
+          const f32x4 x = *reinterpret_cast<const f32x4 *>(st + i * LD::SP + jl + 4 * m);
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
+          for (int e2 = 0; e2 < 4; ++e2) dv[4 * m + e2] = x[e2];
+        }
+        float v[8];
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) w4[m][e2] = __builtin_fmaf(nlr, v[4 * m + e2], w4[m][e2]);
-            pw[m] = w4[m];
+        for (int q = 0; q < 8; ++q) {
+          const float d = dv[q];
+          const bool dg = fold && i == j + q;
+          if constexpr (MODE == MODE_GRAM) {
+            v[q] = c != 0.f ? d : b * d + (dg ? a : 0.f);
+          } else if constexpr (MODE == MODE_SQUARE) {
+            v[q] = c * d + (dg ? a : 0.f);   // d = (b / c) A + A^2
+          } else {
+            v[q] = fold ? d : __builtin_fmaf(a, e[q], d);
+          }
+        }
+        if constexpr (APPLY) {
+          const LayerDesc *L = ap.layers + t.layer;
+          float *wrow = L->w + (int64_t)(t.row0 + i) * L->ld_w + t.col0 + j;
+          const float nlr = -ap.lr;
+          if (L->vec_w) {   // 16-byte aligned rows (the tile's columns start at a multiple of 256)
+            GLOBAL_AS f32x4 *pw = reinterpret_cast<GLOBAL_AS f32x4 *>(gmem(wrow));
+            f32x4 w4[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) w4[m] = pw[m];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+#pragma unroll
+              for (int e2 = 0; e2 < 4; ++e2) w4[m][e2] = __builtin_fmaf(nlr, v[4 * m + e2], w4[m][e2]);
+              pw[m] = w4[m];
+            }
+          } else {
+            GLOBAL_AS float *pw = gmem(wrow);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) pw[q] = __builtin_fmaf(nlr, v[q], pw[q]);
+          }
+          if (ap.write_u) {
+            GLOBAL_AS float *pu = gmem(L->u + (int64_t)(t.row0 + i) * L->ld_u + t.col0 + j);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) pu[q] = v[q];
           }
         } else {
-          GLOBAL_AS float *pw = gmem(wrow);
-#pragma unroll
-          for (int q = 0; q < 16; ++q) pw[q] = __builtin_fmaf(nlr, v[q], pw[q]);
+          if (!(hand_b && j < 64)) O.put8(i, j, v);
         }
-        if (ap.write_u) {
-          GLOBAL_AS float *pu = gmem(L->u + (int64_t)(t.row0 + i) * L->ld_u + t.col0 + j);
-#pragma unroll
-          for (int q = 0; q < 16; ++q) pu[q] = v[q];
-        }
-      } else {
-        if (!(hand_b && j < 64)) O.put16(i, j, v);
       }
     }
     __syncthreads();   // the staging read before the next half lands
