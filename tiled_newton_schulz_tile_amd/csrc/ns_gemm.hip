@@ -1008,6 +1008,77 @@ __device__ __forceinline__ void t256_front(const TileG &t, char *ws, const T256A
   const int cc = (threadIdx.x & 31) * 8, rr = threadIdx.x >> 5;
   const bool vec = L->vec_ok;   // rows 16-byte aligned (the tile's columns start at a multiple of 256)
   const float beta = io.beta;
+  constexpr int NK = T2 / 16;   // row pieces per thread
+  if constexpr (sizeof(S) == 2) {
+    if (vec) {   // (uniform)
+      // bf16 state in aligned rows: every load is issued before the first store (M is
+      // updated in place, so a store to M would otherwise hold back the next piece's
+      // loads), and the stored codes stay in registers for the norm and X0.  Same
+      // arithmetic, in the same order, as the general path below.
+      auto f32_of = [](const u32x4 &w, int q) {
+        return __builtin_bit_cast(float, (q & 1) ? (w[q >> 1] & 0xffff0000u) : (w[q >> 1] << 16));
+      };
+      u32x4 mc[NK], gc[NK];
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const int64_t i = t.row0 + rr + 16 * k;
+        mc[k] = *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(mb + i * ldm + t.col0 + cc));
+        gc[k] = *reinterpret_cast<const GLOBAL_AS u32x4 *>(gmem(gb + i * ldg + t.col0 + cc));
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        unsigned short code[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) code[q] = to_bf16_bits(__builtin_fmaf(beta, f32_of(mc[k], q), f32_of(gc[k], q)));
+        mc[k] = u32x4{code[0] | (unsigned)code[1] << 16, code[2] | (unsigned)code[3] << 16,
+                      code[4] | (unsigned)code[5] << 16, code[6] | (unsigned)code[7] << 16};
+        *reinterpret_cast<GLOBAL_AS u32x4 *>(gmem(mb + (int64_t)(t.row0 + rr + 16 * k) * ldm + t.col0 + cc)) = mc[k];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float v = f32_of(mc[k], q);
+          ss = __builtin_fmaf(v, v, ss);
+        }
+      }
+      ss = t256_sum(ss, red8);
+      float s1 = 1.f, s2 = 1.f;
+      if (!(ss >= 0x1p-100f && ss <= 0x1p100f)) {   // uniform over the workgroup
+        float mx = 0.f;
+#pragma unroll
+        for (int k = 0; k < NK; ++k)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) mx = __builtin_fmaxf(mx, __builtin_fabsf(f32_of(mc[k], q)));
+        mx = t256_max(mx, red8);
+        if (mx > 0.f && mx <= 0x1.fffffep127f) {   // nonzero and finite
+          int ex;
+          (void)__builtin_frexpf(mx, &ex);
+          s1 = __builtin_ldexpf(1.f, (-ex) / 2);
+          s2 = __builtin_ldexpf(1.f, -ex - (-ex) / 2);
+          float s2s = 0.f;
+#pragma unroll
+          for (int k = 0; k < NK; ++k)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const float x = f32_of(mc[k], q) * s1 * s2;
+              s2s = __builtin_fmaf(x, x, s2s);
+            }
+          ss = t256_sum(s2s, red8);
+        }
+      }
+      const float den = __builtin_sqrtf(ss) + (io.eps * s1) * s2;
+      const float inv = den > 0.f ? (s1 / den) * s2 : (den == 0.f ? 0.f : den);
+      const Planes<PREC> X{ws + t.x0, t.r, t.ldx};
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = f32_of(mc[k], q) * inv;
+        X.put8(rr + 16 * k, cc, v);
+      }
+      __syncthreads();   // X0 complete before the first product reads it
+      return;
+    }
+  }
   float ss = 0.f;
   for (int k = 0; k < T2 / 16; ++k) {
     const int i = rr + 16 * k;
