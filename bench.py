@@ -36,16 +36,22 @@ METRIC = "HiMuon step ms & NS TFLOP/s (% MFMA peak) vs T, 8B-shaped stack"
 # HBM bytes of one launch of the T=128 fused kernel (bf16f8) on this workload, from two
 # rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), scaled by the
 # readings of a 1 GiB elementwise copy (x2.0 read, x1.0 write).  Valid only for the
-# kernel source it was measured on (sha256 prefix of ns_fused.hip); null otherwise.
-TRAFFIC_T128 = {"source_sha256_16": "520b407949a22600", "precision": "bf16f8", "fetch_kib": 27291209.4375,
-                "write_kib": 40894464.0, "fetch_scale": 2.0, "write_scale": 1.0}
+# kernel source it was measured on (sha256 prefix of ns_fused.hip followed by the two
+# headers it includes); null otherwise.
+TRAFFIC_T128 = {"source_sha256_16": "e77c109b05cdb98a", "precision": "bf16f8", "fetch_kib": 27291241.8125,
+                "write_kib": 40894464.125, "fetch_scale": 2.0, "write_scale": 1.0}
+
+
+KERNEL_SOURCES = ("ns_fused.hip", "himuon_internal.h", "device_common.h")
 
 
 def measured_traffic():
     import hashlib
-    src = os.path.join(ROOT, "tiled_newton_schulz_tile_amd", "csrc", "ns_fused.hip")
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tiled_newton_schulz_tile_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    sha = h.hexdigest()[:16]
     t = TRAFFIC_T128
     if not t["source_sha256_16"] or sha != t["source_sha256_16"]:
         return None

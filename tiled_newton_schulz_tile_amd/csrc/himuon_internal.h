@@ -84,10 +84,11 @@ struct F8Exps {
 
 // PREC_BF16F8 on full e x e tiles of the fused kernel: the Gram product of the first
 // kF8PlainGramSteps NS steps, and the square product of the first
-// f8_plain_square_steps(e) steps (with A stored as its bf16 plane alone), take the bf16
-// operands only.
+// f8_plain_square_steps(e, dense) steps (with A stored as its bf16 plane alone), take the
+// bf16 operands only.  (128-tiles outside the dense group, whose kernel instance has no
+// registers to spare for the plain square, keep the split square.)
 constexpr int kF8PlainGramSteps = 1;
-constexpr int f8_plain_square_steps(int edge) { return edge == 128 ? 0 : 2; }
+constexpr int f8_plain_square_steps(int edge, bool dense) { return edge == 128 && !dense ? 0 : 2; }
 
 struct NSParams {
   float a, b, c;

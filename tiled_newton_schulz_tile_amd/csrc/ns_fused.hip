@@ -1045,6 +1045,7 @@ struct TileRegs {
     const S *mb = reinterpret_cast<const S *>(L.m);
     const S *gb = reinterpret_cast<const S *>(L.g);
     if constexpr (DENSE) {
+      asm volatile("" : "+v"(gt));   // (formed per tile, as in the X0 stores)
       const int64_t r0 = t.row0 + gt / CPR;
       const int c = (gt % CPR) * 8;
       const S *gp = gb + r0 * L.ld_g + t.col0 + c;
@@ -1103,6 +1104,7 @@ struct TileRegs {
   __device__ __forceinline__ float momentum_dense(TileView t, const LayerView &L, int gt, float beta,
                                                   float (&v)[GM_IT][8]) const {
     S *mb = reinterpret_cast<S *>(L.m);
+    asm volatile("" : "+v"(gt));   // (formed per tile, as in the X0 stores)
     S *mp = mb + (int64_t)(t.row0 + gt / CPR) * L.ld_m + t.col0 + (gt % CPR) * 8;
     const int64_t sm = (int64_t)GM_ROWS * L.ld_m;
     float ss = 0.f;
@@ -1399,9 +1401,13 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     Acc<NI, NJ> xr;
     if constexpr (DIRECT) {
       constexpr int CPR = TS / 8;
+      // (the thread index is made opaque so that these LDS offsets are formed here for
+      // each tile rather than once per launch and held, or spilled, across the tile loop)
+      int gq = gt;
+      asm volatile("" : "+v"(gq));
 #pragma unroll
       for (int i = 0; i < TileRegs<TS, NT, S>::GM_IT; ++i) {
-        const int q = gt + i * NT;
+        const int q = gq + i * NT;
         const int r = q / CPR, c = (q % CPR) * 8;
         if constexpr (!NS) {
           // no iteration: the output is X0 itself, staged for the update in fp32
@@ -1488,9 +1494,10 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     // Gram matrix is spread over r directions, so these roundings cost no accuracy at
     // r = 64 or 128; once the singular values saturate (from step 2 on), and on thin
     // ragged tiles (few large singular values), every product takes the correction terms.
-    // (128-tiles keep the square product split: its plain variant costs registers that
-    // the 128-tile code does not have, and spilling them slows the whole tile loop)
-    constexpr int PLAIN_GRAM_STEPS = kF8PlainGramSteps, PLAIN_SQUARE_STEPS = f8_plain_square_steps(TS);
+    // (128-tiles outside the dense group keep the square product split: their instance
+    // has no registers to spare for the plain variant, and a spill there slows the
+    // whole tile loop)
+    constexpr int PLAIN_GRAM_STEPS = kF8PlainGramSteps, PLAIN_SQUARE_STEPS = f8_plain_square_steps(TS, DENSE);
     const bool full = DENSE || (t.h == TS && t.w == TS);         // wave-uniform
     auto sym_part = [&](int it) {
       const int ex = fs.x(), ea = fs.a(), eb = fs.b();
