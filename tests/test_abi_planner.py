@@ -140,6 +140,13 @@ def test_256_tile_chunks_and_work():
     assert st["tiles"] == st["gemm_tiles"] == 6979321856 // 256 ** 2
     assert st["ns_flops"] == 6 * 6979321856 * 256 * 5
     assert st["issued_flops"] == 3 * st["ns_flops"]
+    # bf16f8 requests run the same products, with the Gram of step 0 and the square of
+    # steps 0 and 1 on the hi operands alone (one bf16 product instead of three):
+    # (1 + 1 + 3) + (3 + 1 + 3) + 3 * (3 + 3 + 3) = 39 units of 2 * 256^3 per tile, not 45
+    p = plan_for(synth.STACKS["llama3-8b-32L"], 256, precision=hm.PREC_BF16F8)
+    st8 = hm.himuon_plan_stats(p)
+    hm.himuon_plan_destroy(p)
+    assert st8["issued_flops"] == 39 * 2 * 256 ** 3 * (6979321856 // 256 ** 2)
     # fp32 keeps the 128-block kernel: upper blocks of the symmetric products (3 of 4)
     p = plan_for(synth.STACKS["llama3-8b-32L"], 256, precision=hm.PREC_F32)
     st = hm.himuon_plan_stats(p)

@@ -130,7 +130,7 @@ def structured_tiles(T, seed):
     return torch.cat([rank1, rank4, orth, decay], dim=1).float()
 
 
-@pytest.mark.parametrize("T", [64, 128])
+@pytest.mark.parametrize("T", [64, 128, 256])
 @pytest.mark.parametrize("coeffs", [Q, C])
 def test_structured_spectra(T, coeffs):
     # Full tiles whose singular values are large from the start (rank 1, rank 4,
@@ -138,7 +138,8 @@ def test_structured_spectra(T, coeffs):
     # of a low-rank tile by about a = 3.4 per step, so there the error is set by how
     # precisely the a X term is formed: both split schemes form it from X held to about
     # 2^-17 (bf16x3 through its hi + lo operands, bf16f8 in fp32 beside the product), and
-    # both must stay inside the bf16 bar on every tile kind.
+    # both must stay inside the bf16 bar on every tile kind.  (At T = 256 bf16f8 runs the
+    # bf16x3 products with the plain early symmetric products of the 256-tile kernel.)
     G = structured_tiles(T, 500 + T)
     for prec in (hm.PREC_BF16X3, hm.PREC_BF16F8):
         (res,), _ = gpu_step([G], T, K=5, coeffs=coeffs, prec=prec)

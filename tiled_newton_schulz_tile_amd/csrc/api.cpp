@@ -242,6 +242,10 @@ himuon_status himuon_step(himuon_plan_t *p, void *workspace, size_t ws_bytes, fl
   prm.steps = prm.identity ? 0 : c.steps;
   prm.write_update = (c.flags & HIMUON_FLAG_WRITE_UPDATE) ? 1 : 0;
   prm.f8 = pl.f8;
+  if (c.precision == HIMUON_PREC_BF16F8) {
+    prm.plain_gram = himuon::kF8PlainGramSteps;
+    prm.plain_square = himuon::f8_plain_square_steps(256, true);
+  }
   // the e4m3 correction products exist for fused tiles of edge 64 and 128 only
   const int gemm_prec = c.precision == HIMUON_PREC_BF16F8 ? (int)HIMUON_PREC_BF16X3 : (int)c.precision;
   const auto *dl = reinterpret_cast<const himuon::LayerDesc *>(tb.d);

@@ -97,6 +97,10 @@ struct NSParams {
   int32_t write_update;
   int32_t identity;  // gather -> scatter only: no normalisation (steps is 0 then)
   F8Exps f8;
+  // PREC_BF16F8 requests on 256-tiles (run with the bf16x3 products): the Gram product of
+  // the first plain_gram NS steps and the square product of the first plain_square take
+  // the bf16 hi operands only, as on full fused tiles; 0 for every other request
+  int32_t plain_gram, plain_square;
 };
 
 // Fills e with the fp8 plane exponents for coefficients (a, b, c) over `steps` steps;

@@ -41,6 +41,7 @@ struct GemmParams {
   float a, b, c;
   int xsel;      // X buffer read this step (0: ws_x0, 1: ws_x1); the other is written
   int fold;      // a added to B's diagonal (fp32, bf16x3); plain bf16 adds a X in fp32
+  int plain_gram, plain_square;   // 256-tiles: early steps whose Gram / square take hi only
 };
 
 // Scalar copies of one GemmTile (read word by word so nothing lands in private memory).
@@ -1206,11 +1207,17 @@ __device__ __forceinline__ void t256_hand_over(const f32x16 (&acc)[2][4], char *
   __syncthreads();   // the stages are complete before the next product reads them
 }
 
+// plain (bf16x3 planes, the symmetric products of early steps; uniform): the product of
+// the hi operands alone, one bf16 product instead of three, with only the hi planes
+// loaded.
 template <int PREC, int MODE, bool APPLY = false>
 __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const GemmParams &gp, char *lds,
-                                             f32x16 (&acc)[2][4], const T256Apply &ap = T256Apply{}) {
+                                             f32x16 (&acc)[2][4], const T256Apply &ap = T256Apply{},
+                                             bool plain = false) {
   static_assert(PREC == PREC_BF16 || PREC == PREC_BF16X3, "bf16 planes");
   using LD = T2Lds<PREC, MODE>;
+  constexpr bool SPLIT = PREC == PREC_BF16X3;
+  const bool lo_in = SPLIT && !(MODE != MODE_UPDATE && plain);   // (uniform) lo planes loaded and multiplied
   // (the thread index is made opaque so that the addresses derived from it are formed
   // inside each product rather than hoisted out of the NS loop for all three at once)
   int tid = threadIdx.x;
@@ -1231,6 +1238,7 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
   auto load = [&](int kb) {
 #pragma unroll
     for (int pl = 0; pl < LD::NPL; ++pl) {
+      if (pl == 1 && !lo_in) break;
       const __bf16 *lb = pl ? Lp.lo() : Lp.hi();
       const __bf16 *xb = pl ? Xc.lo() : Xc.hi();
 #pragma unroll
@@ -1248,6 +1256,7 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
   auto store = [&](char *stage) {
 #pragma unroll
     for (int pl = 0; pl < LD::NPL; ++pl) {
+      if (pl == 1 && !lo_in) break;
 #pragma unroll
       for (int q = 0; q < LD::NQ; ++q) {
         const int idx = tid + q * T2_THREADS;
@@ -1280,21 +1289,21 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         lh[b] = *reinterpret_cast<const bf16x8 *>(L0 + (wm * 64 + b * 32 + li) * LD::RP + k);
-        if constexpr (PREC == PREC_BF16X3)
+        if constexpr (SPLIT)
           ll[b] = *reinterpret_cast<const bf16x8 *>(L1 + (wm * 64 + b * 32 + li) * LD::RP + k);
       }
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if constexpr (MODE == MODE_UPDATE) {
           rh[b] = tr_frag(C0, LD::CP, k, wn * 128 + b * 32, lane);
-          if constexpr (PREC == PREC_BF16X3) rl[b] = tr_frag(C1, LD::CP, k, wn * 128 + b * 32, lane);
+          if constexpr (SPLIT) rl[b] = tr_frag(C1, LD::CP, k, wn * 128 + b * 32, lane);
         } else {
           rh[b] = *reinterpret_cast<const bf16x8 *>(L0 + (wn * 128 + b * 32 + li) * LD::RP + k);
-          if constexpr (PREC == PREC_BF16X3)
+          if constexpr (SPLIT)
             rl[b] = *reinterpret_cast<const bf16x8 *>(L1 + (wn * 128 + b * 32 + li) * LD::RP + k);
         }
       }
-      if constexpr (PREC == PREC_BF16X3) {
+      if (SPLIT && lo_in) {
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -1544,8 +1553,8 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_t256_ns_kernel(const GemmTile
   for (int it = 0; it < steps; ++it) {
     // (each product ends at a barrier after its last global stores, so the next one's
     // loads see them: one workgroup, one CU, one L1)
-    t256_product<PREC, MODE_GRAM>(t, ws, gp, lds, acc);
-    if (gp.c != 0.f) t256_product<PREC, MODE_SQUARE>(t, ws, gp, lds, acc);
+    t256_product<PREC, MODE_GRAM>(t, ws, gp, lds, acc, T256Apply{}, it < gp.plain_gram);
+    if (gp.c != 0.f) t256_product<PREC, MODE_SQUARE>(t, ws, gp, lds, acc, T256Apply{}, it < gp.plain_square);
     if (it + 1 < steps) {
       t256_product<PREC, MODE_UPDATE>(t, ws, gp, lds, acc);
     } else {   // the last update applies O to W instead of storing X_K
@@ -1825,7 +1834,7 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
   if (c.n_mom && !front) hipLaunchKernelGGL(gemm_momentum_kernel<S>, grid(c.n_mom), dim3(THREADS), 0, stream, layers, tiles, c.mom, ws, p.beta);
   if (c.tile_n && !front) hipLaunchKernelGGL(gemm_norm_kernel<S>, grid(c.tile_n), dim3(THREADS), 0, stream, layers, tiles, (int)c.tile_first, ws, p.eps, p.identity);
   if (c.n_stg && !front) hipLaunchKernelGGL((gemm_stage_kernel<S, PREC>), grid(c.n_stg), dim3(THREADS), 0, stream, layers, tiles, c.stg, ws);
-  GemmParams gp{p.a, p.b, p.c, 0, PREC != PREC_BF16};
+  GemmParams gp{p.a, p.b, p.c, 0, PREC != PREC_BF16, p.plain_gram, p.plain_square};
   auto products = [&](auto bkc) {
     constexpr int BK = decltype(bkc)::value;
     for (int it = 0; it < p.steps; ++it) {

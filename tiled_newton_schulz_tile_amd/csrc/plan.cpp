@@ -313,9 +313,13 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
           max_ws = std::max(max_ws, tile_workspace(g, prec));
           const int kind = gemm_kind(g, prec);
           if (kind == 1) {
-            // one workgroup per tile and product, every 256 x 256 block computed
+            // one workgroup per tile and product, every 256 x 256 block computed; bf16f8
+            // requests run the bf16x3 products with the plain early symmetric products
             const double e3 = 2.0 * 256.0 * 256.0 * 256.0;
-            issued += (double)K * split * (e3 + (quintic ? e3 : 0.0) + e3);
+            const bool f8 = prec == HIMUON_PREC_BF16F8;
+            const int pg = f8 ? kF8PlainGramSteps : 0, ps = f8 ? f8_plain_square_steps(256, true) : 0;
+            for (int k = 0; k < K; ++k)
+              issued += e3 * ((k < pg ? 1.0 : split) + (quintic ? (k < ps ? 1.0 : split) : 0.0) + split);
           } else if (kind == 2) {
             // 256-blocks: symmetric products on the upper blocks only; the update over all
             const double nb = (double)(r / 256), nbs = (double)(s / 256);
