@@ -1289,7 +1289,7 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         lh[b] = *reinterpret_cast<const bf16x8 *>(L0 + (wm * 64 + b * 32 + li) * LD::RP + k);
-        if constexpr (SPLIT)
+        if (SPLIT && lo_in)
           ll[b] = *reinterpret_cast<const bf16x8 *>(L1 + (wm * 64 + b * 32 + li) * LD::RP + k);
       }
 #pragma unroll
@@ -1299,7 +1299,7 @@ __device__ __forceinline__ void t256_product(const TileG &t, char *ws, const Gem
           if constexpr (SPLIT) rl[b] = tr_frag(C1, LD::CP, k, wn * 128 + b * 32, lane);
         } else {
           rh[b] = *reinterpret_cast<const bf16x8 *>(L0 + (wn * 128 + b * 32 + li) * LD::RP + k);
-          if constexpr (SPLIT)
+          if (SPLIT && lo_in)
             rl[b] = *reinterpret_cast<const bf16x8 *>(L1 + (wn * 128 + b * 32 + li) * LD::RP + k);
         }
       }
