@@ -179,6 +179,18 @@ def test_256_block_issued_work_at_full():
     hm.himuon_plan_destroy(p)
     assert st["gemm_tiles"] == len(shapes)
     assert st["issued_flops"] == pytest.approx(want, rel=1e-12)
+    # bf16f8 requests run the same products with the Gram of step 0 and the square of
+    # steps 0 and 1 on the hi planes alone (one product each instead of three)
+    want8 = 0.0
+    for H, W in shapes:
+        r, s_ = min(H, W), max(H, W)
+        nb, nbs = r // 256, s_ // 256
+        sym = nb * (nb + 1) / 2 * 2.0 * 256 * 256
+        want8 += (1 + 4 * 3) * sym * s_ + (2 * 1 + 3 * 3) * sym * r + 5 * 3 * 2.0 * 256 * 256 * nb * nbs * r
+    p = plan_for(shapes, 0, precision=hm.PREC_BF16F8)
+    st8 = hm.himuon_plan_stats(p)
+    hm.himuon_plan_destroy(p)
+    assert st8["issued_flops"] == pytest.approx(want8, rel=1e-12)
     # a side that is not a multiple of 256 keeps the 128-blocks
     p = plan_for([(4096, 4000)], 0, precision=hm.PREC_BF16X3)
     st = hm.himuon_plan_stats(p)

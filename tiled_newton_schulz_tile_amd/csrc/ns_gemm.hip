@@ -1588,11 +1588,16 @@ struct B2Lds {
   static_assert(BYTES <= 160 * 1024, "LDS");
 };
 
-template <int PREC, int MODE, bool SAME>
+// PLAIN (bf16x3 symmetric products only): the product of the hi planes alone, the lo
+// operand planes neither loaded nor read; the result is still stored as both planes.
+template <int PREC, int MODE, bool SAME, bool PLAIN>
 __device__ __forceinline__ void b256_block(const TileG &t, int i0, int j0, char *ws, const GemmParams &gp,
                                            char *lds) {
   using LD = B2Lds<PREC, MODE>;
   constexpr int BK = LD::BK;
+  static_assert(!PLAIN || (PREC == PREC_BF16X3 && MODE != MODE_UPDATE), "plain symmetric bf16x3 products");
+  constexpr int NLD = PLAIN ? 1 : LD::NPL;     // operand planes loaded and staged
+  constexpr bool SPLIT = PREC == PREC_BF16X3 && !PLAIN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;   // rows 64 wm.., columns 128 wn.. of the block
   const int li = lane & 31, half = lane >> 5;
@@ -1607,7 +1612,7 @@ __device__ __forceinline__ void b256_block(const TileG &t, int i0, int j0, char 
   u32x4 rl_[LD::NPL * LD::NQ], rr_[LD::NPL * LD::NQ];
   auto load = [&](int kb) {
 #pragma unroll
-    for (int pl = 0; pl < LD::NPL; ++pl) {
+    for (int pl = 0; pl < NLD; ++pl) {
       const __bf16 *lb = pl ? Lp.lo() : Lp.hi();
       const __bf16 *xb = pl ? Xc.lo() : Xc.hi();
 #pragma unroll
@@ -1629,7 +1634,7 @@ __device__ __forceinline__ void b256_block(const TileG &t, int i0, int j0, char 
   };
   auto store = [&](char *stage) {
 #pragma unroll
-    for (int pl = 0; pl < LD::NPL; ++pl) {
+    for (int pl = 0; pl < NLD; ++pl) {
 #pragma unroll
       for (int q = 0; q < LD::NQ; ++q) {
         const int idx = tid + q * T2_THREADS;
@@ -1664,21 +1669,21 @@ __device__ __forceinline__ void b256_block(const TileG &t, int i0, int j0, char 
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         lh[b] = *reinterpret_cast<const bf16x8 *>(L0 + (wm * 64 + b * 32 + li) * LD::RP + k);
-        if constexpr (PREC == PREC_BF16X3)
+        if constexpr (SPLIT)
           ll[b] = *reinterpret_cast<const bf16x8 *>(L1 + (wm * 64 + b * 32 + li) * LD::RP + k);
       }
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if constexpr (MODE == MODE_UPDATE) {
           rh[b] = tr_frag(R0, LD::CP, k, wn * 128 + b * 32, lane);
-          if constexpr (PREC == PREC_BF16X3) rl[b] = tr_frag(R1, LD::CP, k, wn * 128 + b * 32, lane);
+          if constexpr (SPLIT) rl[b] = tr_frag(R1, LD::CP, k, wn * 128 + b * 32, lane);
         } else {
           rh[b] = *reinterpret_cast<const bf16x8 *>(R0 + (wn * 128 + b * 32 + li) * LD::RP + k);
-          if constexpr (PREC == PREC_BF16X3)
+          if constexpr (SPLIT)
             rl[b] = *reinterpret_cast<const bf16x8 *>(R1 + (wn * 128 + b * 32 + li) * LD::RP + k);
         }
       }
-      if constexpr (PREC == PREC_BF16X3) {
+      if constexpr (SPLIT) {
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -1803,7 +1808,7 @@ __device__ __forceinline__ void b256_block(const TileG &t, int i0, int j0, char 
   }
 }
 
-template <int PREC, int MODE>
+template <int PREC, int MODE, bool PLAIN = false>
 __global__ __launch_bounds__(T2_THREADS) void gemm_b256_kernel(const GemmTile *__restrict__ tiles,
                                                                const GemmWork *__restrict__ work, char *ws,
                                                                GemmParams gp) {
@@ -1814,9 +1819,9 @@ __global__ __launch_bounds__(T2_THREADS) void gemm_b256_kernel(const GemmTile *_
   // sides of every tile of the chunk are multiples of 256 (the planner's chunk kind), so
   // ldx = s, lda = r and no block reaches past them
   if (MODE != MODE_UPDATE && wk.bi == wk.bj) {   // uniform over the workgroup
-    b256_block<PREC, MODE, true>(t, wk.bi * T2, wk.bj * T2, ws, gp, lds);
+    b256_block<PREC, MODE, true, PLAIN>(t, wk.bi * T2, wk.bj * T2, ws, gp, lds);
   } else {
-    b256_block<PREC, MODE, false>(t, wk.bi * T2, wk.bj * T2, ws, gp, lds);
+    b256_block<PREC, MODE, false, PLAIN>(t, wk.bi * T2, wk.bj * T2, ws, gp, lds);
   }
 }
 
@@ -1856,8 +1861,19 @@ hipError_t run_chunk(const LayerDesc *layers, const GemmTile *tiles, const GemmC
       for (int it = 0; it < p.steps; ++it) {
         gp.xsel = it & 1;
         const dim3 bl(T2_THREADS);
-        hipLaunchKernelGGL((gemm_b256_kernel<PREC, MODE_GRAM>), grid(c.n_sym), bl, 0, stream, tiles, c.sym, ws, gp);
-        if (p.c != 0.f)
+        // bf16f8 requests (run with the bf16x3 products): the early symmetric products on
+        // the hi planes alone, as on 256-tiles
+        const bool plain_g = PREC == PREC_BF16X3 && it < p.plain_gram;
+        const bool plain_s = PREC == PREC_BF16X3 && it < p.plain_square;
+        if (plain_g)
+          hipLaunchKernelGGL((gemm_b256_kernel<PREC, MODE_GRAM, PREC == PREC_BF16X3>), grid(c.n_sym), bl, 0, stream,
+                             tiles, c.sym, ws, gp);
+        else
+          hipLaunchKernelGGL((gemm_b256_kernel<PREC, MODE_GRAM>), grid(c.n_sym), bl, 0, stream, tiles, c.sym, ws, gp);
+        if (p.c != 0.f && plain_s)
+          hipLaunchKernelGGL((gemm_b256_kernel<PREC, MODE_SQUARE, PREC == PREC_BF16X3>), grid(c.n_sym), bl, 0, stream,
+                             tiles, c.sym, ws, gp);
+        else if (p.c != 0.f)
           hipLaunchKernelGGL((gemm_b256_kernel<PREC, MODE_SQUARE>), grid(c.n_sym), bl, 0, stream, tiles, c.sym, ws, gp);
         hipLaunchKernelGGL((gemm_b256_kernel<PREC, MODE_UPDATE>), grid(c.n_upd), bl, 0, stream, tiles, c.upd, ws, gp);
       }

@@ -321,11 +321,15 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
             for (int k = 0; k < K; ++k)
               issued += e3 * ((k < pg ? 1.0 : split) + (quintic ? (k < ps ? 1.0 : split) : 0.0) + split);
           } else if (kind == 2) {
-            // 256-blocks: symmetric products on the upper blocks only; the update over all
+            // 256-blocks: symmetric products on the upper blocks only; the update over all;
+            // bf16f8 requests: the same plain early symmetric products as 256-tiles
             const double nb = (double)(r / 256), nbs = (double)(s / 256);
             const double sym = nb * (nb + 1) / 2 * 2.0 * 256 * 256;
-            issued += (double)K * split * (sym * z.ldx + (quintic ? sym * z.lda : 0.0) +
-                                           2.0 * 256 * 256 * nb * nbs * z.lda);
+            const bool f8 = prec == HIMUON_PREC_BF16F8;
+            const int pg = f8 ? kF8PlainGramSteps : 0, ps = f8 ? f8_plain_square_steps(256, true) : 0;
+            for (int k = 0; k < K; ++k)
+              issued += (k < pg ? 1.0 : split) * sym * z.ldx + (quintic ? (k < ps ? 1.0 : split) * sym * z.lda : 0.0) +
+                        split * 2.0 * 256 * 256 * nb * nbs * z.lda;
           } else {
             // 128-blocks as launched: symmetric products on the upper blocks only, K
             // padded to 64; the update over all blocks
