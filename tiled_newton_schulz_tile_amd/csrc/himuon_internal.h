@@ -86,9 +86,15 @@ struct F8Exps {
 // kF8PlainGramSteps NS steps, and the square product of the first
 // f8_plain_square_steps(e, dense) steps (with A stored as its bf16 plane alone), take the
 // bf16 operands only.  (128-tiles outside the dense group, whose kernel instance has no
-// registers to spare for the plain square, keep the split square.)
+// registers to spare for the plain square, keep the split square.)  On dense 128-tiles
+// the update product B X of the first f8_plain_update_steps(e, dense) steps takes them
+// too, except in the last step (B stored as its bf16 plane alone; the a X term stays in
+// fp32), and X_0, which then no product reads in split form, is stored without its e4m3
+// planes.  (Other 128-tiles lack the registers; on 64-tiles the plain update raised the
+// error of quintic runs with K = 8 on ragged stacks above 5e-3 max-abs.)
 constexpr int kF8PlainGramSteps = 1;
 constexpr int f8_plain_square_steps(int edge, bool dense) { return edge == 128 && !dense ? 0 : 2; }
+constexpr int f8_plain_update_steps(int edge, bool dense) { return edge == 128 && dense ? 1 : 0; }
 
 struct NSParams {
   float a, b, c;

@@ -1435,11 +1435,15 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
             rv[e + 1] = __builtin_fmaf(vd[i][e + 1], inv, -__builtin_bit_cast(float, hi[e / 2] & 0xffff0000u));
           }
           *reinterpret_cast<u32x4 *>(X.hi + G::bidx(r, c)) = hi;
-          const int o8 = G::b8idx(r, c);
-          *reinterpret_cast<u32x2 *>(X.h8 + o8) = u32x2{pack_fp8x4(xv[0], xv[1], xv[2], xv[3], f8.h),
-                                                        pack_fp8x4(xv[4], xv[5], xv[6], xv[7], f8.h)};
-          *reinterpret_cast<u32x2 *>(X.l8 + o8) = u32x2{pack_fp8x4(rv[0], rv[1], rv[2], rv[3], f8.l),
-                                                        pack_fp8x4(rv[4], rv[5], rv[6], rv[7], f8.l)};
+          // (dense tiles are full: with the Gram and the update of step 0 plain, nothing
+          // reads X_0's e4m3 planes)
+          if constexpr (kF8PlainGramSteps < 1 || f8_plain_update_steps(TS, DENSE) < 1) {
+            const int o8 = G::b8idx(r, c);
+            *reinterpret_cast<u32x2 *>(X.h8 + o8) = u32x2{pack_fp8x4(xv[0], xv[1], xv[2], xv[3], f8.h),
+                                                          pack_fp8x4(xv[4], xv[5], xv[6], xv[7], f8.h)};
+            *reinterpret_cast<u32x2 *>(X.l8 + o8) = u32x2{pack_fp8x4(rv[0], rv[1], rv[2], rv[3], f8.l),
+                                                          pack_fp8x4(rv[4], rv[5], rv[6], rv[7], f8.l)};
+          }
           if constexpr (G::XLO > 0)
             *reinterpret_cast<u32x4 *>(xlo + G::bidx(r, c)) =
                 u32x4{pack_bf16x2(rv[0], rv[1]), pack_bf16x2(rv[2], rv[3]), pack_bf16x2(rv[4], rv[5]),
@@ -1463,8 +1467,16 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
       if constexpr (NS) {
         load_acc_t<TS, PREC>(xr, st, p0, q0, lane, inv);
         tile_sync<G::WPT>();
-        store_acc_t<TS, PREC, false, false, NI, false, (G::XLO > 0)>(xr, X, p0, q0, lane, 1.f, 1.f, f8s_of(fx0),
-                                                                      xlo);
+        constexpr bool PLAIN_X0 = PREC == PREC_BF16F8 && G::XLO == 0 && kF8PlainGramSteps >= 1 &&
+                                  f8_plain_update_steps(TS, DENSE) >= 1;
+        bool plain_x0 = false;
+        if constexpr (PLAIN_X0) {
+          plain_x0 = DENSE || (t.h == TS && t.w == TS);   // (wave-uniform) step 0 reads hi alone
+          if (plain_x0) store_acc_t<TS, PREC_BF16>(xr, Mat<PREC_BF16>{X.hi}, p0, q0, lane);
+        }
+        if (!plain_x0)
+          store_acc_t<TS, PREC, false, false, NI, false, (G::XLO > 0)>(xr, X, p0, q0, lane, 1.f, 1.f,
+                                                                        f8s_of(fx0), xlo);
         tile_sync<G::WPT>();
       }
     }
@@ -1498,11 +1510,14 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     // has no registers to spare for the plain variant, and a spill there slows the
     // whole tile loop)
     constexpr int PLAIN_GRAM_STEPS = kF8PlainGramSteps, PLAIN_SQUARE_STEPS = f8_plain_square_steps(TS, DENSE);
+    constexpr int PLAIN_UPDATE_STEPS = f8_plain_update_steps(TS, DENSE);
     const bool full = DENSE || (t.h == TS && t.w == TS);         // wave-uniform
     auto sym_part = [&](int it) {
       const int ex = fs.x(), ea = fs.a(), eb = fs.b();
       const bool pg = F8 && full && it < PLAIN_GRAM_STEPS;      // wave-uniform
       const bool pa = F8 && full && it < PLAIN_SQUARE_STEPS && cc != 0.f;
+      // B stored as its hi plane alone (the last step keeps the split update)
+      const bool pu = F8 && full && it < PLAIN_UPDATE_STEPS && it + 1 < prm.steps;
       Acc<NI, NJ> acc;
       with_job<TS>(jb, [&](auto NBC, auto ALC) {
         constexpr int NB = decltype(NBC)::value;
@@ -1514,7 +1529,9 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
           } else {
             wave_gemm<TS, PREC, false, true, NB, AL>(acc, X, jb.p0, X, jb.q0, lane, 127 - (2 * ex + 8));
           }
-          if (cc == 0.f) {
+          if (cc == 0.f && pu) {
+            store_acc_t<TS, PREC_BF16, true, false, NB, true>(acc, ABh, jb.p0, jb.q0, lane, cb);   // B = b A
+          } else if (cc == 0.f) {
             store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cb, 1.f, f8s_of(eb));   // B = b A
           } else if (pa) {
             store_acc_t<TS, PREC_BF16, false, true, NB, true>(acc, ABh, jb.p0, jb.q0, lane, 1.f, cb / cc);
@@ -1552,7 +1569,11 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
         with_job<TS>(jb, [&](auto NBC, auto) {
           constexpr int NB = decltype(NBC)::value;
           if constexpr (F8) {
-            store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cc, 1.f, f8s_of(eb));   // B
+            if (pu) {
+              store_acc_t<TS, PREC_BF16, true, false, NB, true>(acc, Mat<PREC_BF16>{AB.hi}, jb.p0, jb.q0, lane, cc);
+            } else {
+              store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cc, 1.f, f8s_of(eb));   // B
+            }
           } else {
             store_acc_t<TS, PREC, true, false, NB, true>(acc, AB, jb.p0, jb.q0, lane, cc);   // B
             if constexpr (FOLD_A) add_diag<TS, PREC, NB>(AB, jb.p0, jb.q0, lane, ca);       // B + a I
@@ -1594,7 +1615,17 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
           }
           break;
         }
-        wave_gemm<TS, PREC, true, !XREG>(xr, X, p0, AB, q0, lane, sxb);     // X^T <- a X^T + X^T B
+        // X^T <- a X^T + X^T B; in the first steps of a full tile on the hi planes alone
+        if (PLAIN_UPDATE_STEPS > 0 && full && it < PLAIN_UPDATE_STEPS) {
+          // (an opaque lane index, so that this product's LDS addresses are formed here
+          // rather than hoisted out of the loop and held across it)
+          int ln = lane;
+          asm volatile("" : "+v"(ln));
+          wave_gemm_std<TS, PREC_BF16, true, !XREG, NI, false>(xr, Mat<PREC_BF16>{X.hi}, p0,
+                                                               Mat<PREC_BF16>{AB.hi}, q0, ln);
+        } else {
+          wave_gemm<TS, PREC, true, !XREG>(xr, X, p0, AB, q0, lane, sxb);
+        }
         if constexpr (!XREG) {
           XPiece<TS> xp;
           xp.load(X.hi, xlo, p0, q0, lane);

@@ -282,13 +282,15 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
             // the symmetric products (X X^T, A^2) run on the (nb + 1) / (2 nb) share of
             // 32x32 blocks on and above the diagonal; the update on all blocks.  bf16f8
             // issues two bf16-product units per product, one for the plain products of
-            // the first steps on full tiles.
+            // the first steps on full tiles (Gram, square and update).
             const double nb = e / 32.0, f = (nb + 1.0) / (2.0 * nb);
             if (prec == HIMUON_PREC_BF16F8 && e >= 64) {
               const bool full = h == e && w == e;
               const int pg = full ? kF8PlainGramSteps : 0, ps = full ? f8_plain_square_steps(e, dense) : 0;
+              const int pu = full ? f8_plain_update_steps(e, dense) : 0;   // never the last step
               for (int k = 0; k < K; ++k) {
-                const double units = f * (k < pg ? 1.0 : 2.0) + (quintic ? f * (k < ps ? 1.0 : 2.0) : 0.0) + 2.0;
+                const double units = f * (k < pg ? 1.0 : 2.0) + (quintic ? f * (k < ps ? 1.0 : 2.0) : 0.0) +
+                                     (k < pu && k + 1 < K ? 1.0 : 2.0);
                 issued += 2.0 * e * e * e * units;
               }
             } else {
