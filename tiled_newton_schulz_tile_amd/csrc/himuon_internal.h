@@ -94,7 +94,7 @@ struct F8Exps {
 // error of quintic runs with K = 8 on ragged stacks above 5e-3 max-abs.)
 constexpr int kF8PlainGramSteps = 1;
 constexpr int f8_plain_square_steps(int edge, bool dense) { return edge == 128 && !dense ? 0 : 2; }
-constexpr int f8_plain_update_steps(int edge, bool dense) { return edge == 128 && dense ? 1 : 0; }
+constexpr int f8_plain_update_steps(int edge, bool dense) { return edge == 128 && dense ? 2 : 0; }
 
 struct NSParams {
   float a, b, c;
