@@ -70,10 +70,14 @@ typedef enum {
                              MFMA time; each fp8 operand carries a power-of-two scale
                              chosen at plan time from bounds on the iterates.  Fused tiles
                              of edge 64 and 128 run it; smaller tiles and the large-tile
-                             path run HIMUON_PREC_BF16X3.  On tiles that fill 64 x 64 or
-                             128 x 128, the Gram product of NS step 0 (and at edge 64 the
-                             square product of steps 0 and 1) uses the bf16 hi operands
-                             alone.  The a X term of each step is added in fp32 from X
+                             path run HIMUON_PREC_BF16X3 (256-tiles and 256-blocks with
+                             the plain early Gram and square below).  On tiles that fill
+                             64 x 64 or 128 x 128, the Gram product of NS step 0 and the
+                             square product of steps 0 and 1 use the bf16 hi operands
+                             alone, and on dense 128-tiles (full, 16-byte aligned rows)
+                             so does the B X product of steps 0 and 1 (never of the last
+                             step); other 128-tiles keep the split square and update.
+                             The a X term of each step is added in fp32 from X
                              held to about 2^-17 (bf16 hi + lo, or fp32), not through the
                              e4m3 operands, so rounding noise does not build up in the
                              empty directions of low-rank tiles.  himuon_plan returns
