@@ -91,9 +91,12 @@ struct F8Exps {
 // too, except in the last step (B stored as its bf16 plane alone; the a X term stays in
 // fp32), and X_0, which then no product reads in split form, is stored without its e4m3
 // planes.  (Other 128-tiles lack the registers; on 64-tiles the plain update raised the
-// error of quintic runs with K = 8 on ragged stacks above 5e-3 max-abs.)
+// error of quintic runs with K = 8 on ragged stacks above 5e-3 max-abs.)  Dense 128-tiles
+// run the Gram product of the first f8_plain_gram_steps(e, dense) steps plain, and an X
+// whose next Gram and update are both plain is stored as bf16 hi + lo alone.
 constexpr int kF8PlainGramSteps = 1;
 constexpr int f8_plain_square_steps(int edge, bool dense) { return edge == 128 && !dense ? 0 : 2; }
+constexpr int f8_plain_gram_steps(int edge, bool dense) { return edge == 128 && dense ? 2 : kF8PlainGramSteps; }
 constexpr int f8_plain_update_steps(int edge, bool dense) { return edge == 128 && dense ? 2 : 0; }
 
 struct NSParams {

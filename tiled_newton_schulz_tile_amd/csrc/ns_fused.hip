@@ -1509,7 +1509,7 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
     // (128-tiles outside the dense group keep the square product split: their instance
     // has no registers to spare for the plain variant, and a spill there slows the
     // whole tile loop)
-    constexpr int PLAIN_GRAM_STEPS = kF8PlainGramSteps, PLAIN_SQUARE_STEPS = f8_plain_square_steps(TS, DENSE);
+    constexpr int PLAIN_GRAM_STEPS = f8_plain_gram_steps(TS, DENSE), PLAIN_SQUARE_STEPS = f8_plain_square_steps(TS, DENSE);
     constexpr int PLAIN_UPDATE_STEPS = f8_plain_update_steps(TS, DENSE);
     const bool full = DENSE || (t.h == TS && t.w == TS);         // wave-uniform
     auto sym_part = [&](int it) {
@@ -1634,8 +1634,16 @@ void fused_step_kernel(const LayerDesc *__restrict__ layers, const FusedTile *__
         } else {
           tile_sync<G::WPT>();
         }
-        store_acc_t<TS, PREC, false, false, NI, false, (G::XLO > 0)>(xr, X, p0, q0, lane, 1.f, 1.f, f8s_of(fs.xn()),
-                                                                      xlo);
+        // X_{it+1}: without its e4m3 planes when the next step's Gram and update both read
+        // hi alone (hi + lo is the bf16x3 layout, lo where the a X term reads it)
+        bool plain_x = false;
+        if constexpr (G::XLO > 0 && PLAIN_GRAM_STEPS > 1 && PLAIN_UPDATE_STEPS > 1) {
+          plain_x = full && it + 1 < PLAIN_GRAM_STEPS && it + 1 < PLAIN_UPDATE_STEPS && it + 2 < prm.steps;
+          if (plain_x) store_acc_t<TS, PREC_BF16X3>(xr, Mat<PREC_BF16X3>{X.hi, xlo}, p0, q0, lane);
+        }
+        if (!plain_x)
+          store_acc_t<TS, PREC, false, false, NI, false, (G::XLO > 0)>(xr, X, p0, q0, lane, 1.f, 1.f,
+                                                                        f8s_of(fs.xn()), xlo);
         tile_sync<G::WPT>();
         fs.advance();
       }

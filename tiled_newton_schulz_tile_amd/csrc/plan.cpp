@@ -286,7 +286,7 @@ himuon_status plan_partition(Plan &p, int32_t tile, std::string &err) {
             const double nb = e / 32.0, f = (nb + 1.0) / (2.0 * nb);
             if (prec == HIMUON_PREC_BF16F8 && e >= 64) {
               const bool full = h == e && w == e;
-              const int pg = full ? kF8PlainGramSteps : 0, ps = full ? f8_plain_square_steps(e, dense) : 0;
+              const int pg = full ? f8_plain_gram_steps(e, dense) : 0, ps = full ? f8_plain_square_steps(e, dense) : 0;
               const int pu = full ? f8_plain_update_steps(e, dense) : 0;   // never the last step
               for (int k = 0; k < K; ++k) {
                 const double units = f * (k < pg ? 1.0 : 2.0) + (quintic ? f * (k < ps ? 1.0 : 2.0) : 0.0) +
