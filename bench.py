@@ -38,7 +38,7 @@ METRIC = "HiMuon step ms & NS TFLOP/s (% MFMA peak) vs T, 8B-shaped stack"
 # readings of a 1 GiB elementwise copy (x2.0 read, x1.0 write).  Valid only for the
 # kernel source it was measured on (sha256 prefix of ns_fused.hip followed by the two
 # headers it includes); null otherwise.
-TRAFFIC_T128 = {"source_sha256_16": "1165052ef657dded", "precision": "bf16f8", "fetch_kib": 27291293.625,
+TRAFFIC_T128 = {"source_sha256_16": "c052f9a1f7329e72", "precision": "bf16f8", "fetch_kib": 27291272.4375,
                 "write_kib": 40894464.0, "fetch_scale": 2.0, "write_scale": 1.0}
 
 

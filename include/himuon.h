@@ -75,8 +75,9 @@ typedef enum {
                              64 x 64 or 128 x 128, the Gram product of NS step 0 and the
                              square product of steps 0 and 1 use the bf16 hi operands
                              alone, and on dense 128-tiles (full, 16-byte aligned rows)
-                             so does the B X product of steps 0 and 1 (never of the last
-                             step); other 128-tiles keep the split square and update.
+                             so do the Gram and B X products of step 1 and the B X
+                             product of step 0 (never the last step's B X); other
+                             128-tiles keep the split square and update.
                              The a X term of each step is added in fp32 from X
                              held to about 2^-17 (bf16 hi + lo, or fp32), not through the
                              e4m3 operands, so rounding noise does not build up in the
